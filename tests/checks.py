@@ -1,0 +1,106 @@
+"""Shared test helpers: input poisoning, tolerance rule, exact comparisons.
+
+Tolerance (reading R14 of the values the step must match):
+* BF16 cache: every element |got - ref| <= 2e-2 + 1e-2 |ref|, and for the
+  attention output also ||got - ref||_2 / ||ref||_2 <= 1e-2 (the elementwise
+  bound alone is looser than the signal at long lengths).
+* FP8 cache: every element |got - ref| <= 6e-2 on the attention output.
+* The schedule and every cache index: bit-exact.
+"""
+
+import numpy as np
+import torch
+
+from oracle import tile_offset, PAGE_SIZE, BF16_NAN_BITS, E4M3_NAN_CODE
+
+BF16_ATOL, BF16_RTOL, BF16_REL_L2 = 2e-2, 1e-2, 1e-2
+FP8_ATOL = 6e-2
+
+
+def to_f64(t):
+    """A torch tensor (bf16/fp32) -> fp64 numpy on the host."""
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def bits_u16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_output(got, ref, kv_dtype, what="output", rel_l2=True):
+    """Apply the tolerance rule; return (max_abs, rel_l2) or raise AssertionError."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    rl2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    if kv_dtype == "bf16":
+        bad = err > BF16_ATOL + BF16_RTOL * np.abs(ref)
+        assert not bad.any(), f"{what}: {int(bad.sum())} elements out of tolerance, max abs {max_abs:.3e}"
+        if rel_l2:
+            assert rl2 <= BF16_REL_L2, f"{what}: relative L2 {rl2:.3e} > {BF16_REL_L2}"
+    else:
+        assert max_abs <= FP8_ATOL, f"{what}: max abs {max_abs:.3e} > {FP8_ATOL}"
+    return max_abs, rl2
+
+
+def poison_indices(inp, w, kind):
+    """Pool indices (one pool) of every element the step must not read.
+
+    Pages no sequence owns, the rows at or past L_b of each sequence's last
+    page, and the new token's own slot (the prologue must overwrite it before
+    attention reads it).
+    """
+    bt = inp["block_table"].cpu().numpy()
+    lens = [int(L) for L in w.seq_lens]
+    Hkv, ps, hs = w.num_kv_heads, inp["page_stride"], inp["head_stride"]
+    owned = set()
+    for b, L in enumerate(lens):
+        owned.update(bt[b, :-(-L // PAGE_SIZE)].tolist())
+    idx = [np.arange(p * ps, p * ps + Hkv * hs) for p in range(inp["num_pages"]) if p not in owned]
+    d = np.arange(128)
+    for b, L in enumerate(lens):
+        t = (L - 1) // PAGE_SIZE
+        rows = np.array(list(range(L - t * PAGE_SIZE, PAGE_SIZE)) + [(L - 1) % PAGE_SIZE])
+        page = int(bt[b, t])
+        for g in range(Hkv):
+            off = tile_offset(kind, w.kv_dtype, rows[:, None], d[None, :]).reshape(-1)
+            idx.append(page * ps + g * hs + off)
+    return np.concatenate(idx)
+
+
+def poison_cache(inp, w):
+    """Fill every cache element the step must not read with NaN, in place."""
+    nan = BF16_NAN_BITS if w.kv_dtype == "bf16" else E4M3_NAN_CODE
+    for key, kind in (("k_cache", "k"), ("v_cache", "v")):
+        pool = inp[key]
+        ti = torch.from_numpy(poison_indices(inp, w, kind).astype(np.int64)).to(pool.device)
+        if pool.dtype == torch.bfloat16:
+            pool.view(torch.int16).index_fill_(0, ti, int(np.int16(np.uint16(nan).view(np.int16))))
+        else:
+            pool.index_fill_(0, ti, nan)
+
+
+def oracle_cfg(inp, w):
+    return {"kv_dtype": w.kv_dtype, "k_scale": w.k_scale, "v_scale": w.v_scale,
+            "sm_scale": 1.0 / np.sqrt(128.0), "page_stride": inp["page_stride"],
+            "head_stride": inp["head_stride"], "num_kv_heads": w.num_kv_heads}
+
+
+def host_pools(inp, w):
+    """Host numpy views of the pools: uint16 BF16 bits or uint8 codes."""
+    if w.kv_dtype == "bf16":
+        return bits_u16(inp["k_cache"]), bits_u16(inp["v_cache"])
+    return inp["k_cache"].cpu().numpy(), inp["v_cache"].cpu().numpy()
+
+
+def host_step_inputs(inp):
+    """The small per-step arrays as host numpy (BF16 as uint16 bits)."""
+    return {
+        "q": bits_u16(inp["q"]), "k": bits_u16(inp["k"]), "v": bits_u16(inp["v"]),
+        "wq": bits_u16(inp["q_norm_w"]), "wk": bits_u16(inp["k_norm_w"]),
+        "positions": inp["positions"].cpu().numpy().astype(np.int64),
+        "seq_lens": inp["seq_lens"].cpu().numpy().astype(np.int64),
+        "block_table": inp["block_table"].cpu().numpy().astype(np.int64),
+    }

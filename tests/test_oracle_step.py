@@ -1,0 +1,160 @@
+"""Whole-step oracle checks on the CPU, and mutation tests of the checkers.
+
+The step composes the pinned parts; here the composition is checked:
+split-then-merge over both schedules equals full attention, poisoned cache
+elements never reach an output, relabelling physical pages changes nothing,
+and the checkers used by the GPU tests fail on planted mistakes.
+"""
+
+import copy
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import step as ostep
+from load_balanced_split_rope_amd import workloads as wl
+from checks import (poison_cache, host_pools, host_step_inputs, oracle_cfg,
+                    check_output)
+
+
+def run_oracle(w, inp, plan_kind=("dynamic", 3)):
+    h = host_step_inputs(inp)
+    pools = host_pools(inp, w)
+    pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                          h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
+                          kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    cfg = oracle_cfg(inp, w)
+    full = oracle.decode_attention(pro["q_out"], pools, pro, h["seq_lens"], h["block_table"], cfg)
+    return h, pools, pro, cfg, full
+
+
+@pytest.mark.parametrize("name_or_lens,dtype", [("tiny", "bf16"), ([1, 65, 130, 7], "fp8"),
+                                                 ([300, 64, 1], "bf16")])
+def test_split_equals_full_for_both_schedules(name_or_lens, dtype):
+    if name_or_lens == "tiny":
+        w = wl.named("tiny")
+    else:
+        w = wl.custom(name_or_lens, num_q_heads=16, num_kv_heads=2, kv_dtype=dtype, seed=7)
+    inp = wl.make_inputs(w)
+    poison_cache(inp, w)
+    h, pools, pro, cfg, full = run_oracle(w, inp)
+    B, Hq = w.batch, w.num_q_heads
+    ref_o = np.stack([np.stack([full[(b, hh)][0] for hh in range(Hq)]) for b in range(B)])
+    ref_l = np.array([[full[(b, hh)][1] for hh in range(Hq)] for b in range(B)])
+    assert np.all(np.isfinite(ref_o)) and np.all(np.isfinite(ref_l))
+    for plan in (oracle.plan_dynamic(h["seq_lens"], 1), oracle.plan_dynamic(h["seq_lens"], 3),
+                 oracle.plan_dynamic(h["seq_lens"], 256), oracle.plan_static(h["seq_lens"], 2)):
+        o, lse, _ = oracle.split_attention(pro["q_out"], pools, pro, h["seq_lens"],
+                                           h["block_table"], cfg, plan)
+        assert np.allclose(o, ref_o, rtol=1e-12, atol=1e-14)
+        assert np.allclose(lse, ref_l, rtol=1e-13, atol=1e-13)
+
+
+def test_prologue_writes_only_the_new_slots():
+    w = wl.named("tiny")
+    inp = wl.make_inputs(w)
+    h, pools, pro, cfg, _ = run_oracle(w, inp)
+    k0, v0 = pools[0].copy(), pools[1].copy()
+    k1, v1 = k0.copy(), v0.copy()
+    ostep.apply_prologue_writes(k1, v1, pro, kv_dtype="bf16", page_stride=inp["page_stride"],
+                                head_stride=inp["head_stride"])
+    changed = np.nonzero(k1 != k0)[0].size + np.nonzero(v1 != v0)[0].size
+    # B tokens x Hkv heads x 128 channels in each of K and V, at most
+    assert changed <= 2 * 4 * 1 * 128
+    # every written slot reads back through the layout as the stored row
+    for b in range(4):
+        page, row = pro["slots"][b]
+        L = int(h["seq_lens"][b])
+        assert (page, row) == (h["block_table"][b][(L - 1) // 64], (L - 1) % 64)
+        got = ostep.gather_kv(k1, "k", "bf16", h["block_table"][b], L, 0,
+                              page_stride=inp["page_stride"], head_stride=inp["head_stride"])
+        assert np.array_equal(got[L - 1], oracle.bf16_bits_to_f64(pro["k_store"][b, 0]))
+
+
+def test_page_relabelling_changes_nothing():
+    w = wl.custom([200, 5, 129], num_q_heads=8, num_kv_heads=1, seed=3)
+    inp = wl.make_inputs(w)
+    _, _, _, _, full = run_oracle(w, inp)
+    # move every page to a new physical index, and the block table with it
+    inp2 = dict(inp)
+    n = inp["num_pages"]
+    perm = np.random.default_rng(0).permutation(n)
+    ps = inp["page_stride"]
+    for key in ("k_cache", "v_cache"):
+        pool = inp[key].clone().view(n, ps)
+        moved = pool.clone()
+        moved[perm] = pool
+        inp2[key] = moved.view(-1)
+    bt = inp["block_table"].clone()
+    mask = bt >= 0
+    bt[mask] = __import__("torch").from_numpy(perm.astype(np.int32))[bt[mask].long()]
+    inp2["block_table"] = bt
+    _, _, _, _, full2 = run_oracle(w, inp2)
+    for key in full:
+        assert np.array_equal(full[key][0], full2[key][0]) and full[key][1] == full2[key][1]
+
+
+def test_single_token_sequence_returns_its_own_v():
+    w = wl.custom([1, 1], num_q_heads=8, num_kv_heads=1, seed=11)
+    inp = wl.make_inputs(w)
+    h, _, pro, _, full = run_oracle(w, inp)
+    for b in range(2):
+        for hh in range(8):
+            assert np.array_equal(full[(b, hh)][0], oracle.bf16_bits_to_f64(h["v"][b, 0]))
+
+
+# ---------------------------------------------------------------- mutations
+# Each test plants one plausible mistake in a copy of an oracle result or
+# function, on the CPU, and shows that the check the GPU tests rely on fails.
+
+def test_mutation_dropped_tile_fails_schedule_invariants():
+    from test_oracle_schedule import check_plan_invariants
+    lens = [131072] + [4096] * 31
+    plan = oracle.plan_dynamic(lens, 256)
+    bad = copy.deepcopy(plan)
+    bad.chunks[5, 2] -= 1                       # chunk 5 loses its last tile
+    with pytest.raises(AssertionError):
+        check_plan_invariants(bad, lens)
+    bad = copy.deepcopy(plan)
+    bad.chunks[7, 1] -= 1                       # chunk 7 repeats a tile
+    with pytest.raises(AssertionError):
+        check_plan_invariants(bad, lens)
+
+
+def test_mutation_swapped_fp8_scales_fail_tolerance():
+    w = wl.custom([300, 40], num_q_heads=8, num_kv_heads=1, kv_dtype="fp8", seed=5)
+    inp = wl.make_inputs(w)
+    h, pools, pro, cfg, full = run_oracle(w, inp)
+    cfg_bad = dict(cfg, k_scale=cfg["v_scale"], v_scale=cfg["k_scale"])
+    bad = oracle.decode_attention(pro["q_out"], pools, pro, h["seq_lens"], h["block_table"], cfg_bad)
+    got = np.stack([bad[k][0] for k in sorted(full)])
+    ref = np.stack([full[k][0] for k in sorted(full)])
+    with pytest.raises(AssertionError):
+        check_output(got, ref, "fp8")
+
+
+def test_mutation_off_by_one_slot_is_detected():
+    w = wl.named("tiny")
+    inp = wl.make_inputs(w)
+    poison_cache(inp, w)
+    h, pools, pro, cfg, full = run_oracle(w, inp)
+    bad_pro = dict(pro)
+    bad_pro["slots"] = pro["slots"].copy()
+    bad_pro["slots"][:, 1] = (bad_pro["slots"][:, 1] + 1) % 64   # write one row too far
+    bad = oracle.decode_attention(pro["q_out"], pools, bad_pro, h["seq_lens"], h["block_table"], cfg)
+    # the new token's own slot stays poisoned, so the output is NaN somewhere
+    assert any(not np.all(np.isfinite(bad[k][0])) for k in bad)
+
+
+def test_mutation_dropped_tile_moves_lse_beyond_fp32_noise():
+    """q = 0 (zero norm weight): lse = ln L; one dropped tile is caught."""
+    w = wl.custom([4096 + 64], num_q_heads=8, num_kv_heads=1, seed=9)
+    inp = wl.make_inputs(w)
+    h, pools, pro, cfg, _ = run_oracle(w, inp)
+    zero_q = np.zeros_like(pro["q_out"])
+    full = oracle.decode_attention(zero_q, pools, pro, h["seq_lens"], h["block_table"], cfg)
+    lens_short = h["seq_lens"] - 64
+    short = oracle.decode_attention(zero_q, pools, None, lens_short, h["block_table"], cfg)
+    assert abs(full[(0, 0)][1] - np.log(4160)) < 1e-12
+    assert abs(full[(0, 0)][1] - short[(0, 0)][1]) > 100 * np.finfo(np.float32).eps * np.log(4160)
