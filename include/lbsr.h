@@ -1,0 +1,271 @@
+/*
+ * lbsr -- load-balanced split-KV decode attention with a fused RoPE/QK-Norm
+ * prologue, for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of grouped-query attention over a paged KV cache:
+ *
+ *   1. lbsr_rope_norm_kv_write  RoPE + QK-Norm on the new token's q and k and
+ *                               the KV-cache write, in one kernel;
+ *   2. lbsr_plan                a per-step schedule that deals 64-token tiles
+ *                               to workers in proportion to each sequence's
+ *                               length (or a static equal split, for
+ *                               comparison);
+ *   3. lbsr_attention           split attention over the scheduled tiles with
+ *                               an online softmax, then a log-sum-exp merge of
+ *                               the pieces of sequences that were split;
+ *   4. lbsr_decode_step         2 -> 1 -> 3 on one stream (the plan does not
+ *                               depend on the prologue and clears the error
+ *                               word, so it runs first).
+ *
+ * Sources (titles translated from Korean):
+ *   [A] 24-ai.news, "vLLM and Tencent Hunyuan upstream two HPC backends for
+ *       NVIDIA Hopper GPUs", sections "Two new HPC backends in the vLLM
+ *       ecosystem" (64 q heads, 8 KV heads, head dim 128) and "Why does
+ *       dynamic scheduling matter in attention?" (length-proportional
+ *       64-token tiles vs static split-KV; fused RoPE + QK-Norm + KV write;
+ *       BF16 and FP8).
+ *   [B] blog.secrett2633.cloud, "[vllm] Introducing the HPC-Ops attention
+ *       backend for high-performance inference in vLLM", intro (FP8 E4M3),
+ *       "Code analysis 1" (output dtype passed explicitly), "Code analysis 2"
+ *       (the fused op writes a caller-provided output and is entered directly,
+ *       so it can be captured in a graph).
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are DEVICE pointers unless a comment says "host".
+ *     `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - The caller owns and allocates every buffer (inputs, outputs, caches,
+ *     workspace).  The library allocates no device memory, keeps no pointer
+ *     after a call returns, and launches asynchronously on `stream`; buffers
+ *     must stay alive until the stream has passed the launch.
+ *   - Host-side validation happens before any launch; on failure nothing is
+ *     launched, a status is returned and lbsr_last_error() holds a message.
+ *   - No entry point synchronises, except lbsr_decode_step_timed (bench).
+ *   - Device-side preconditions are checked in the kernels without faulting:
+ *     a violating input is clamped or skipped and a bit is OR-ed into the
+ *     workspace's sticky error word (see LBSR_DEV_ERR_*).
+ *   - Calls on different streams need different workspaces.
+ */
+#ifndef LBSR_H
+#define LBSR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LBSR_ABI_VERSION 1
+#define LBSR_HEAD_DIM 128
+#define LBSR_PAGE_SIZE 64
+#define LBSR_TILE_ELEMS (LBSR_HEAD_DIM * LBSR_PAGE_SIZE) /* 8192 elements */
+
+typedef enum {
+  LBSR_OK = 0,
+  LBSR_E_INVALID = 1,     /* null pointer, size out of range, bad alignment */
+  LBSR_E_UNSUPPORTED = 2, /* head_dim != 128, page_size != 64, group > 16, non-gfx950 */
+  LBSR_E_WORKSPACE = 3,   /* ws_bytes < the size lbsr_workspace_size reports */
+  LBSR_E_HIP = 4          /* a HIP runtime call or launch failed */
+} lbsr_status;
+
+typedef enum { LBSR_KV_BF16 = 0, LBSR_KV_FP8_E4M3 = 1 } lbsr_kv_dtype;
+typedef enum { LBSR_SCHED_DYNAMIC = 0, LBSR_SCHED_STATIC = 1 } lbsr_sched;
+
+/* Sticky device error bits (int32 at lbsr_ws_layout.error_word). */
+#define LBSR_DEV_ERR_SEQ_LEN 1   /* seq_len outside [1, max_blocks_per_seq*64]: clamped */
+#define LBSR_DEV_ERR_PAGE 2      /* block-table entry outside [0, num_pages): page 0 used */
+#define LBSR_DEV_ERR_POSITION 4  /* position outside [0, max_blocks_per_seq*64): write skipped */
+
+/*
+ * Cache page layout ([A] "Why does dynamic scheduling matter in attention?"
+ * fixes only the 64-token tile; the layout is this library's own).
+ *
+ * The K cache and the V cache are two pools of the same geometry.  Element
+ * (page p, KV head g, token row r in [0,64), channel d in [0,128)) lives at
+ *     p * page_stride + g * head_stride + tile_offset(r, d)
+ * elements from the pool's base.  A tile (one page of one KV head) is 8192
+ * contiguous elements: BF16 (16 KiB) or E4M3 codes (8 KiB).  It is stored as
+ * 1 KiB fragments of 64 consecutive 16-byte "lanes"; with tb = r/16,
+ * kc = (d%32)/8, s = d/32, db = d/16, kv = (r%16)/4, e = 4*(tb%2) + r%4:
+ *
+ *   K, BF16: 512*(4*tb + s)    + 8*(16*kc + r%16)  + d%8
+ *   V, BF16: 512*(2*db + tb/2) + 8*(16*kv + d%16)  + e
+ *   K, FP8 : 1024*(2*tb + s/2) + 16*(16*kc + r%16) + 8*(s%2) + d%8
+ *   V, FP8 : 1024*db           + 16*(16*kv + d%16) + 8*(tb/2) + e
+ *
+ * (integer division).  One wave reading one fragment with one 16-byte load
+ * per lane gets exactly the operand of one (K) or one (V) matrix-core step;
+ * every global read is a contiguous 1 KiB.  Tile t of sequence b is page
+ * block_table[b * max_blocks_per_seq + t].
+ */
+
+typedef struct {
+  int32_t num_q_heads;        /* Hq >= 1, a multiple of Hkv */
+  int32_t num_kv_heads;       /* Hkv >= 1; group G = Hq / Hkv must be <= 16 */
+  int32_t head_dim;           /* must be 128 */
+  int32_t page_size;          /* must be 64 */
+  int32_t kv_dtype;           /* lbsr_kv_dtype */
+  int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
+  int64_t num_pages;          /* pages in each pool, >= 1 */
+  int64_t page_stride;        /* elements; multiple of 8192 */
+  int64_t head_stride;        /* elements; multiple of 8192 */
+} lbsr_shape;
+
+typedef struct {
+  double rope_theta;        /* RoPE base, > 0 (e.g. 1e4) */
+  float rms_eps;            /* RMSNorm epsilon, >= 0 (e.g. 1e-6) */
+  int32_t norm_before_rope; /* 0: RoPE then RMSNorm (default); 1: RMSNorm then RoPE */
+  float k_scale;            /* FP8 cache: value = code * k_scale; > 0; ignored for BF16 */
+  float v_scale;            /* FP8 cache: value = code * v_scale; > 0; ignored for BF16 */
+  float sm_scale;           /* softmax scale; 0 -> 1/sqrt(128) */
+} lbsr_params;
+
+typedef struct {
+  int32_t sched;         /* lbsr_sched */
+  int32_t num_workers;   /* dynamic: P workers; 0 -> the device's CU count */
+  int32_t static_splits; /* static: S splits per sequence; 0 -> max(1, P / batch) */
+  int32_t reserved;      /* must be 0 */
+} lbsr_sched_cfg;
+
+/* Byte offsets of the arrays inside a workspace (all 256-byte aligned). */
+typedef struct {
+  size_t error_word;   /* int32: sticky LBSR_DEV_ERR_* bits (the plan clears it) */
+  size_t cu_tiles;     /* int32[batch + 1]: prefix sums of ceil(L_b / 64) */
+  size_t worker_chunk; /* int32[W + 1]: worker w owns chunks [wc[w], wc[w+1]) */
+  size_t chunks;       /* int32[C_max][4]: (sequence, first tile, end tile, worker) */
+  size_t seq_chunk;    /* int32[batch + 1]: sequence b owns chunks [sc[b], sc[b+1]) */
+  size_t seq_len_eff;  /* int32[batch]: lengths after clamping */
+  size_t partial_o;    /* float[C_max][Hq][128]: normalised partial outputs */
+  size_t partial_lse;  /* float[C_max][Hq]: partial log2-sum-exp (internal) */
+  size_t total;        /* bytes the workspace needs */
+  int32_t num_workers; /* W: workers (= attention workgroups) */
+  int32_t max_chunks;  /* C_max = W + batch - 1 (dynamic) or batch * S (static) */
+  int32_t static_splits; /* S actually used (static), else 0 */
+  int32_t reserved;
+} lbsr_ws_layout;
+
+/* ABI version of the loaded library (LBSR_ABI_VERSION). Host only. */
+int32_t lbsr_abi_version(void);
+
+/* Text of a status code. Host only; never NULL. */
+const char *lbsr_status_string(lbsr_status status);
+
+/* Detail of the last failed call on this thread (empty if none). Host only. */
+const char *lbsr_last_error(void);
+
+/* Number of workers the dynamic schedule uses by default on `device`: its
+ * compute-unit count (256 on MI355X).  Fails with LBSR_E_UNSUPPORTED if the
+ * device is not gfx950. */
+lbsr_status lbsr_device_workers(int device, int32_t *out);
+
+/* Workspace layout for a step of `batch` sequences under `cfg`.  Host only
+ * when cfg->num_workers > 0 (else it queries the current device).  Like the
+ * shape-only "fake" implementation of [B] "Code analysis 2", it needs no
+ * device data. */
+lbsr_status lbsr_workspace_layout(const lbsr_shape *shape, int32_t batch,
+                                  const lbsr_sched_cfg *cfg, lbsr_ws_layout *out);
+
+/* Shorthand: *bytes = lbsr_workspace_layout(...).total. */
+lbsr_status lbsr_workspace_size(const lbsr_shape *shape, int32_t batch,
+                                const lbsr_sched_cfg *cfg, size_t *bytes);
+
+/*
+ * Fused prologue ([A] "Why does dynamic scheduling matter in attention?";
+ * [B] "Code analysis 2"): for each new token b at position pos = positions[b]
+ *   q_out[b][h] = RMSNorm_wq(RoPE(q[b][h], pos))    for every q head h (BF16)
+ *   k'          = RMSNorm_wk(RoPE(k[b][g], pos))    for every KV head g
+ * and stores k' and v[b][g] (unchanged) into row pos % 64 of page
+ * block_table[b][pos / 64] of the K and V pools: as BF16, or as E4M3 codes
+ * RNE(clamp(x / scale, -448, 448)) with k_scale / v_scale.
+ * RoPE is rotate-half over all 128 channels: channel i pairs with i + 64 and
+ * turns by pos * rope_theta^(-2i/128).  RMSNorm is x / sqrt(mean(x^2) + eps) * w.
+ * The arithmetic is fp64; each stored value is rounded once.
+ *
+ *   q        [batch][Hq][128] BF16           k, v   [batch][Hkv][128] BF16
+ *   positions [batch] int32                  q_norm_w, k_norm_w [128] BF16
+ *   block_table [batch][max_blocks_per_seq] int32
+ *   k_cache, v_cache  pools (layout above)   q_out  [batch][Hq][128] BF16
+ *   error_word  nullable int32*: LBSR_DEV_ERR_POSITION / _PAGE are OR-ed in
+ * All pointers 16-byte aligned.  A position outside [0, max_blocks*64) or a
+ * page outside [0, num_pages) skips that token's cache write (q_out is still
+ * written).  q_out may not alias q.
+ */
+lbsr_status lbsr_rope_norm_kv_write(const lbsr_shape *shape, const lbsr_params *params,
+                                    int32_t batch, const void *q, const void *k,
+                                    const void *v, const int32_t *positions,
+                                    const void *q_norm_w, const void *k_norm_w,
+                                    const int32_t *block_table, void *k_cache,
+                                    void *v_cache, void *q_out, int32_t *error_word,
+                                    void *stream);
+
+/*
+ * Tile schedule ([A] "Why does dynamic scheduling matter in attention?").
+ * A sequence of length L (the new token included) has n = ceil(L/64) tiles.
+ *   dynamic: all tiles laid end to end (T in total); worker w of P owns flat
+ *            tiles [floor(w*T/P), floor((w+1)*T/P)), cut at sequence ends
+ *            into chunks, numbered in flat order.
+ *   static:  every sequence is cut into the same S parts of its own tiles,
+ *            [floor(s*n/S), floor((s+1)*n/S)); worker b*S+s; empty parts skipped.
+ * Writes the arrays of lbsr_ws_layout into `workspace` (one workgroup, no
+ * host sync) and clears the error word.  seq_lens [batch] int32 (device).
+ */
+lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq_lens,
+                      const lbsr_sched_cfg *cfg, void *workspace, size_t ws_bytes,
+                      void *stream);
+
+/*
+ * Split attention + merge over the schedule in `workspace` (run lbsr_plan
+ * first with the same shape, batch and cfg).  For sequence b, q head h and
+ * KV head g = h / (Hq/Hkv), over the rows j < L_b:
+ *   out[b][h] = sum_j softmax_j(sm_scale * <q_out[b][h], K_j>) V_j      (BF16)
+ *   lse_out[b][h] = ln sum_j exp(sm_scale * <q_out[b][h], K_j>)        (fp32)
+ * with K_j = code*k_scale and V_j = code*v_scale for an FP8 cache.  Each
+ * chunk is one online-softmax pass over its tiles; a sequence with several
+ * chunks is merged by log-sum-exp weights in ascending chunk order.
+ *   q_out [batch][Hq][128] BF16   out [batch][Hq][128] BF16
+ *   lse_out nullable float[batch][Hq]
+ * Rows at or past L_b of a sequence's last page are never used, whatever
+ * they hold.  Deterministic: no atomics.
+ */
+lbsr_status lbsr_attention(const lbsr_shape *shape, const lbsr_params *params, int32_t batch,
+                           const void *q_out, const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, const lbsr_sched_cfg *cfg,
+                           void *workspace, size_t ws_bytes, void *out, float *lse_out,
+                           void *stream);
+
+/*
+ * One whole decode step: lbsr_plan, lbsr_rope_norm_kv_write, lbsr_attention
+ * on `stream`, in that order (arguments as there; the prologue's error bits
+ * go to the workspace's error word, which the plan cleared).  Requires
+ * positions[b] = seq_lens[b] - 1 for the new token to be part of its own
+ * attention.
+ */
+lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
+                             int32_t batch, const void *q, const void *k, const void *v,
+                             const int32_t *positions, const int32_t *seq_lens,
+                             const void *q_norm_w, const void *k_norm_w,
+                             const int32_t *block_table, void *k_cache, void *v_cache,
+                             void *q_out, const lbsr_sched_cfg *cfg, void *workspace,
+                             size_t ws_bytes, void *out, float *lse_out, void *stream);
+
+/*
+ * Benchmark helper: lbsr_decode_step with a HIP event recorded on `stream`
+ * around each of its four kernels (plan, prologue, split attention,
+ * merge, in that order); waits for the stream and writes the four durations in
+ * milliseconds to kernel_ms[4] (host).  Synchronises.  Not for production.
+ */
+lbsr_status lbsr_decode_step_timed(const lbsr_shape *shape, const lbsr_params *params,
+                                   int32_t batch, const void *q, const void *k,
+                                   const void *v, const int32_t *positions,
+                                   const int32_t *seq_lens, const void *q_norm_w,
+                                   const void *k_norm_w, const int32_t *block_table,
+                                   void *k_cache, void *v_cache, void *q_out,
+                                   const lbsr_sched_cfg *cfg, void *workspace,
+                                   size_t ws_bytes, void *out, float *lse_out,
+                                   void *stream, float *kernel_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBSR_H */

@@ -1,0 +1,143 @@
+"""ctypes binding of liblbsr (include/lbsr.h): argument marshalling only.
+
+Every step of the decode path runs in the library's HIP kernels; this module
+checks tensor dtypes, devices and sizes, builds the C structs, and passes raw
+device pointers and the current torch stream.  If the library has not been
+built, every call raises ``LibraryNotBuilt`` -- there is no fallback.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblbsr.so")
+
+HEAD_DIM = 128
+PAGE_SIZE = 64
+TILE_ELEMS = HEAD_DIM * PAGE_SIZE
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
+KV_BF16, KV_FP8_E4M3 = 0, 1
+SCHED_DYNAMIC, SCHED_STATIC = 0, 1
+DEV_ERR_SEQ_LEN, DEV_ERR_PAGE, DEV_ERR_POSITION = 1, 2, 4
+
+# Every symbol include/lbsr.h declares.
+EXPORTS = (
+    "lbsr_abi_version", "lbsr_status_string", "lbsr_last_error", "lbsr_device_workers",
+    "lbsr_workspace_layout", "lbsr_workspace_size", "lbsr_rope_norm_kv_write", "lbsr_plan",
+    "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed",
+)
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class LbsrError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_STATUS_NAMES = {OK: "LBSR_OK", E_INVALID: "LBSR_E_INVALID", E_UNSUPPORTED: "LBSR_E_UNSUPPORTED",
+                 E_WORKSPACE: "LBSR_E_WORKSPACE", E_HIP: "LBSR_E_HIP"}
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("page_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float),
+                ("norm_before_rope", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float), ("sm_scale", ctypes.c_float)]
+
+
+class SchedCfg(ctypes.Structure):
+    _fields_ = [("sched", ctypes.c_int32), ("num_workers", ctypes.c_int32),
+                ("static_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [("error_word", ctypes.c_size_t), ("cu_tiles", ctypes.c_size_t),
+                ("worker_chunk", ctypes.c_size_t), ("chunks", ctypes.c_size_t),
+                ("seq_chunk", ctypes.c_size_t), ("seq_len_eff", ctypes.c_size_t),
+                ("partial_o", ctypes.c_size_t), ("partial_lse", ctypes.c_size_t),
+                ("total", ctypes.c_size_t), ("num_workers", ctypes.c_int32),
+                ("max_chunks", ctypes.c_int32), ("static_splits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+def _declare(lib):
+    st = ctypes.c_int
+    sig = {
+        "lbsr_abi_version": (_I32, []),
+        "lbsr_status_string": (ctypes.c_char_p, [st]),
+        "lbsr_last_error": (ctypes.c_char_p, []),
+        "lbsr_device_workers": (st, [ctypes.c_int, ctypes.POINTER(_I32)]),
+        "lbsr_workspace_layout": (st, [ctypes.POINTER(Shape), _I32, ctypes.POINTER(SchedCfg),
+                                       ctypes.POINTER(WsLayout)]),
+        "lbsr_workspace_size": (st, [ctypes.POINTER(Shape), _I32, ctypes.POINTER(SchedCfg),
+                                     ctypes.POINTER(ctypes.c_size_t)]),
+        "lbsr_rope_norm_kv_write": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
+                                    + [_P] * 11 + [_P]),
+        "lbsr_plan": (st, [ctypes.POINTER(Shape), _I32, _P, ctypes.POINTER(SchedCfg), _P,
+                           ctypes.c_size_t, _P]),
+        "lbsr_attention": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32, _P, _P, _P,
+                                _P, ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t, _P, _P, _P]),
+        "lbsr_decode_step": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
+                             + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t, _P,
+                                            _P, _P]),
+        "lbsr_decode_step_timed": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
+                                   + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t,
+                                                  _P, _P, _P, ctypes.POINTER(ctypes.c_float)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def lib():
+    """The loaded library; raises LibraryNotBuilt if it is missing."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise LibraryNotBuilt(
+                        f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                        "(hipcc, gfx950); there is no fallback implementation")
+                handle = ctypes.CDLL(LIB_PATH)
+                _declare(handle)
+                _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != OK:
+        raise LbsrError(status, lib().lbsr_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)

@@ -1,0 +1,484 @@
+// C ABI of liblbsr: argument validation, workspace layout, kernel launches.
+// The declarations and their contracts are in include/lbsr.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/lbsr.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+lbsr_status fail(lbsr_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lbsr_status fail(lbsr_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define LBSR_CHECK(expr)                  \
+  do {                                    \
+    const lbsr_status st_ = (expr);       \
+    if (st_ != LBSR_OK) return st_;       \
+  } while (0)
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool queried = false;
+  bool gfx950 = false;
+  int cu_count = 0;
+  char arch[64] = {0};
+};
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_device_mutex;
+
+lbsr_status device_info(int device, DeviceInfo* out) {
+  if (device < 0 || device >= kMaxDevices) return fail(LBSR_E_INVALID, "device %d out of range", device);
+  std::lock_guard<std::mutex> lock(g_device_mutex);
+  DeviceInfo& d = g_devices[device];
+  if (!d.queried) {
+    hipDeviceProp_t prop;
+    const hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess)
+      return fail(LBSR_E_HIP, "hipGetDeviceProperties(%d): %s", device, hipGetErrorString(e));
+    d.cu_count = prop.multiProcessorCount;
+    snprintf(d.arch, sizeof d.arch, "%s", prop.gcnArchName);
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.queried = true;
+  }
+  *out = d;
+  return LBSR_OK;
+}
+
+lbsr_status current_device(DeviceInfo* out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LBSR_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  LBSR_CHECK(device_info(dev, out));
+  if (!out->gfx950)
+    return fail(LBSR_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev, out->arch);
+  return LBSR_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+lbsr_status check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(LBSR_E_INVALID, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(LBSR_E_INVALID, "%s is not %zu-byte aligned", name, align);
+  return LBSR_OK;
+}
+
+lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
+  if (!s) return fail(LBSR_E_INVALID, "shape is NULL");
+  if (s->head_dim != LBSR_HEAD_DIM)
+    return fail(LBSR_E_UNSUPPORTED, "head_dim %d: only 128 is supported", s->head_dim);
+  if (s->page_size != LBSR_PAGE_SIZE)
+    return fail(LBSR_E_UNSUPPORTED, "page_size %d: only 64 is supported", s->page_size);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(LBSR_E_INVALID, "head counts must be >= 1 (Hq %d, Hkv %d)", s->num_q_heads,
+                s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(LBSR_E_INVALID, "Hq %d is not a multiple of Hkv %d", s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads / s->num_kv_heads > lbsr::kMaxGroup)
+    return fail(LBSR_E_UNSUPPORTED, "group size %d > 16", s->num_q_heads / s->num_kv_heads);
+  if (s->num_q_heads > 4096) return fail(LBSR_E_UNSUPPORTED, "Hq %d > 4096", s->num_q_heads);
+  if (s->kv_dtype != LBSR_KV_BF16 && s->kv_dtype != LBSR_KV_FP8_E4M3)
+    return fail(LBSR_E_INVALID, "kv_dtype %d unknown", s->kv_dtype);
+  if (s->max_blocks_per_seq < 1)
+    return fail(LBSR_E_INVALID, "max_blocks_per_seq %d < 1", s->max_blocks_per_seq);
+  if ((int64_t)s->max_blocks_per_seq * LBSR_PAGE_SIZE > INT32_MAX)
+    return fail(LBSR_E_INVALID, "max_blocks_per_seq %d too large", s->max_blocks_per_seq);
+  if (s->num_pages < 1 || s->num_pages > INT32_MAX)
+    return fail(LBSR_E_INVALID, "num_pages %lld out of [1, 2^31)", (long long)s->num_pages);
+  if (s->page_stride < LBSR_TILE_ELEMS || s->page_stride % LBSR_TILE_ELEMS ||
+      s->head_stride < LBSR_TILE_ELEMS || s->head_stride % LBSR_TILE_ELEMS)
+    return fail(LBSR_E_INVALID, "page_stride %lld / head_stride %lld must be positive multiples of 8192",
+                (long long)s->page_stride, (long long)s->head_stride);
+  const bool page_major = s->page_stride >= (int64_t)s->num_kv_heads * s->head_stride;
+  const bool head_major = s->head_stride >= s->num_pages * s->page_stride;
+  if (!page_major && !head_major)
+    return fail(LBSR_E_INVALID, "page_stride/head_stride make tiles overlap");
+  if (batch < 1) return fail(LBSR_E_INVALID, "batch %d < 1", batch);
+  if (batch > lbsr::kMaxBatch)
+    return fail(LBSR_E_UNSUPPORTED, "batch %d > %d", batch, lbsr::kMaxBatch);
+  if ((int64_t)batch * s->max_blocks_per_seq > INT32_MAX)
+    return fail(LBSR_E_UNSUPPORTED, "batch * max_blocks_per_seq exceeds 2^31 tiles");
+  return LBSR_OK;
+}
+
+lbsr_status check_params(const lbsr_params* p, int32_t kv_dtype) {
+  if (!p) return fail(LBSR_E_INVALID, "params is NULL");
+  if (!(p->rope_theta > 0) || !isfinite(p->rope_theta))
+    return fail(LBSR_E_INVALID, "rope_theta %g must be finite and > 0", p->rope_theta);
+  if (!(p->rms_eps >= 0) || !isfinite(p->rms_eps))
+    return fail(LBSR_E_INVALID, "rms_eps %g must be finite and >= 0", (double)p->rms_eps);
+  if (p->norm_before_rope != 0 && p->norm_before_rope != 1)
+    return fail(LBSR_E_INVALID, "norm_before_rope must be 0 or 1");
+  if (!(p->sm_scale >= 0) || !isfinite(p->sm_scale))
+    return fail(LBSR_E_INVALID, "sm_scale %g must be finite and >= 0", (double)p->sm_scale);
+  if (kv_dtype == LBSR_KV_FP8_E4M3 &&
+      (!(p->k_scale > 0) || !isfinite(p->k_scale) || !(p->v_scale > 0) || !isfinite(p->v_scale)))
+    return fail(LBSR_E_INVALID, "k_scale %g / v_scale %g must be finite and > 0",
+                (double)p->k_scale, (double)p->v_scale);
+  return LBSR_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sched_cfg* cfg,
+                           lbsr_ws_layout* out) {
+  LBSR_CHECK(check_shape(shape, batch));
+  if (!cfg) return fail(LBSR_E_INVALID, "cfg is NULL");
+  if (!out) return fail(LBSR_E_INVALID, "out is NULL");
+  if (cfg->sched != LBSR_SCHED_DYNAMIC && cfg->sched != LBSR_SCHED_STATIC)
+    return fail(LBSR_E_INVALID, "sched %d unknown", cfg->sched);
+  if (cfg->reserved != 0) return fail(LBSR_E_INVALID, "cfg.reserved must be 0");
+  if (cfg->num_workers < 0 || cfg->num_workers > 65536)
+    return fail(LBSR_E_INVALID, "num_workers %d out of [0, 65536]", cfg->num_workers);
+  if (cfg->static_splits < 0 || cfg->static_splits > 65536)
+    return fail(LBSR_E_INVALID, "static_splits %d out of [0, 65536]", cfg->static_splits);
+  int32_t P = cfg->num_workers;
+  if (P == 0) {
+    DeviceInfo d;
+    LBSR_CHECK(current_device(&d));
+    P = d.cu_count;
+  }
+  int64_t W, cmax;
+  int32_t S = 0;
+  if (cfg->sched == LBSR_SCHED_DYNAMIC) {
+    W = P;
+    cmax = (int64_t)P + batch - 1;
+  } else {
+    S = cfg->static_splits ? cfg->static_splits : (P / batch > 1 ? P / batch : 1);
+    W = (int64_t)batch * S;
+    cmax = W;
+  }
+  if (W > (1 << 22)) return fail(LBSR_E_UNSUPPORTED, "%lld workers is too many", (long long)W);
+  const int64_t Hq = shape->num_q_heads;
+  size_t off = 0;
+  memset(out, 0, sizeof *out);
+  out->error_word = off;   off = align256(off + 4);
+  out->cu_tiles = off;     off = align256(off + 4 * (size_t)(batch + 1));
+  out->worker_chunk = off; off = align256(off + 4 * (size_t)(W + 1));
+  out->chunks = off;       off = align256(off + 16 * (size_t)cmax);
+  out->seq_chunk = off;    off = align256(off + 4 * (size_t)(batch + 1));
+  out->seq_len_eff = off;  off = align256(off + 4 * (size_t)batch);
+  out->partial_o = off;    off = align256(off + 4 * (size_t)cmax * Hq * LBSR_HEAD_DIM);
+  out->partial_lse = off;  off = align256(off + 4 * (size_t)cmax * Hq);
+  out->total = off;
+  out->num_workers = (int32_t)W;
+  out->max_chunks = (int32_t)cmax;
+  out->static_splits = S;
+  return LBSR_OK;
+}
+
+lbsr::PlanPtrs plan_ptrs(void* ws, const lbsr_ws_layout& l) {
+  char* base = (char*)ws;
+  lbsr::PlanPtrs p;
+  p.error_word = (int32_t*)(base + l.error_word);
+  p.cu_tiles = (int32_t*)(base + l.cu_tiles);
+  p.worker_chunk = (int32_t*)(base + l.worker_chunk);
+  p.chunks = (int32_t*)(base + l.chunks);
+  p.seq_chunk = (int32_t*)(base + l.seq_chunk);
+  p.seq_len_eff = (int32_t*)(base + l.seq_len_eff);
+  p.partial_o = (float*)(base + l.partial_o);
+  p.partial_lse = (float*)(base + l.partial_lse);
+  return p;
+}
+
+lbsr::Geometry geometry(const lbsr_shape* s, int32_t batch) {
+  lbsr::Geometry g;
+  g.batch = batch;
+  g.num_q_heads = s->num_q_heads;
+  g.num_kv_heads = s->num_kv_heads;
+  g.group = s->num_q_heads / s->num_kv_heads;
+  g.max_blocks = s->max_blocks_per_seq;
+  g.pad = 0;
+  g.num_pages = s->num_pages;
+  g.page_stride = s->page_stride;
+  g.head_stride = s->head_stride;
+  return g;
+}
+
+lbsr_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LBSR_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return LBSR_OK;
+}
+
+lbsr_status check_workspace(void* ws, size_t ws_bytes, const lbsr_ws_layout& l) {
+  LBSR_CHECK(check_ptr(ws, 256, "workspace"));
+  if (ws_bytes < l.total)
+    return fail(LBSR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, l.total);
+  return LBSR_OK;
+}
+
+// ---- the four stages, validated separately so each entry point can reuse them ----
+
+lbsr_status validate_prologue(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                              const void* q, const void* k, const void* v, const int32_t* positions,
+                              const void* wq, const void* wk, const int32_t* bt, void* kc, void* vc,
+                              void* q_out, const int32_t* error_word) {
+  LBSR_CHECK(check_shape(shape, batch));
+  LBSR_CHECK(check_params(params, shape->kv_dtype));
+  LBSR_CHECK(check_ptr(q, 16, "q"));
+  LBSR_CHECK(check_ptr(k, 16, "k"));
+  LBSR_CHECK(check_ptr(v, 16, "v"));
+  LBSR_CHECK(check_ptr(positions, 4, "positions"));
+  LBSR_CHECK(check_ptr(wq, 16, "q_norm_w"));
+  LBSR_CHECK(check_ptr(wk, 16, "k_norm_w"));
+  LBSR_CHECK(check_ptr(bt, 4, "block_table"));
+  LBSR_CHECK(check_ptr(kc, 16, "k_cache"));
+  LBSR_CHECK(check_ptr(vc, 16, "v_cache"));
+  LBSR_CHECK(check_ptr(q_out, 16, "q_out"));
+  if (error_word && !aligned(error_word, 4)) return fail(LBSR_E_INVALID, "error_word misaligned");
+  if (q_out == q) return fail(LBSR_E_INVALID, "q_out may not alias q");
+  return LBSR_OK;
+}
+
+lbsr_status validate_attention(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                               const void* q_out, const void* kc, const void* vc, const int32_t* bt,
+                               void* out, const float* lse_out) {
+  LBSR_CHECK(check_shape(shape, batch));
+  LBSR_CHECK(check_params(params, shape->kv_dtype));
+  LBSR_CHECK(check_ptr(q_out, 16, "q_out"));
+  LBSR_CHECK(check_ptr(kc, 16, "k_cache"));
+  LBSR_CHECK(check_ptr(vc, 16, "v_cache"));
+  LBSR_CHECK(check_ptr(bt, 4, "block_table"));
+  LBSR_CHECK(check_ptr(out, 16, "out"));
+  if (lse_out && !aligned(lse_out, 4)) return fail(LBSR_E_INVALID, "lse_out misaligned");
+  return LBSR_OK;
+}
+
+lbsr_status run_prologue(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                         const void* q, const void* k, const void* v, const int32_t* positions,
+                         const void* wq, const void* wk, const int32_t* bt, void* kc, void* vc,
+                         void* q_out, int32_t* error_word, hipStream_t stream) {
+  const lbsr::Geometry geo = geometry(shape, batch);
+  const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
+  return hip_status(lbsr::launch_prologue(geo, fp8, q, k, v, positions, wq, wk, bt, kc, vc, q_out,
+                                          error_word, params->rope_theta, (double)params->rms_eps,
+                                          params->norm_before_rope, fp8 ? params->k_scale : 1.0,
+                                          fp8 ? params->v_scale : 1.0, stream),
+                    "prologue launch");
+}
+
+lbsr_status run_plan(const lbsr_shape* shape, int32_t batch, const int32_t* seq_lens,
+                     const lbsr_sched_cfg* cfg, const lbsr_ws_layout& l, void* ws, hipStream_t stream) {
+  return hip_status(lbsr::launch_plan(seq_lens, batch, shape->max_blocks_per_seq,
+                                      cfg->sched == LBSR_SCHED_DYNAMIC, l.num_workers,
+                                      l.static_splits, plan_ptrs(ws, l), stream),
+                    "plan launch");
+}
+
+float score_scale_log2(const lbsr_params* p, int32_t kv_dtype) {
+  const double sm = p->sm_scale > 0 ? (double)p->sm_scale : 1.0 / sqrt((double)LBSR_HEAD_DIM);
+  const double ks = kv_dtype == LBSR_KV_FP8_E4M3 ? (double)p->k_scale : 1.0;
+  return (float)(sm * ks * 1.4426950408889634074);
+}
+
+lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                      const void* q_out, const void* kc, const void* vc, const int32_t* bt,
+                      const lbsr_ws_layout& l, void* ws, void* out, float* lse_out,
+                      hipStream_t stream) {
+  const lbsr::Geometry geo = geometry(shape, batch);
+  const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
+  return hip_status(lbsr::launch_split_attention(geo, fp8, l.num_workers, q_out, kc, vc, bt,
+                                                 plan_ptrs(ws, l), out, lse_out,
+                                                 score_scale_log2(params, shape->kv_dtype),
+                                                 fp8 ? params->v_scale : 1.0f, stream),
+                    "split attention launch");
+}
+
+lbsr_status run_combine(const lbsr_shape* shape, int32_t batch, const lbsr_ws_layout& l, void* ws,
+                        void* out, float* lse_out, hipStream_t stream) {
+  const lbsr::Geometry geo = geometry(shape, batch);
+  return hip_status(lbsr::launch_combine(geo, plan_ptrs(ws, l), out, lse_out, stream),
+                    "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lbsr_abi_version(void) { return LBSR_ABI_VERSION; }
+
+const char* lbsr_status_string(lbsr_status status) {
+  switch (status) {
+    case LBSR_OK: return "LBSR_OK";
+    case LBSR_E_INVALID: return "LBSR_E_INVALID: invalid argument";
+    case LBSR_E_UNSUPPORTED: return "LBSR_E_UNSUPPORTED: unsupported shape or device";
+    case LBSR_E_WORKSPACE: return "LBSR_E_WORKSPACE: workspace too small";
+    case LBSR_E_HIP: return "LBSR_E_HIP: HIP runtime error";
+  }
+  return "unknown lbsr_status";
+}
+
+const char* lbsr_last_error(void) { return g_last_error; }
+
+lbsr_status lbsr_device_workers(int device, int32_t* out) {
+  g_last_error[0] = 0;
+  if (!out) return fail(LBSR_E_INVALID, "out is NULL");
+  DeviceInfo d;
+  LBSR_CHECK(device_info(device, &d));
+  if (!d.gfx950)
+    return fail(LBSR_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950", device, d.arch);
+  *out = d.cu_count;
+  return LBSR_OK;
+}
+
+lbsr_status lbsr_workspace_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sched_cfg* cfg,
+                                  lbsr_ws_layout* out) {
+  g_last_error[0] = 0;
+  return compute_layout(shape, batch, cfg, out);
+}
+
+lbsr_status lbsr_workspace_size(const lbsr_shape* shape, int32_t batch, const lbsr_sched_cfg* cfg,
+                                size_t* bytes) {
+  g_last_error[0] = 0;
+  if (!bytes) return fail(LBSR_E_INVALID, "bytes is NULL");
+  lbsr_ws_layout l;
+  LBSR_CHECK(compute_layout(shape, batch, cfg, &l));
+  *bytes = l.total;
+  return LBSR_OK;
+}
+
+lbsr_status lbsr_rope_norm_kv_write(const lbsr_shape* shape, const lbsr_params* params,
+                                    int32_t batch, const void* q, const void* k, const void* v,
+                                    const int32_t* positions, const void* q_norm_w,
+                                    const void* k_norm_w, const int32_t* block_table,
+                                    void* k_cache, void* v_cache, void* q_out, int32_t* error_word,
+                                    void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(validate_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
+                               block_table, k_cache, v_cache, q_out, error_word));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  return run_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w, block_table,
+                      k_cache, v_cache, q_out, error_word, (hipStream_t)stream);
+}
+
+lbsr_status lbsr_plan(const lbsr_shape* shape, int32_t batch, const int32_t* seq_lens,
+                      const lbsr_sched_cfg* cfg, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  lbsr_ws_layout l;
+  LBSR_CHECK(compute_layout(shape, batch, cfg, &l));
+  LBSR_CHECK(check_ptr(seq_lens, 4, "seq_lens"));
+  LBSR_CHECK(check_workspace(workspace, ws_bytes, l));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  return run_plan(shape, batch, seq_lens, cfg, l, workspace, (hipStream_t)stream);
+}
+
+lbsr_status lbsr_attention(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                           const void* q_out, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const lbsr_sched_cfg* cfg, void* workspace,
+                           size_t ws_bytes, void* out, float* lse_out, void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(validate_attention(shape, params, batch, q_out, k_cache, v_cache, block_table, out,
+                                lse_out));
+  lbsr_ws_layout l;
+  LBSR_CHECK(compute_layout(shape, batch, cfg, &l));
+  LBSR_CHECK(check_workspace(workspace, ws_bytes, l));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  const hipStream_t s = (hipStream_t)stream;
+  LBSR_CHECK(run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
+                       lse_out, s));
+  return run_combine(shape, batch, l, workspace, out, lse_out, s);
+}
+
+static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                                    const void* q, const void* k, const void* v,
+                                    const int32_t* positions, const int32_t* seq_lens,
+                                    const void* q_norm_w, const void* k_norm_w,
+                                    const int32_t* block_table, void* k_cache, void* v_cache,
+                                    void* q_out, const lbsr_sched_cfg* cfg, void* workspace,
+                                    size_t ws_bytes, void* out, float* lse_out, void* stream,
+                                    float* kernel_ms) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(validate_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
+                               block_table, k_cache, v_cache, q_out, nullptr));
+  LBSR_CHECK(validate_attention(shape, params, batch, q_out, k_cache, v_cache, block_table, out,
+                                lse_out));
+  LBSR_CHECK(check_ptr(seq_lens, 4, "seq_lens"));
+  lbsr_ws_layout l;
+  LBSR_CHECK(compute_layout(shape, batch, cfg, &l));
+  LBSR_CHECK(check_workspace(workspace, ws_bytes, l));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  const hipStream_t s = (hipStream_t)stream;
+  int32_t* err = plan_ptrs(workspace, l).error_word;
+
+  hipEvent_t ev[5] = {};
+  if (kernel_ms) {
+    for (int i = 0; i < 5; ++i) {
+      const hipError_t e = hipEventCreate(&ev[i]);
+      if (e != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+        return hip_status(e, "hipEventCreate");
+      }
+    }
+  }
+  lbsr_status st = LBSR_OK;
+  auto mark = [&](int i) {
+    if (kernel_ms && st == LBSR_OK) st = hip_status(hipEventRecord(ev[i], s), "hipEventRecord");
+  };
+  // The plan clears the error word, so it runs first; it does not depend on the prologue.
+  mark(0);
+  if (st == LBSR_OK) st = run_plan(shape, batch, seq_lens, cfg, l, workspace, s);
+  mark(1);
+  if (st == LBSR_OK)
+    st = run_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w, block_table,
+                      k_cache, v_cache, q_out, err, s);
+  mark(2);
+  if (st == LBSR_OK)
+    st = run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
+                   lse_out, s);
+  mark(3);
+  if (st == LBSR_OK) st = run_combine(shape, batch, l, workspace, out, lse_out, s);
+  mark(4);
+  if (kernel_ms) {
+    if (st == LBSR_OK) st = hip_status(hipEventSynchronize(ev[4]), "hipEventSynchronize");
+    for (int i = 0; i < 4 && st == LBSR_OK; ++i)
+      st = hip_status(hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]), "hipEventElapsedTime");
+    for (int i = 0; i < 5; ++i) (void)hipEventDestroy(ev[i]);
+  }
+  return st;
+}
+
+lbsr_status lbsr_decode_step(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                             const void* q, const void* k, const void* v, const int32_t* positions,
+                             const int32_t* seq_lens, const void* q_norm_w, const void* k_norm_w,
+                             const int32_t* block_table, void* k_cache, void* v_cache, void* q_out,
+                             const lbsr_sched_cfg* cfg, void* workspace, size_t ws_bytes, void* out,
+                             float* lse_out, void* stream) {
+  return decode_step_impl(shape, params, batch, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
+                          block_table, k_cache, v_cache, q_out, cfg, workspace, ws_bytes, out,
+                          lse_out, stream, nullptr);
+}
+
+lbsr_status lbsr_decode_step_timed(const lbsr_shape* shape, const lbsr_params* params,
+                                   int32_t batch, const void* q, const void* k, const void* v,
+                                   const int32_t* positions, const int32_t* seq_lens,
+                                   const void* q_norm_w, const void* k_norm_w,
+                                   const int32_t* block_table, void* k_cache, void* v_cache,
+                                   void* q_out, const lbsr_sched_cfg* cfg, void* workspace,
+                                   size_t ws_bytes, void* out, float* lse_out, void* stream,
+                                   float* kernel_ms) {
+  if (!kernel_ms) return fail(LBSR_E_INVALID, "kernel_ms is NULL");
+  return decode_step_impl(shape, params, batch, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
+                          block_table, k_cache, v_cache, q_out, cfg, workspace, ws_bytes, out,
+                          lse_out, stream, kernel_ms);
+}
+
+}  // extern "C"

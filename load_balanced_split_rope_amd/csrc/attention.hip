@@ -1,0 +1,388 @@
+// Split attention over scheduled 64-token tiles, and the log-sum-exp merge.
+//
+// [A] "Why does dynamic scheduling matter in attention?" splits the KV range
+// of a sequence across compute units (split-KV) in 64-token tiles; a split's
+// partial result then has to be merged.  Each chunk of the schedule is one
+// online-softmax pass (running max, running sum, rescaled accumulator) over
+// its tiles; a sequence cut into several chunks is merged with log-sum-exp
+// weights in ascending chunk order.  [A] "Two new HPC backends in the vLLM
+// ecosystem": 8 query heads share each KV head, so one KV read serves the
+// whole group.
+//
+// Mapping on CDNA4 (wave64, matrix cores):
+//   * workgroup = one worker of the schedule; wave = one KV head of it.
+//   * S^T[64 tokens][16 cols] = K[64][128] . Q^T[128][16] with
+//     v_mfma_f32_16x16x32_bf16 (the 8 q heads of the group fill 8 of the 16
+//     columns; the rest are zero): 4 token blocks x 4 channel steps.
+//   * O^T[128][16] += V^T[128][64] . P^T[64][16]: 8 channel blocks x 2 token
+//     steps.  The score accumulator's lane layout is reused as the P^T operand
+//     without moving data: the V page layout orders tokens to match it.
+//   * every K or V fragment is one contiguous 1 KiB global read per wave
+//     (16 bytes per lane), straight into the matrix-core operand registers;
+//     the next tile's K and V are in flight while the current one is used.
+//   * FP8 E4M3 codes are widened to BF16 exactly (v_cvt_scalef32_pk_bf16_fp8
+//     with scale 1); k_scale folds into the softmax scale, v_scale into the
+//     output.
+//   * row max and row sum: 16 values per lane in registers, then two xor
+//     shuffles across the 4 lanes that hold the same column.
+
+#include "common.h"
+#include "launch.h"
+
+namespace lbsr {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// 8 E4M3 codes (two dwords) -> 8 BF16 values, exactly.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <bool kFp8>
+struct TileRegs {
+  static constexpr int kFrags = kFp8 ? 8 : 16;  // 1 KiB fragments per K (or V) tile
+  u32x4 k[kFrags];
+  u32x4 v[kFrags];
+};
+
+template <bool kFp8>
+__device__ __forceinline__ void load_frags(u32x4 (&dst)[TileRegs<kFp8>::kFrags],
+                                           const u32x4* __restrict__ tile, int lane) {
+#pragma unroll
+  for (int f = 0; f < TileRegs<kFp8>::kFrags; ++f) dst[f] = tile[f * kWave + lane];
+}
+
+// Page id of tile t, validated without branching: a bad id reads page 0 and
+// sets `bad` (reported once per chunk).
+__device__ __forceinline__ int fetch_page(const int32_t* __restrict__ row, int t, int64_t num_pages,
+                                          bool& bad) {
+  const int p = wave_uniform(row[t]);
+  const bool ok = p >= 0 && p < num_pages;
+  bad |= !ok;
+  return ok ? p : 0;
+}
+
+// Pairwise max / sum with lane l ^ 16 and lane l ^ 32 (VALU lane swaps, no LDS).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Online-softmax state of one (chunk, KV head) pass.
+struct SoftmaxState {
+  f32x4 O[8];   // O^T: lane holds channels 16*db + 4*kc + e of column col
+  float m;      // running max (log2 domain), uniform over the 4 lanes of a column
+  float lsum;   // this lane's share of the running sum
+};
+
+// One 64-token tile: scores, online softmax update, P.V.  When kPrefetch, the
+// next tile's K fragments are requested right after the scores are formed and
+// its V fragments right after P.V, so a tile's loads overlap the previous
+// tile's arithmetic.  `rem` = valid rows of this tile (1..64).
+template <bool kFp8, bool kPrefetch>
+__device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
+                                            const bf16x8 (&qB)[4], int rem, int kc, int lane,
+                                            float score_scale_log2, const u32x4* next_k,
+                                            const u32x4* next_v) {
+  constexpr int NF = TileRegs<kFp8>::kFrags;
+  // ---- scores: S^T[token][col], lane holds tokens 16*tb + 4*kc + e ----
+  f32x4 S[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 a;
+      if constexpr (kFp8) {
+        const u32x4 w = R.k[2 * tb + (s >> 1)];
+        a = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+      } else {
+        a = as_bf16x8(R.k[4 * tb + s]);
+      }
+      acc = mfma_bf16(a, qB[s], acc);
+    }
+    S[tb] = acc;
+  }
+  if constexpr (kPrefetch) {
+    // keep the scheduler from hoisting the next loads above the MFMAs that
+    // still read these registers (that would need a second register set)
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<kFp8>(R.k, next_k, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- online softmax (log2 domain) ----
+  float p[16];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[4 * tb + e] = S[tb][e] * score_scale_log2;
+  if (rem < kPage) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (16 * tb + 4 * kc + e >= rem) p[4 * tb + e] = -__builtin_inff();
+  }
+  float mx = p[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, p[i]);
+  mx = max_xor32(max_xor16(mx));
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = fast_exp2(st.m - m_new);
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = fast_exp2(p[i] - m_new);
+    psum += p[i];
+  }
+  st.lsum = st.lsum * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.O[i] *= alpha;
+  // P^T operand for token step s: elements e<4 from token block 2s, e>=4 from 2s+1
+  bf16x8 pB[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)p[8 * s + e];
+
+  // ---- rows past the sequence end hold anything (even NaN): zero their V ----
+  if (rem < kPage) {
+    if constexpr (kFp8) {
+      // dword j of a lane holds tokens 16*j + 4*kc + (0..3), one per byte
+      uint32_t keep[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t mk = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * j + 4 * kc + i < rem) mk |= 0xFFu << (8 * i);
+        keep[j] = mk;
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R.v[f][j] &= keep[j];
+    } else {
+      // fragment 2*db + s, dword j holds tokens 16*(2s + j/2) + 4*kc + 2*(j%2) + (0,1)
+      uint32_t keep[2][4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t0k = 16 * (2 * s + (j >> 1)) + 4 * kc + 2 * (j & 1);
+          keep[s][j] = (t0k < rem ? 0xFFFFu : 0u) | (t0k + 1 < rem ? 0xFFFF0000u : 0u);
+        }
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) R.v[2 * db + s][j] &= keep[s][j];
+    }
+  }
+
+  // ---- O^T[channel][col] += V^T . P^T ----
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 a;
+      if constexpr (kFp8) {
+        const u32x4 w = R.v[db];
+        a = s ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+      } else {
+        a = as_bf16x8(R.v[2 * db + s]);
+      }
+      st.O[db] = mfma_bf16(a, pB[s], st.O[db]);
+    }
+  }
+  if constexpr (kPrefetch) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<kFp8>(R.v, next_v, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
+    Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table, PlanPtrs plan,
+    uint16_t* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
+    float out_scale) {
+  constexpr int kElemBytes = kFp8 ? 1 : 2;
+  const int worker = blockIdx.x;
+  const int c_begin = wave_uniform(plan.worker_chunk[worker]);
+  const int c_end = wave_uniform(plan.worker_chunk[worker + 1]);
+  if (c_begin >= c_end) return;
+
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;  // matrix column = q head inside the group
+  const int kc = lane >> 4;   // which 8-element slice of the contraction this lane feeds
+  const int nwaves = blockDim.x >> 6;
+  const int Hq = geo.num_q_heads, G = geo.group;
+
+  for (int g = threadIdx.x >> 6; g < geo.num_kv_heads; g += nwaves) {
+    for (int c = c_begin; c < c_end; ++c) {
+      const int32_t* ch = plan.chunks + 4 * (size_t)c;
+      const int b = wave_uniform(ch[0]);
+      const int t0 = wave_uniform(ch[1]);
+      const int t1 = wave_uniform(ch[2]);
+      const int L = wave_uniform(plan.seq_len_eff[b]);
+      const bool single = wave_uniform(plan.seq_chunk[b + 1] - plan.seq_chunk[b]) == 1;
+      const int32_t* bt_row = block_table + (size_t)b * geo.max_blocks;
+
+      // Q^T operand: column col = q head g*G + col (zero past the group), channels
+      // 32*s + 8*kc .. +8 for contraction step s.
+      bf16x8 qB[4];
+      if (col < G) {
+        const u32x4* qp =
+            (const u32x4*)(q_out + ((size_t)b * Hq + (size_t)g * G + col) * kHeadDim) + kc;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(qp[4 * s]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+      }
+
+      SoftmaxState st;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.m = -__builtin_inff();
+      st.lsum = 0.f;
+
+      const size_t head_off = (size_t)g * geo.head_stride;
+      auto tile_ptr = [&](const uint8_t* pool, int page) {
+        return (const u32x4*)(pool + ((size_t)page * geo.page_stride + head_off) * kElemBytes);
+      };
+
+      bool bad_page = false;
+      int page = fetch_page(bt_row, t0, geo.num_pages, bad_page);
+      TileRegs<kFp8> R;
+      load_frags<kFp8>(R.k, tile_ptr(k_pool, page), lane);
+      load_frags<kFp8>(R.v, tile_ptr(v_pool, page), lane);
+      // all tiles but the last prefetch their successor; the last one is peeled
+      // so the loop body has no conditional loads
+      for (int t = t0; t < t1 - 1; ++t) {
+        const int next = fetch_page(bt_row, t + 1, geo.num_pages, bad_page);
+        attend_tile<kFp8, true>(R, st, qB, L - t * kPage, kc, lane, score_scale_log2,
+                                tile_ptr(k_pool, next), tile_ptr(v_pool, next));
+      }
+      attend_tile<kFp8, false>(R, st, qB, L - (t1 - 1) * kPage, kc, lane, score_scale_log2,
+                               nullptr, nullptr);
+      if (bad_page && lane == 0) atomicOr(plan.error_word, (int32_t)kErrPage);
+      const float m = st.m;
+      const float lsum = st.lsum;
+      const f32x4* O = st.O;
+
+      // ---- finish the chunk ----
+      const float l = sum_xor32(sum_xor16(lsum));
+      const float scale = out_scale / l;
+      const float lse2 = m + __builtin_amdgcn_logf(l);  // log2
+      if (col < G) {
+        const int h = g * G + col;
+        if (single) {
+          uint16_t* o = out + ((size_t)b * Hq + h) * kHeadDim + 4 * kc;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(O[db][e] * scale);
+            *(bf16x4*)(o + 16 * db) = v4;
+          }
+          if (kc == 0 && lse_out) lse_out[(size_t)b * Hq + h] = lse2 * kLn2;
+        } else {
+          float* po = plan.partial_o + ((size_t)c * Hq + h) * kHeadDim + 4 * kc;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) *(f32x4*)(po + 16 * db) = O[db] * scale;
+          if (kc == 0) plan.partial_lse[(size_t)c * Hq + h] = lse2;
+        }
+      }
+    }
+  }
+}
+
+// Merge of the chunks of every sequence that has more than one: one wave per
+// (sequence, q head); lane l owns channels 2l and 2l+1.
+__global__ __launch_bounds__(256) void combine_kernel(Geometry geo, PlanPtrs plan,
+                                                      uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse_out) {
+  const int b = blockIdx.y;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int Hq = geo.num_q_heads;
+  if (h >= Hq) return;
+  const int c0 = plan.seq_chunk[b], c1 = plan.seq_chunk[b + 1];
+  if (c1 - c0 <= 1) return;  // written directly by the split kernel
+  const int lane = threadIdx.x & 63;
+  const float* lse = plan.partial_lse;
+  float mx = -__builtin_inff();
+  for (int c = c0 + lane; c < c1; c += kWave) mx = fmaxf(mx, lse[(size_t)c * Hq + h]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+  float ws = 0.f;
+  for (int c = c0 + lane; c < c1; c += kWave) ws += fast_exp2(lse[(size_t)c * Hq + h] - mx);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) ws += __shfl_xor(ws, d, kWave);
+  const float inv = 1.0f / ws;
+  f32x2 acc = {0.f, 0.f};
+  for (int c = c0; c < c1; ++c) {  // ascending chunk order
+    const float wgt = fast_exp2(lse[(size_t)c * Hq + h] - mx) * inv;
+    const f32x2 o = *(const f32x2*)(plan.partial_o + ((size_t)c * Hq + h) * kHeadDim + 2 * lane);
+    acc += wgt * o;
+  }
+  bf16x2 r = {(__bf16)acc[0], (__bf16)acc[1]};
+  *(bf16x2*)(out + ((size_t)b * Hq + h) * kHeadDim + 2 * lane) = r;
+  if (lane == 0 && lse_out) lse_out[(size_t)b * Hq + h] = (mx + __builtin_amdgcn_logf(ws)) * kLn2;
+}
+
+hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers,
+                                  const void* q_out, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const PlanPtrs& plan, void* out,
+                                  float* lse_out, float score_scale_log2, float out_scale,
+                                  hipStream_t stream) {
+  const int waves = geo.num_kv_heads < kMaxAttnWaves ? geo.num_kv_heads : kMaxAttnWaves;
+  if (fp8) {
+    split_attention_kernel<true><<<num_workers, waves * kWave, 0, stream>>>(
+        geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
+        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale);
+  } else {
+    split_attention_kernel<false><<<num_workers, waves * kWave, 0, stream>>>(
+        geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
+        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
+                          hipStream_t stream) {
+  dim3 grid((geo.num_q_heads + 3) / 4, geo.batch);
+  combine_kernel<<<grid, 256, 0, stream>>>(geo, plan, (uint16_t*)out, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace lbsr

@@ -1,0 +1,86 @@
+// Shared definitions for the lbsr HIP kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lbsr {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 64;          // tokens per page = tokens per scheduled tile
+constexpr int kTileElems = kHeadDim * kPage;
+constexpr int kWave = 64;
+constexpr int kMaxGroup = 16;      // q heads per KV head that one matrix-core column block holds
+constexpr int kMaxBatch = 16384;   // the plan keeps per-sequence prefix sums in LDS
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxAttnWaves = 8;   // waves (KV heads in flight) per attention workgroup
+
+enum : int32_t { kErrSeqLen = 1, kErrPage = 2, kErrPosition = 4 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Device pointers of the plan arrays inside a workspace.
+struct PlanPtrs {
+  int32_t* error_word;
+  int32_t* cu_tiles;      // [B+1]
+  int32_t* worker_chunk;  // [W+1]
+  int32_t* chunks;        // [C_max][4] = seq, first tile, end tile, worker
+  int32_t* seq_chunk;     // [B+1]
+  int32_t* seq_len_eff;   // [B]
+  float* partial_o;       // [C_max][Hq][128]
+  float* partial_lse;     // [C_max][Hq], log2 domain
+};
+
+// Geometry every kernel needs, passed by value.
+struct Geometry {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;          // Hq / Hkv
+  int32_t max_blocks;     // block_table row stride
+  int32_t pad;
+  int64_t num_pages;
+  int64_t page_stride;    // elements
+  int64_t head_stride;    // elements
+};
+
+// ---- element offsets inside one KV tile (the library's page layout) ----
+// r: token row [0,64), d: channel [0,128).  See include/lbsr.h.
+__device__ __forceinline__ int k_offset_bf16(int r, int d) {
+  return 512 * (4 * (r >> 4) + (d >> 5)) + 8 * (16 * ((d & 31) >> 3) + (r & 15)) + (d & 7);
+}
+__device__ __forceinline__ int v_offset_bf16(int r, int d) {
+  const int tb = r >> 4;
+  const int e = 4 * (tb & 1) + (r & 3);
+  return 512 * (2 * (d >> 4) + (tb >> 1)) + 8 * (16 * ((r & 15) >> 2) + (d & 15)) + e;
+}
+__device__ __forceinline__ int k_offset_fp8(int r, int d) {
+  const int s = d >> 5;
+  return 1024 * (2 * (r >> 4) + (s >> 1)) + 16 * (16 * ((d & 31) >> 3) + (r & 15)) + 8 * (s & 1) +
+         (d & 7);
+}
+__device__ __forceinline__ int v_offset_fp8(int r, int d) {
+  const int tb = r >> 4;
+  const int e = 4 * (tb & 1) + (r & 3);
+  return 1024 * (d >> 4) + 16 * (16 * ((r & 15) >> 2) + (d & 15)) + 8 * (tb >> 1) + e;
+}
+
+// ---- wave64 helpers ----
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <typename T>
+__device__ __forceinline__ T wave_uniform(T x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+}  // namespace lbsr

@@ -1,0 +1,30 @@
+// Host-side launchers of the lbsr kernels (one per kernel file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace lbsr {
+
+hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const void* k,
+                           const void* v, const int32_t* positions, const void* wq,
+                           const void* wk, const int32_t* block_table, void* k_cache,
+                           void* v_cache, void* q_out, int32_t* error_word, double theta,
+                           double eps, int norm_first, double k_scale, double v_scale,
+                           hipStream_t stream);
+
+hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, bool dynamic,
+                       int num_workers, int static_splits, const PlanPtrs& plan,
+                       hipStream_t stream);
+
+hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers,
+                                  const void* q_out, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const PlanPtrs& plan, void* out,
+                                  float* lse_out, float score_scale_log2, float out_scale,
+                                  hipStream_t stream);
+
+hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
+                          hipStream_t stream);
+
+}  // namespace lbsr

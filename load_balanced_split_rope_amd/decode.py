@@ -1,0 +1,242 @@
+"""Python face of the decode step: the same calls as include/lbsr.h, on torch tensors.
+
+Nothing here computes: it validates tensors, marshals pointers and the current
+torch stream, and calls liblbsr.  Device memory comes from torch.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _binding as B
+
+
+@dataclass
+class DecodeConfig:
+    """Geometry of the KV pools and the per-step constants (lbsr_shape + lbsr_params)."""
+    num_q_heads: int
+    num_kv_heads: int
+    kv_dtype: str                 # "bf16" or "fp8"
+    max_blocks_per_seq: int
+    num_pages: int
+    page_stride: int = 0          # elements; 0 -> num_kv_heads * 8192 (page-major pools)
+    head_stride: int = 0          # elements; 0 -> 8192
+    rope_theta: float = 1e4
+    rms_eps: float = 1e-6
+    norm_before_rope: bool = False
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    sm_scale: float = 0.0         # 0 -> 1/sqrt(128)
+
+    def shape(self):
+        return B.Shape(self.num_q_heads, self.num_kv_heads, B.HEAD_DIM, B.PAGE_SIZE,
+                       B.KV_BF16 if self.kv_dtype == "bf16" else B.KV_FP8_E4M3,
+                       self.max_blocks_per_seq, self.num_pages,
+                       self.page_stride or self.num_kv_heads * B.TILE_ELEMS,
+                       self.head_stride or B.TILE_ELEMS)
+
+    def params(self):
+        return B.Params(self.rope_theta, self.rms_eps, int(self.norm_before_rope),
+                        self.k_scale, self.v_scale, self.sm_scale)
+
+    @property
+    def cache_dtype(self):
+        return torch.bfloat16 if self.kv_dtype == "bf16" else torch.uint8
+
+    def pool_elems(self):
+        s = self.shape()
+        return max(s.num_pages * s.page_stride, s.num_kv_heads * s.head_stride)
+
+
+@dataclass
+class Schedule:
+    """lbsr_sched_cfg: "dynamic" (P workers, 0 = CU count) or "static" (S splits, 0 = P/B)."""
+    kind: str = "dynamic"
+    num_workers: int = 0
+    static_splits: int = 0
+
+    def cfg(self):
+        if self.kind not in ("dynamic", "static"):
+            raise ValueError(f"unknown schedule {self.kind!r}")
+        return B.SchedCfg(B.SCHED_DYNAMIC if self.kind == "dynamic" else B.SCHED_STATIC,
+                          self.num_workers, self.static_splits, 0)
+
+
+def device_workers(device=0):
+    out = ctypes.c_int32()
+    B._check(B.lib().lbsr_device_workers(int(device), ctypes.byref(out)))
+    return out.value
+
+
+def workspace_layout(cfg: DecodeConfig, batch: int, sched: Schedule):
+    out = B.WsLayout()
+    s, c = cfg.shape(), sched.cfg()
+    B._check(B.lib().lbsr_workspace_layout(ctypes.byref(s), int(batch), ctypes.byref(c),
+                                           ctypes.byref(out)))
+    return out
+
+
+def alloc_workspace(cfg: DecodeConfig, batch: int, sched: Schedule, device="cuda"):
+    lay = workspace_layout(cfg, batch, sched)
+    return torch.empty(lay.total, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- checks
+
+def _need(t, name, dtype, shape=None, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} elements, has {t.numel()}")
+
+
+def _check_pools(cfg, k_cache, v_cache):
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, cfg.cache_dtype, numel=cfg.pool_elems())
+
+
+def _check_table(cfg, block_table, batch):
+    _need(block_table, "block_table", torch.int32, shape=(batch, cfg.max_blocks_per_seq))
+
+
+# ---------------------------------------------------------------- entry points
+
+def rope_norm_kv_write(cfg: DecodeConfig, q, k, v, positions, q_norm_w, k_norm_w, block_table,
+                       k_cache, v_cache, q_out, error_word=None, stream=None):
+    """lbsr_rope_norm_kv_write: RoPE + QK-Norm + cache write of the new tokens."""
+    batch = q.shape[0]
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, B.HEAD_DIM
+    _need(q, "q", torch.bfloat16, shape=(batch, Hq, D))
+    _need(k, "k", torch.bfloat16, shape=(batch, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=(batch, Hkv, D))
+    _need(q_out, "q_out", torch.bfloat16, shape=(batch, Hq, D))
+    _need(positions, "positions", torch.int32, shape=(batch,))
+    _need(q_norm_w, "q_norm_w", torch.bfloat16, shape=(D,))
+    _need(k_norm_w, "k_norm_w", torch.bfloat16, shape=(D,))
+    _check_table(cfg, block_table, batch)
+    _check_pools(cfg, k_cache, v_cache)
+    if error_word is not None:
+        _need(error_word, "error_word", torch.int32, numel=1)
+    s, p = cfg.shape(), cfg.params()
+    B._check(B.lib().lbsr_rope_norm_kv_write(
+        ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
+        B._ptr(positions), B._ptr(q_norm_w), B._ptr(k_norm_w), B._ptr(block_table),
+        B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out), B._ptr(error_word), B._stream(stream)))
+
+
+def plan(cfg: DecodeConfig, seq_lens, sched: Schedule, workspace, stream=None):
+    """lbsr_plan: the step's tile schedule, written into ``workspace``."""
+    batch = seq_lens.shape[0]
+    _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+    _need(workspace, "workspace", torch.uint8)
+    s, c = cfg.shape(), sched.cfg()
+    B._check(B.lib().lbsr_plan(ctypes.byref(s), batch, B._ptr(seq_lens), ctypes.byref(c),
+                               B._ptr(workspace), workspace.numel(), B._stream(stream)))
+
+
+def attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, sched: Schedule,
+              workspace, out, lse_out=None, stream=None):
+    """lbsr_attention: split attention + merge over the planned schedule."""
+    batch = q_out.shape[0]
+    Hq, D = cfg.num_q_heads, B.HEAD_DIM
+    _need(q_out, "q_out", torch.bfloat16, shape=(batch, Hq, D))
+    _need(out, "out", torch.bfloat16, shape=(batch, Hq, D))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, shape=(batch, Hq))
+    _check_table(cfg, block_table, batch)
+    _check_pools(cfg, k_cache, v_cache)
+    _need(workspace, "workspace", torch.uint8)
+    s, p, c = cfg.shape(), cfg.params(), sched.cfg()
+    B._check(B.lib().lbsr_attention(
+        ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q_out), B._ptr(k_cache),
+        B._ptr(v_cache), B._ptr(block_table), ctypes.byref(c), B._ptr(workspace),
+        workspace.numel(), B._ptr(out), B._ptr(lse_out), B._stream(stream)))
+
+
+def _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table, k_cache,
+               v_cache, q_out, sched, workspace, out, lse_out):
+    batch = q.shape[0]
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, B.HEAD_DIM
+    _need(q, "q", torch.bfloat16, shape=(batch, Hq, D))
+    _need(k, "k", torch.bfloat16, shape=(batch, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=(batch, Hkv, D))
+    _need(q_out, "q_out", torch.bfloat16, shape=(batch, Hq, D))
+    _need(out, "out", torch.bfloat16, shape=(batch, Hq, D))
+    _need(positions, "positions", torch.int32, shape=(batch,))
+    _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+    _need(q_norm_w, "q_norm_w", torch.bfloat16, shape=(D,))
+    _need(k_norm_w, "k_norm_w", torch.bfloat16, shape=(D,))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, shape=(batch, Hq))
+    _check_table(cfg, block_table, batch)
+    _check_pools(cfg, k_cache, v_cache)
+    _need(workspace, "workspace", torch.uint8)
+    s, p, c = cfg.shape(), cfg.params(), sched.cfg()
+    return (ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
+            B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
+            B._ptr(block_table), B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out),
+            ctypes.byref(c), B._ptr(workspace), workspace.numel(), B._ptr(out),
+            B._ptr(lse_out)), (s, p, c)
+
+
+def decode_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table,
+                k_cache, v_cache, q_out, sched: Schedule, workspace, out, lse_out=None,
+                stream=None):
+    """lbsr_decode_step: plan, prologue, split attention and merge on one stream."""
+    args, keep = _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table,
+                            k_cache, v_cache, q_out, sched, workspace, out, lse_out)
+    B._check(B.lib().lbsr_decode_step(*args, B._stream(stream)))
+    del keep
+
+
+def decode_step_timed(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
+                      block_table, k_cache, v_cache, q_out, sched: Schedule, workspace, out,
+                      lse_out=None, stream=None):
+    """lbsr_decode_step_timed: the step with HIP events around each kernel (synchronises).
+
+    Returns milliseconds of (plan, prologue, split attention, merge)."""
+    args, keep = _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table,
+                            k_cache, v_cache, q_out, sched, workspace, out, lse_out)
+    ms = (ctypes.c_float * 4)()
+    B._check(B.lib().lbsr_decode_step_timed(*args, B._stream(stream), ms))
+    del keep
+    return list(ms)
+
+
+def read_plan(cfg: DecodeConfig, batch: int, sched: Schedule, workspace):
+    """Copy the plan arrays out of a workspace (synchronises; for tests and tools)."""
+    lay = workspace_layout(cfg, batch, sched)
+    ws = workspace.cpu().numpy()
+
+    def arr(off, n):
+        return ws[off:off + 4 * n].view(np.int32).copy()
+
+    W = lay.num_workers
+    worker_chunk = arr(lay.worker_chunk, W + 1)
+    n_chunks = int(worker_chunk[-1])
+    return {
+        "error_word": int(arr(lay.error_word, 1)[0]),
+        "cu_tiles": arr(lay.cu_tiles, batch + 1),
+        "worker_chunk": worker_chunk,
+        "chunks": arr(lay.chunks, 4 * n_chunks).reshape(-1, 4),
+        "seq_chunk": arr(lay.seq_chunk, batch + 1),
+        "seq_len_eff": arr(lay.seq_len_eff, batch),
+        "num_workers": W,
+        "max_chunks": lay.max_chunks,
+    }
+
+
+def read_error(cfg: DecodeConfig, batch: int, sched: Schedule, workspace):
+    """The workspace's sticky device error bits (synchronises)."""
+    lay = workspace_layout(cfg, batch, sched)
+    return int(workspace[lay.error_word:lay.error_word + 4].cpu().numpy().view(np.int32)[0])

@@ -45,7 +45,7 @@ def check_output(got, ref, kv_dtype, what="output", rel_l2=True):
     return max_abs, rl2
 
 
-def poison_indices(inp, w, kind):
+def poison_indices(inp, w, kind, spare_pages=True):
     """Pool indices (one pool) of every element the step must not read.
 
     Pages no sequence owns, the rows at or past L_b of each sequence's last
@@ -58,7 +58,9 @@ def poison_indices(inp, w, kind):
     owned = set()
     for b, L in enumerate(lens):
         owned.update(bt[b, :-(-L // PAGE_SIZE)].tolist())
-    idx = [np.arange(p * ps, p * ps + Hkv * hs) for p in range(inp["num_pages"]) if p not in owned]
+    idx = [np.zeros(0, dtype=np.int64)]
+    if spare_pages:
+        idx += [np.arange(p * ps, p * ps + Hkv * hs) for p in range(inp["num_pages"]) if p not in owned]
     d = np.arange(128)
     for b, L in enumerate(lens):
         t = (L - 1) // PAGE_SIZE
@@ -70,12 +72,13 @@ def poison_indices(inp, w, kind):
     return np.concatenate(idx)
 
 
-def poison_cache(inp, w):
-    """Fill every cache element the step must not read with NaN, in place."""
+def poison_cache(inp, w, spare_pages=True):
+    """Fill every cache element the step must not read with NaN, in place
+    (spare_pages=False leaves unowned pages alone, for very large pools)."""
     nan = BF16_NAN_BITS if w.kv_dtype == "bf16" else E4M3_NAN_CODE
     for key, kind in (("k_cache", "k"), ("v_cache", "v")):
         pool = inp[key]
-        ti = torch.from_numpy(poison_indices(inp, w, kind).astype(np.int64)).to(pool.device)
+        ti = torch.from_numpy(poison_indices(inp, w, kind, spare_pages).astype(np.int64)).to(pool.device)
         if pool.dtype == torch.bfloat16:
             pool.view(torch.int16).index_fill_(0, ti, int(np.int16(np.uint16(nan).view(np.int16))))
         else:

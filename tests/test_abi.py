@@ -1,0 +1,149 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-only parts (layout, validation) behave as documented.  Nothing here
+launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from load_balanced_split_rope_amd import _binding as B
+from load_balanced_split_rope_amd import DecodeConfig, Schedule, workspace_layout, LbsrError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "lbsr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lbsr_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("liblbsr.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 11
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.lbsr_abi_version() == 1
+    for st in range(5):
+        assert lib.lbsr_status_string(st).startswith(b"LBSR_")
+    assert lib.lbsr_status_string(99) == b"unknown lbsr_status"
+
+
+def cfg_mix():
+    return DecodeConfig(64, 8, "bf16", max_blocks_per_seq=2048, num_pages=4300)
+
+
+def test_workspace_layout_dynamic_and_static():
+    lay = workspace_layout(cfg_mix(), 32, Schedule("dynamic", num_workers=256))
+    assert lay.num_workers == 256 and lay.max_chunks == 256 + 31
+    offs = [lay.error_word, lay.cu_tiles, lay.worker_chunk, lay.chunks, lay.seq_chunk,
+            lay.seq_len_eff, lay.partial_o, lay.partial_lse, lay.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.partial_lse - lay.partial_o >= 4 * 287 * 64 * 128
+    st = workspace_layout(cfg_mix(), 32, Schedule("static", num_workers=256))
+    assert st.static_splits == 8 and st.num_workers == 256 and st.max_chunks == 256
+    st = workspace_layout(cfg_mix(), 32, Schedule("static", num_workers=256, static_splits=3))
+    assert st.static_splits == 3 and st.num_workers == 96
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, B.E_UNSUPPORTED), ("page_size", 16, B.E_UNSUPPORTED),
+    ("num_kv_heads", 3, B.E_INVALID), ("num_q_heads", 8 * 17, B.E_UNSUPPORTED),
+    ("kv_dtype", 7, B.E_INVALID), ("max_blocks_per_seq", 0, B.E_INVALID),
+    ("num_pages", 0, B.E_INVALID), ("page_stride", 100, B.E_INVALID),
+    ("head_stride", 8192 * 1000, B.E_INVALID),
+])
+def test_shape_validation(lib, field, value, status):
+    s = cfg_mix().shape()
+    setattr(s, field, value)
+    c = Schedule("dynamic", num_workers=256).cfg()
+    out = B.WsLayout()
+    got = lib.lbsr_workspace_layout(ctypes.byref(s), 32, ctypes.byref(c), ctypes.byref(out))
+    assert got == status, lib.lbsr_last_error()
+    assert lib.lbsr_last_error() != b""
+
+
+def test_batch_and_schedule_validation(lib):
+    s = cfg_mix().shape()
+    out = B.WsLayout()
+    for batch, cfg, status in [
+        (0, B.SchedCfg(0, 256, 0, 0), B.E_INVALID),
+        (20000, B.SchedCfg(0, 256, 0, 0), B.E_UNSUPPORTED),
+        (32, B.SchedCfg(5, 256, 0, 0), B.E_INVALID),
+        (32, B.SchedCfg(0, -1, 0, 0), B.E_INVALID),
+        (32, B.SchedCfg(0, 256, 0, 1), B.E_INVALID),
+    ]:
+        assert lib.lbsr_workspace_layout(ctypes.byref(s), batch, ctypes.byref(cfg),
+                                         ctypes.byref(out)) == status
+
+
+def test_entry_points_reject_bad_pointers_before_any_launch(lib):
+    """Null or misaligned pointers return LBSR_E_INVALID without touching a device."""
+    s = cfg_mix().shape()
+    p = cfg_mix().params()
+    c = Schedule("dynamic", num_workers=256).cfg()
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x10002)
+    assert lib.lbsr_plan(ctypes.byref(s), 32, nul, ctypes.byref(c), fake, 1 << 30, nul) == B.E_INVALID
+    assert lib.lbsr_plan(ctypes.byref(s), 32, fake, ctypes.byref(c), odd, 1 << 30, nul) == B.E_INVALID
+    assert lib.lbsr_plan(ctypes.byref(s), 32, fake, ctypes.byref(c), fake, 16, nul) == B.E_WORKSPACE
+    # q, k, v, positions, q_norm_w, k_norm_w, block_table, k_cache, v_cache, q_out, error_word
+    args = [fake] * 11
+    args[9] = odd                          # q_out misaligned
+    assert lib.lbsr_rope_norm_kv_write(ctypes.byref(s), ctypes.byref(p), 32, *args, nul) == B.E_INVALID
+    args = [fake] * 11
+    args[9] = args[0]                      # q_out aliases q
+    assert lib.lbsr_rope_norm_kv_write(ctypes.byref(s), ctypes.byref(p), 32, *args, nul) == B.E_INVALID
+    args = [fake] * 11
+    args[3] = nul                          # positions missing
+    assert lib.lbsr_rope_norm_kv_write(ctypes.byref(s), ctypes.byref(p), 32, *args, nul) == B.E_INVALID
+    assert lib.lbsr_attention(ctypes.byref(s), ctypes.byref(p), 32, fake, fake, fake, fake,
+                              ctypes.byref(c), fake, 1 << 30, nul, nul, nul) == B.E_INVALID
+
+
+def test_params_validation(lib):
+    s = cfg_mix().shape()
+    s.kv_dtype = B.KV_FP8_E4M3
+    c = Schedule("dynamic", num_workers=256).cfg()
+    fake = ctypes.c_void_p(0x10000)
+    for field, value in [("rope_theta", 0.0), ("rms_eps", -1.0), ("k_scale", 0.0),
+                         ("v_scale", float("inf")), ("sm_scale", float("nan")),
+                         ("norm_before_rope", 2)]:
+        p = DecodeConfig(64, 8, "fp8", 2048, 4300).params()
+        setattr(p, field, value)
+        got = lib.lbsr_attention(ctypes.byref(s), ctypes.byref(p), 32, fake, fake, fake, fake,
+                                 ctypes.byref(c), fake, 1 << 30, fake, fake, ctypes.c_void_p(0))
+        assert got == B.E_INVALID, field
+
+
+def test_python_layer_raises_on_status():
+    bad = DecodeConfig(64, 8, "bf16", max_blocks_per_seq=0, num_pages=10)
+    with pytest.raises(LbsrError, match="LBSR_E_INVALID"):
+        workspace_layout(bad, 4, Schedule("dynamic", num_workers=8))
+
+
+def test_binding_signatures_match_header(lib):
+    """Each ctypes prototype has as many parameters as the header declares."""
+    text = open(os.path.join(ROOT, "include", "lbsr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    seen = 0
+    for m in re.finditer(r"\b(lbsr_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        name, params = m.group(1), m.group(2).strip()
+        n = 0 if params in ("void", "") else len(params.split(","))
+        assert len(getattr(lib, name).argtypes) == n, name
+        seen += 1
+    assert seen == len(B.EXPORTS)

@@ -1,0 +1,83 @@
+"""Full-size workloads, in the launch configuration the benchmark times
+(dynamic over every CU, and the static baseline): the schedule bit-exact,
+every new token's q_out, sampled (sequence, head) outputs against the fp64
+oracle, and a zero-query run whose lse must be ln L for every sequence."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import load_balanced_split_rope_amd as lb
+from load_balanced_split_rope_amd import workloads as wl
+from checks import (poison_cache, host_step_inputs, oracle_cfg, check_output, to_f64, bits_u16)
+from gpu_util import device, run_step, compact_pools, remap_slots
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+FULL = ["uniform", "mix", "mix_fp8", "loguniform"]
+
+
+def sampled_checks(w, g, res, h, pro):
+    lens = np.asarray(w.seq_lens)
+    order = np.argsort(lens)
+    seqs = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2])})
+    G = w.num_q_heads // w.num_kv_heads
+    heads = sorted({0, G + 1, w.num_q_heads - 1})
+    kp, vp, bt, pmap = compact_pools(g, w, seqs)
+    cfg = oracle_cfg(g, w)
+    pro_c = remap_slots(pro, pmap)
+    ref = oracle.decode_attention(pro["q_out"], (kp, vp), pro_c, h["seq_lens"], bt, cfg,
+                                  seqs=seqs, heads=heads)
+    out = to_f64(res["out"])
+    lse = to_f64(res["lse"])
+    for (b, hh), (o, l) in ref.items():
+        check_output(out[b, hh], o, w.kv_dtype, f"output seq {b} head {hh}")
+        assert abs(lse[b, hh] - l) <= 1e-4 + 1e-5 * abs(l), (b, hh, lse[b, hh], l)
+    return len(ref)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload(name):
+    dev = device()
+    w = wl.named(name)
+    print(f"full workload {name}: B={w.batch} {w.kv_dtype}, generating on device", flush=True)
+    g = wl.make_inputs(w, device=dev)
+    poison_cache(g, w, spare_pages=False)
+    h = host_step_inputs(g)
+    pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                          h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
+                          kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    P = lb.device_workers(0)
+    for sched in (lb.Schedule("dynamic"), lb.Schedule("static")):
+        # the pools keep the pre-step contents the oracle reads: run on a copy
+        gg = dict(g)
+        gg["k_cache"], gg["v_cache"] = g["k_cache"].clone(), g["v_cache"].clone()
+        res = run_step(w, gg, sched)
+        assert res["error"] == 0
+        ref_plan = (oracle.plan_dynamic(w.seq_lens, P) if sched.kind == "dynamic"
+                    else oracle.plan_static(w.seq_lens, max(1, P // w.batch)))
+        got = res["plan"]
+        for key in ("cu_tiles", "worker_chunk", "chunks", "seq_chunk"):
+            assert np.array_equal(got[key], getattr(ref_plan, key)), key
+        assert np.array_equal(bits_u16(res["q_out"]), pro["q_out"]) or \
+            np.mean(bits_u16(res["q_out"]) != pro["q_out"]) < 1e-6
+        n = sampled_checks(w, gg, res, h, pro)
+        print(f"  {sched.kind}: plan exact, {n} sampled heads match", flush=True)
+        del gg, res
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["mix", "mix_fp8", "loguniform"])
+def test_full_zero_query_lse(name):
+    """Every (sequence, head) at full size: with q = 0 the lse is ln L."""
+    dev = device()
+    w = wl.named(name)
+    g = wl.make_inputs(w, device=dev)
+    g["q_norm_w"].zero_()
+    res = run_step(w, g, lb.Schedule("dynamic"))
+    lse = to_f64(res["lse"])
+    want = np.log(np.asarray(w.seq_lens, dtype=np.float64))[:, None]
+    err = np.abs(lse - want)
+    print(f"{name}: max |lse - ln L| = {err.max():.2e}", flush=True)
+    assert np.all(err <= 16 * np.finfo(np.float32).eps * np.maximum(want, 1))
