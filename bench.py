@@ -1,0 +1,301 @@
+"""Decode-step benchmark on one MI355X.
+
+One step = the whole hot path through lbsr_decode_step: the length-
+proportional tile plan, the fused RoPE + QK-Norm + KV-write prologue, split
+attention and the LSE merge, on the 1 x 131072 + 31 x 4096-token mix (64 q
+heads, 8 KV heads, head dim 128, BF16 cache, 64-token pages).  Inputs are
+seeded synthetic tensors already resident in HBM; two copies of the inputs
+(separate page pools) alternate between steps so the 256 MB Infinity Cache
+cannot serve a step's KV from the previous one.
+
+Prints one JSON line.  value = compulsory bytes per step / step time (GB/s).
+Also reported: the same for the FP8 cache, the static equal split-KV
+baseline (default S = floor(256/B) and the best S of a sweep), per-kernel
+times from HIP events on the launch stream, the split-attention kernel's
+roofline, and the fp64 CPU oracle timed on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import load_balanced_split_rope_amd as lb                      # noqa: E402
+from load_balanced_split_rope_amd import workloads as wl        # noqa: E402
+
+METRIC = ("decode-attn µs/step + achieved HBM GB/s (% peak), 1x128K+31x4K mix, BF16/FP8")
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_attention_traffic.json")
+
+
+def compulsory_bytes(w):
+    """Bytes the step must move: KV read, q/out, block table and lengths, prologue I/O."""
+    e = 2 if w.kv_dtype == "bf16" else 1
+    B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, 128
+    T = sum(w.tiles)
+    kv = sum(w.seq_lens) * Hkv * D * 2 * e
+    attn_qo = 2 * B * Hq * D * 2
+    meta = T * 4 + B * 4
+    pro_in = B * (Hq + 2 * Hkv) * D * 2 + 2 * D * 2 + B * 4 + B * 4
+    pro_out = B * Hq * D * 2 + 2 * B * Hkv * D * e
+    return {"kv": kv, "attention_q_out": attn_qo, "meta": meta, "prologue": pro_in + pro_out,
+            "total": kv + attn_qo + meta + pro_in + pro_out}
+
+
+def split_kernel_bytes(w):
+    """Algorithmic bytes of one split-attention launch: every KV element of every
+    (token, KV head) once, q once, the final output once, the block table once."""
+    e = 2 if w.kv_dtype == "bf16" else 1
+    B, Hq, Hkv, D = w.batch, w.num_q_heads, w.num_kv_heads, 128
+    return sum(w.seq_lens) * Hkv * D * 2 * e + 2 * B * Hq * D * 2 + sum(w.tiles) * 4
+
+
+class Case:
+    """Two independent input sets of one workload on the GPU, plus outputs."""
+
+    def __init__(self, w, dev):
+        self.w = w
+        self.sets = []
+        for copy in range(2):
+            g = wl.make_inputs(w, device=dev)
+            self.sets.append(g)
+        g = self.sets[0]
+        self.cfg = lb.DecodeConfig(w.num_q_heads, w.num_kv_heads, w.kv_dtype, g["max_blocks"],
+                                   g["num_pages"], rope_theta=w.rope_theta, rms_eps=w.rms_eps,
+                                   k_scale=w.k_scale, v_scale=w.v_scale)
+        self.q_out = torch.empty_like(g["q"])
+        self.out = torch.empty_like(g["q"])
+        self.lse = torch.empty(w.batch, w.num_q_heads, dtype=torch.float32, device=dev)
+        self.ws = {}
+
+    def workspace(self, sched):
+        key = (sched.kind, sched.num_workers, sched.static_splits)
+        if key not in self.ws:
+            self.ws[key] = lb.alloc_workspace(self.cfg, self.w.batch, sched,
+                                              device=self.q_out.device)
+        return self.ws[key]
+
+    def args(self, i, sched):
+        g = self.sets[i % 2]
+        return (self.cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"], g["q_norm_w"],
+                g["k_norm_w"], g["block_table"], g["k_cache"], g["v_cache"], self.q_out, sched,
+                self.workspace(sched), self.out, self.lse)
+
+    def step(self, i, sched):
+        lb.decode_step(*self.args(i, sched))
+
+    def timed_steps(self, sched, steps, warmup):
+        for i in range(warmup):
+            self.step(i, sched)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, sched)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    def kernel_times(self, sched, reps):
+        """Per-kernel ms (plan, prologue, split, merge): HIP events on the launch stream."""
+        ms = np.array([lb.decode_step_timed(*self.args(i, sched)) for i in range(reps)])
+        return np.median(ms, axis=0), ms.mean(axis=0)
+
+    def graph_ms(self, sched, steps):
+        """Step time with the step captured once in a graph and replayed."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(s):
+            for i in range(2):
+                self.step(i, sched)          # warm the workspace on this stream
+            torch.cuda.synchronize()
+            for i in range(2):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=s):
+                    self.step(i, sched)
+                graphs.append(gr)
+        torch.cuda.current_stream().wait_stream(s)
+        for i in range(4):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("attention.hip", "common.h"):
+        with open(os.path.join(ROOT, "load_balanced_split_rope_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kv_dtype):
+    """HBM bytes per split-attention launch from committed rocprofv3 counters,
+    or None if they were taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    entry = rec.get("workloads", {}).get(f"{workload}/{kv_dtype}")
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, dev):
+    """The fp64 oracle on the host: the whole step (plan, prologue, attention over
+    every sequence and head) on a fresh input set of the workload, drawn by the
+    seeded generator on the device and copied to the host untouched."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    g = wl.make_inputs(w, device=dev)
+    host = {k: g[k].cpu() for k in ("q", "k", "v", "q_norm_w", "k_norm_w", "positions",
+                                      "seq_lens", "block_table")}
+    bits = {k: host[k].view(torch.int16).numpy().view(np.uint16)
+            for k in ("q", "k", "v", "q_norm_w", "k_norm_w")}
+    if w.kv_dtype == "bf16":
+        kp = g["k_cache"].cpu().view(torch.int16).numpy().view(np.uint16)
+        vp = g["v_cache"].cpu().view(torch.int16).numpy().view(np.uint16)
+    else:
+        kp, vp = g["k_cache"].cpu().numpy(), g["v_cache"].cpu().numpy()
+    page_stride, head_stride = g["page_stride"], g["head_stride"]
+    del g
+    torch.cuda.empty_cache()
+    lens = host["seq_lens"].numpy().astype(np.int64)
+    bt = host["block_table"].numpy().astype(np.int64)
+    cfg = {"kv_dtype": w.kv_dtype, "k_scale": w.k_scale, "v_scale": w.v_scale,
+           "sm_scale": 1 / np.sqrt(128.0), "page_stride": page_stride,
+           "head_stride": head_stride, "num_kv_heads": w.num_kv_heads}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.plan_dynamic(lens, 256)
+        pro = oracle.prologue(bits["q"], bits["k"], bits["v"], host["positions"].numpy(),
+                              bits["q_norm_w"], bits["k_norm_w"], bt, theta=w.rope_theta,
+                              eps=w.rms_eps, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
+                              v_scale=w.v_scale)
+        oracle.decode_attention(pro["q_out"], (kp, vp), pro, lens, bt, cfg)
+        dt = time.perf_counter() - t0
+    nbytes = compulsory_bytes(w)["total"]
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole {w.name} step (plan, prologue for {w.batch} tokens, "
+                      f"full-softmax attention for all {w.batch} sequences x "
+                      f"{w.num_q_heads} heads), fp64 numpy, BLAS limited to 1 thread",
+            "seconds": round(dt, 2)}
+
+
+def measure(w, dev, P, steps, warmup, full):
+    """Dynamic step time, per-kernel times, and (full) graph time and static sweep."""
+    dyn = lb.Schedule("dynamic")
+    case = Case(w, dev)
+    r = {"ms": case.timed_steps(dyn, steps, warmup)}
+    _, kmean = case.kernel_times(dyn, max(20, min(steps, 100)))
+    r["kernel_ms"] = kmean
+    if full:
+        r["graph_ms"] = case.graph_ms(dyn, steps)
+        static = {}
+        for S in (0, 1, 2, 4, 8, 16, 32, 64):
+            sc = lb.Schedule("static", num_workers=P, static_splits=S)
+            static["default" if S == 0 else str(S)] = case.timed_steps(sc, max(20, steps // 4), 5)
+        r["static_ms"] = static
+    del case
+    torch.cuda.empty_cache()
+    return r
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mix", choices=["mix", "uniform"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline workload only: no graph, static sweep, FP8 or CPU legs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path here "
+              "is single-GPU and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    P = lb.device_workers(0)
+    full = not args.quick
+
+    w = wl.named(args.workload)
+    r = measure(w, dev, P, args.steps, args.warmup, full)
+    ms = r["ms"]
+    cb = compulsory_bytes(w)
+    value = cb["total"] / (ms * 1e-3) / 1e9
+    split_ms = float(r["kernel_ms"][2])
+    split_gbs = split_kernel_bytes(w) / (split_ms * 1e-3) / 1e9
+    names = ("plan", "prologue", "split_attention", "merge")
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{w.name}: 1 x 131072 + 31 x 4096 tokens" if w.name == "mix"
+                                else f"{w.name}: 32 x 4096 tokens"),
+                   "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": 128, "page": 64, "kv_cache": w.kv_dtype,
+                   "schedule": f"dynamic, {P} workers", "parallelism": "1 GPU"},
+        "us_per_step": round(ms * 1e3, 2),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "compulsory_bytes": cb["total"],
+        "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, r["kernel_ms"])},
+        "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, w.kv_dtype),
+                     "kernel": "split_attention_kernel<bf16>",
+                     "algorithmic_bytes": split_kernel_bytes(w)},
+        "cpu_baseline": None,
+    }
+    if full:
+        result["us_per_step_graph"] = round(r["graph_ms"] * 1e3, 2)
+        st = r["static_ms"]
+        result["static_us_per_step"] = {k: round(v * 1e3, 2) for k, v in st.items()}
+        best = min(v for k, v in st.items() if k != "default")
+        result["dynamic_speedup_vs_static"] = {"default_S": round(st["default"] / ms, 3),
+                                               "best_S": round(best / ms, 3)}
+        if w.name == "mix":
+            w8 = wl.named("mix_fp8")
+            r8 = measure(w8, dev, P, args.steps, args.warmup, full)
+            ms8 = r8["ms"]
+            cb8 = compulsory_bytes(w8)["total"]
+            sp8 = split_kernel_bytes(w8) / (float(r8["kernel_ms"][2]) * 1e-3) / 1e9
+            st8 = r8["static_ms"]
+            best8 = min(v for k, v in st8.items() if k != "default")
+            result["fp8"] = {
+                "workload": "mix_fp8: the same mix with an FP8 E4M3 cache "
+                            "(k scale 2^-5, v scale 2^-4)",
+                "us_per_step": round(ms8 * 1e3, 2),
+                "us_per_step_graph": round(r8["graph_ms"] * 1e3, 2),
+                "value_GBs": round(cb8 / (ms8 * 1e-3) / 1e9, 1),
+                "hbm_frac_step": round(cb8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, r8["kernel_ms"])},
+                "split_attention_GBs": round(sp8, 1),
+                "split_attention_frac": round(sp8 / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(w8.name, w8.kv_dtype),
+                "static_us_per_step": {k: round(v * 1e3, 2) for k, v in st8.items()},
+                "dynamic_speedup_vs_static": {"default_S": round(st8["default"] / ms8, 3),
+                                              "best_S": round(best8 / ms8, 3)},
+            }
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(w, dev)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

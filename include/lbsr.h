@@ -221,7 +221,8 @@ lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq
  *   lse_out[b][h] = ln sum_j exp(sm_scale * <q_out[b][h], K_j>)        (fp32)
  * with K_j = code*k_scale and V_j = code*v_scale for an FP8 cache.  Each
  * chunk is one online-softmax pass over its tiles; a sequence with several
- * chunks is merged by log-sum-exp weights in ascending chunk order.
+ * chunks is merged by log-sum-exp weights (chunks are summed in a fixed
+ * order, so the result is deterministic).
  *   q_out [batch][Hq][128] BF16   out [batch][Hq][128] BF16
  *   lse_out nullable float[batch][Hq]
  * Rows at or past L_b of a sequence's last page are never used, whatever
