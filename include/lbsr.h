@@ -122,8 +122,8 @@ typedef struct {
 
 typedef struct {
   int32_t sched;         /* lbsr_sched */
-  int32_t num_workers;   /* dynamic: P workers; 0 -> the device's CU count */
-  int32_t static_splits; /* static: S splits per sequence; 0 -> max(1, P / batch) */
+  int32_t num_workers;   /* dynamic: P workers in [1, 1024]; 0 -> the device's CU count */
+  int32_t static_splits; /* static: S splits per sequence in [1, 1024]; 0 -> max(1, P / batch) */
   int32_t reserved;      /* must be 0 */
 } lbsr_sched_cfg;
 

@@ -13,7 +13,8 @@ import threading
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblbsr.so")
+# LBSR_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("LBSR_LIB") or os.path.join(HERE, "liblbsr.so")
 
 HEAD_DIM = 128
 PAGE_SIZE = 64

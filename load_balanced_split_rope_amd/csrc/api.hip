@@ -143,10 +143,11 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
   if (cfg->sched != LBSR_SCHED_DYNAMIC && cfg->sched != LBSR_SCHED_STATIC)
     return fail(LBSR_E_INVALID, "sched %d unknown", cfg->sched);
   if (cfg->reserved != 0) return fail(LBSR_E_INVALID, "cfg.reserved must be 0");
-  if (cfg->num_workers < 0 || cfg->num_workers > 65536)
-    return fail(LBSR_E_INVALID, "num_workers %d out of [0, 65536]", cfg->num_workers);
-  if (cfg->static_splits < 0 || cfg->static_splits > 65536)
-    return fail(LBSR_E_INVALID, "static_splits %d out of [0, 65536]", cfg->static_splits);
+  // a sequence gets at most one chunk per worker or split; the merge handles 1024
+  if (cfg->num_workers < 0 || cfg->num_workers > 1024)
+    return fail(LBSR_E_INVALID, "num_workers %d out of [0, 1024]", cfg->num_workers);
+  if (cfg->static_splits < 0 || cfg->static_splits > 1024)
+    return fail(LBSR_E_INVALID, "static_splits %d out of [0, 1024]", cfg->static_splits);
   int32_t P = cfg->num_workers;
   if (P == 0) {
     DeviceInfo d;
@@ -302,8 +303,12 @@ lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_
 lbsr_status run_combine(const lbsr_shape* shape, int32_t batch, const lbsr_ws_layout& l, void* ws,
                         void* out, float* lse_out, hipStream_t stream) {
   const lbsr::Geometry geo = geometry(shape, batch);
-  return hip_status(lbsr::launch_combine(geo, plan_ptrs(ws, l), out, lse_out, stream),
-                    "combine launch");
+  // a sequence has at most one chunk per worker (dynamic) or split (static),
+  // and at most one per tile: the merge stages that many rows' lse in LDS
+  const int per_seq = l.static_splits ? l.static_splits : l.num_workers;
+  const int bound = per_seq < shape->max_blocks_per_seq ? per_seq : shape->max_blocks_per_seq;
+  return hip_status(lbsr::launch_combine(geo, plan_ptrs(ws, l), out, lse_out, bound, stream),
+                    "merge launch");
 }
 
 }  // namespace

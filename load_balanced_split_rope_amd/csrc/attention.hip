@@ -332,89 +332,126 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
 }
 
 // Merge of the chunks of every sequence that has more than one.
-// One 1024-thread workgroup per (KV head g, sequence b): the G q heads of the
-// group share the chunk rows partial_o[c][g*G .. g*G+G) (G*512 contiguous
-// bytes).  Waves < G first find each head's max and sum of 2^(lse - max) over
-// the chunks; then wave w accumulates chunks c0+w, c0+w+16, ..., with kVec
-// float4 of a row per lane and 16/kVec rows in flight, and the 16 per-wave
-// sums are added in wave order through LDS.  Fixed assignment and order:
-// deterministic.
-constexpr int kMergeWaves = 16;
+//
+// A sequence's n chunk rows (partial_o[c][g*G .. g*G+G) plus their log2-sum-
+// exp) are read in parallel: workgroup (s, g, b) owns channel slice s (128/S
+// channels of every head of KV group g, S slices) of sequence b.  A slice is
+// 32G/S float4 (at most 64), so one wave instruction covers 64/(32G/S) rows,
+// and each lane keeps kMergeUnroll rows in flight.  The first round of row
+// reads is issued before the lse are staged in LDS and turned into weights
+// 2^(lse - max) / sum per head, so the two overlap.  Per-(wave, row-lane)
+// sums are added in a fixed order: deterministic.
+#ifndef LBSR_MERGE_WAVES
+#define LBSR_MERGE_WAVES 4
+#endif
+#ifndef LBSR_MERGE_UNROLL
+#define LBSR_MERGE_UNROLL 16
+#endif
+#ifndef LBSR_MERGE_MIN_SLICES
+#define LBSR_MERGE_MIN_SLICES 4
+#endif
+constexpr int kMergeWaves = LBSR_MERGE_WAVES;
+constexpr int kMergeUnroll = LBSR_MERGE_UNROLL;
 
-template <int kVec>  // float4 per lane per chunk row: G*32/64 rounded up
-__global__ __launch_bounds__(kMergeWaves * kWave) void combine_kernel(Geometry geo, PlanPtrs plan,
-                                                                      uint16_t* __restrict__ out,
-                                                                      float* __restrict__ lse_out) {
-  constexpr int kUnroll = 16 / kVec;
-  const int g = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(Geometry geo, PlanPtrs plan,
+                                                                    uint16_t* __restrict__ out,
+                                                                    float* __restrict__ lse_out) {
+  constexpr int kThreads = kMergeWaves * kWave;
+  const int slice = blockIdx.x, nslices = gridDim.x, g = blockIdx.y, b = blockIdx.z;
   const int c0 = plan.seq_chunk[b], c1 = plan.seq_chunk[b + 1];
-  if (c1 - c0 <= 1) return;  // written directly by the split kernel
+  const int count = c1 - c0;
+  if (count <= 1) return;  // written directly by the split kernel
   const int Hq = geo.num_q_heads, G = geo.group;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float* lse = plan.partial_lse;
-  __shared__ float s_max[kMaxGroup], s_inv[kMaxGroup];
-  __shared__ f32x4 s_acc[kMergeWaves][kMaxGroup * 32];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t head0 = (size_t)g * G;
+  extern __shared__ float s_w[];                           // [count][G]: lse, then weights
+  __shared__ f32x4 s_acc[kThreads];                        // one partial sum per lane
 
-  if (wave < G) {
-    const int h = g * G + wave;
+  // Loads below are unconditional (indices clamped into range, results of the
+  // clamped ones discarded) so that a thread's loads issue back to back.
+  const int head_vec = 32 / nslices;      // float4 of one head in a slice
+  const int per_row = G * head_vec;       // float4 of one row's slice (<= 64)
+  const int rows_per_inst = kWave / per_row;
+  const int r_sub_raw = lane / per_row;
+  const bool active = r_sub_raw < rows_per_inst;
+  const int r_sub = active ? r_sub_raw : 0;
+  const int e = lane - r_sub_raw * per_row;
+  const int hh = active ? e / head_vec : 0;
+  const int q = slice * head_vec + (active ? e - hh * head_vec : 0);
+  const int rows_per_round = kMergeWaves * rows_per_inst * kMergeUnroll;
+  const f32x4* po = (const f32x4*)plan.partial_o + (head0 + hh) * 32 + q;
+  auto row_of = [&](int base, int u) { return base + (u * kMergeWaves + wave) * rows_per_inst + r_sub; };
+  f32x4 o[kMergeUnroll];
+  auto load_round = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int i = min(row_of(base, u), count - 1);
+      o[u] = po[(size_t)(c0 + i) * Hq * 32];
+    }
+  };
+
+  // 1. lse of every row, 16 loads per thread per pass, with the first round of
+  //    row reads issued right behind them.  idx = i*G + h: i by a float divide,
+  //    exact since idx < 2^14 and the quotient is at least 0.5/G from an integer.
+  const int nval = count * G;
+  const float inv_g = 1.0f / (float)G;
+  for (int base = 0; base < nval; base += 16 * kThreads) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int idx = min(base + tid + u * kThreads, nval - 1);
+      const int i = (int)(((float)idx + 0.5f) * inv_g);
+      v[u] = plan.partial_lse[(size_t)(c0 + i) * Hq + head0 + (idx - i * G)];
+    }
+    if (base == 0) load_round(0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int idx = base + tid + u * kThreads;
+      if (idx < nval) s_w[idx] = v[u];
+    }
+  }
+  __syncthreads();
+  // 2. 16 lanes per head: max and sum over the rows, then the weights in place
+  for (int h2 = tid >> 4; h2 < G; h2 += kThreads / 16) {
+    const int sub = tid & 15;
     float mx = -__builtin_inff();
-    for (int c = c0 + lane; c < c1; c += kWave) mx = fmaxf(mx, lse[(size_t)c * Hq + h]);
+    for (int i = sub; i < count; i += 16) mx = fmaxf(mx, s_w[i * G + h2]);
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
-    float ws = 0.f;
-    for (int c = c0 + lane; c < c1; c += kWave) ws += fast_exp2(lse[(size_t)c * Hq + h] - mx);
+    for (int d = 8; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+    float sum = 0.f;
+    for (int i = sub; i < count; i += 16) sum += fast_exp2(s_w[i * G + h2] - mx);
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) ws += __shfl_xor(ws, d, kWave);
-    if (lane == 0) {
-      s_max[wave] = mx;
-      s_inv[wave] = 1.0f / ws;
-      if (lse_out) lse_out[(size_t)b * Hq + h] = (mx + __builtin_amdgcn_logf(ws)) * kLn2;
-    }
+    for (int d = 8; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, kWave);
+    const float inv = 1.0f / sum;
+    for (int i = sub; i < count; i += 16) s_w[i * G + h2] = fast_exp2(s_w[i * G + h2] - mx) * inv;
+    if (sub == 0 && slice == 0 && lse_out)
+      lse_out[(size_t)b * Hq + head0 + h2] = (mx + __builtin_amdgcn_logf(sum)) * kLn2;
   }
   __syncthreads();
 
-  const int nvec = G * 32;  // float4 per chunk row
-  f32x4 acc[kVec];
+  // 3. weighted sum of this channel slice over the rows
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < count; base += rows_per_round) {
+    if (base > 0) load_round(base);
 #pragma unroll
-  for (int k = 0; k < kVec; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const f32x4* po = (const f32x4*)plan.partial_o;
-  for (int cb = c0 + wave; cb < c1; cb += kMergeWaves * kUnroll) {
-    f32x4 o[kUnroll][kVec];
-    float wgt[kUnroll][kVec];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = cb + u * kMergeWaves;
-#pragma unroll
-      for (int k = 0; k < kVec; ++k) {
-        const int j = lane + kWave * k;
-        o[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        wgt[u][k] = 0.f;
-        if (c < c1 && j < nvec) {
-          const int hh = j >> 5;
-          o[u][k] = po[((size_t)c * Hq + (size_t)g * G) * 32 + j];
-          wgt[u][k] = fast_exp2(lse[(size_t)c * Hq + g * G + hh] - s_max[hh]) * s_inv[hh];
-        }
-      }
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int i = row_of(base, u);
+      const float wgt = (active && i < count) ? s_w[min(i, count - 1) * G + hh] : 0.f;
+      acc += wgt * o[u];
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int k = 0; k < kVec; ++k) acc[k] += wgt[u][k] * o[u][k];
   }
-#pragma unroll
-  for (int k = 0; k < kVec; ++k) {
-    const int j = lane + kWave * k;
-    if (j < nvec) s_acc[wave][j] = acc[k];
-  }
+  s_acc[tid] = acc;
   __syncthreads();
-  for (int j = threadIdx.x; j < nvec; j += kMergeWaves * kWave) {
-    f32x4 sum = s_acc[0][j];
-    for (int w = 1; w < kMergeWaves; ++w) sum += s_acc[w][j];
-    const int hh = j >> 5, d = (j & 31) * 4;
-    bf16x4 r;
+  for (int t = tid; t < per_row; t += kThreads) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kMergeWaves; ++w)
+      for (int r = 0; r < rows_per_inst; ++r) sum += s_acc[w * kWave + r * per_row + t];
+    const int h3 = t / head_vec;
+    const int d = (slice * head_vec + (t - h3 * head_vec)) * 4;
+    bf16x4 rr;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = (__bf16)sum[e];
-    *(bf16x4*)(out + ((size_t)b * Hq + (size_t)g * G + hh) * kHeadDim + d) = r;
+    for (int x = 0; x < 4; ++x) rr[x] = (__bf16)sum[x];
+    *(bf16x4*)(out + ((size_t)b * Hq + head0 + h3) * kHeadDim + d) = rr;
   }
 }
 
@@ -437,18 +474,13 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
 }
 
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
-                          hipStream_t stream) {
-  dim3 grid(geo.num_kv_heads, geo.batch);
-  const dim3 block(kMergeWaves * kWave);
-  uint16_t* o = (uint16_t*)out;
-  if (geo.group <= 2)
-    combine_kernel<1><<<grid, block, 0, stream>>>(geo, plan, o, lse_out);
-  else if (geo.group <= 4)
-    combine_kernel<2><<<grid, block, 0, stream>>>(geo, plan, o, lse_out);
-  else if (geo.group <= 8)
-    combine_kernel<4><<<grid, block, 0, stream>>>(geo, plan, o, lse_out);
-  else
-    combine_kernel<8><<<grid, block, 0, stream>>>(geo, plan, o, lse_out);
+                          int max_chunks_per_seq, hipStream_t stream) {
+  // S slices: a power of two dividing 32 with 32G/S <= 64 float4 per row slice
+  int slices = LBSR_MERGE_MIN_SLICES;
+  while (slices < 32 && 32 * geo.group / slices > kWave) slices *= 2;
+  dim3 grid(slices, geo.num_kv_heads, geo.batch);
+  const size_t lds = (size_t)max_chunks_per_seq * geo.group * sizeof(float);
+  merge_kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, (uint16_t*)out, lse_out);
   return hipGetLastError();
 }
 

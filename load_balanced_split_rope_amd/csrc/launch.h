@@ -25,6 +25,6 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
                                   hipStream_t stream);
 
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
-                          hipStream_t stream);
+                          int max_chunks_per_seq, hipStream_t stream);
 
 }  // namespace lbsr

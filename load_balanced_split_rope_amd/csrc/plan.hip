@@ -56,8 +56,9 @@ __device__ static int seq_of_tile(const int* cu, int batch, int t) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seq_lens,
                                                             int batch, int max_blocks,
-                                                            int dynamic, int num_workers,
-                                                            int splits, PlanPtrs plan) {
+                                                            int dynamic,
+                                                            int num_workers, int splits,
+                                                            PlanPtrs plan) {
   __shared__ int s_cu[kMaxBatch + 1];
   __shared__ int s_wave[kPlanThreads / kWave + 1];
   const int tid = threadIdx.x;
