@@ -107,6 +107,13 @@ class Case:
         ms = np.array([lb.decode_step_timed(*self.args(i, sched)) for i in range(reps)])
         return np.median(ms, axis=0), ms.mean(axis=0)
 
+    def trace(self, sched):
+        """Per-worker {start, end, HW_ID, XCC_ID} of one split-attention launch."""
+        lay = lb.workspace_layout(self.cfg, self.w.batch, sched)
+        tr = torch.zeros(lay.num_workers, 4, dtype=torch.int64, device=self.q_out.device)
+        lb.decode_step_timed(*self.args(0, sched), trace=tr)
+        return tr.cpu().numpy()
+
     def graph_ms(self, sched, steps):
         """Step time with the step captured once in a graph and replayed."""
         s = torch.cuda.Stream()
@@ -130,6 +137,28 @@ class Case:
             graphs[i % 2].replay()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
+
+
+WALL_CLOCK_MHZ = 100.0   # the constant clock the trace stamps (100 MHz on MI300-class GPUs)
+
+
+def load_balance(tr):
+    """Summarise a worker trace: per-worker busy time and per-CU busy time."""
+    start, end, hw, xcc = tr[:, 0], tr[:, 1], tr[:, 2], tr[:, 3]
+    dur = (end - start) / WALL_CLOCK_MHZ                     # us
+    cu = ((xcc & 0xF) << 16) | (((hw >> 13) & 0x7) << 8) | (((hw >> 12) & 1) << 4) | ((hw >> 8) & 0xF)
+    per_cu = {}
+    for c, d in zip(cu.tolist(), dur.tolist()):
+        per_cu[c] = per_cu.get(c, 0.0) + d
+    busy = np.array(list(per_cu.values()))
+    span = (end.max() - start.min()) / WALL_CLOCK_MHZ
+    return {"workers": int(len(dur)), "cus_used": int(len(per_cu)),
+            "max_workers_per_cu": int(np.max(np.bincount(np.unique(cu, return_inverse=True)[1]))),
+            "worker_us_max": round(float(dur.max()), 2), "worker_us_mean": round(float(dur.mean()), 2),
+            "worker_us_min": round(float(dur.min()), 2),
+            "cu_busy_us_max": round(float(busy.max()), 2), "cu_busy_us_mean": round(float(busy.mean()), 2),
+            "span_us": round(float(span), 2),
+            "busy_fraction": round(float(busy.sum() / (span * 256)), 4)}
 
 
 def source_hash():
@@ -202,7 +231,9 @@ def measure(w, dev, P, steps, warmup, full):
     r = {"ms": case.timed_steps(dyn, steps, warmup)}
     _, kmean = case.kernel_times(dyn, max(20, min(steps, 100)))
     r["kernel_ms"] = kmean
+    r["balance"] = {"dynamic": load_balance(case.trace(dyn))}
     if full:
+        r["balance"]["static_default"] = load_balance(case.trace(lb.Schedule("static", num_workers=P)))
         r["graph_ms"] = case.graph_ms(dyn, steps)
         static = {}
         for S in (0, 1, 2, 4, 8, 16, 32, 64):
@@ -261,6 +292,7 @@ def main():
                      "kernel": "split_attention_kernel<bf16>",
                      "algorithmic_bytes": split_kernel_bytes(w)},
         "cpu_baseline": None,
+        "load_balance": r["balance"],
     }
     if full:
         result["us_per_step_graph"] = round(r["graph_ms"] * 1e3, 2)
@@ -291,6 +323,7 @@ def main():
                 "static_us_per_step": {k: round(v * 1e3, 2) for k, v in st8.items()},
                 "dynamic_speedup_vs_static": {"default_S": round(st8["default"] / ms8, 3),
                                               "best_S": round(best8 / ms8, 3)},
+                "load_balance": r8["balance"],
             }
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(w, dev)

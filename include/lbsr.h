@@ -251,9 +251,14 @@ lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
 
 /*
  * Benchmark helper: lbsr_decode_step with a HIP event recorded on `stream`
- * around each of its four kernels (plan, prologue, split attention,
- * merge, in that order); waits for the stream and writes the four durations in
- * milliseconds to kernel_ms[4] (host).  Synchronises.  Not for production.
+ * around each of its four kernels (plan, prologue, split attention, merge, in
+ * that order); waits for the stream and writes the four durations in
+ * milliseconds to kernel_ms[4] (host).  If `trace` (device, nullable,
+ * int64[W][4], W = lbsr_ws_layout.num_workers) is given, the split-attention
+ * workgroup of worker w writes {start, end, HW_ID, XCC_ID}: start and end of
+ * the device's constant wall clock (hipDeviceAttributeWallClockRate) and the
+ * hardware ids of the compute unit it ran on.  Synchronises.  Not for
+ * production use.
  */
 lbsr_status lbsr_decode_step_timed(const lbsr_shape *shape, const lbsr_params *params,
                                    int32_t batch, const void *q, const void *k,
@@ -263,7 +268,7 @@ lbsr_status lbsr_decode_step_timed(const lbsr_shape *shape, const lbsr_params *p
                                    void *k_cache, void *v_cache, void *q_out,
                                    const lbsr_sched_cfg *cfg, void *workspace,
                                    size_t ws_bytes, void *out, float *lse_out,
-                                   void *stream, float *kernel_ms);
+                                   void *stream, float *kernel_ms, int64_t *trace);
 
 #ifdef __cplusplus
 }

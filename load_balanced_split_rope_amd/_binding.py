@@ -105,7 +105,7 @@ def _declare(lib):
                                             _P, _P]),
         "lbsr_decode_step_timed": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                                    + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t,
-                                                  _P, _P, _P, ctypes.POINTER(ctypes.c_float)]),
+                                                  _P, _P, _P, ctypes.POINTER(ctypes.c_float), _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

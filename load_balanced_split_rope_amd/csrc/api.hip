@@ -290,13 +290,13 @@ float score_scale_log2(const lbsr_params* p, int32_t kv_dtype) {
 lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
                       const void* q_out, const void* kc, const void* vc, const int32_t* bt,
                       const lbsr_ws_layout& l, void* ws, void* out, float* lse_out,
-                      hipStream_t stream) {
+                      int64_t* trace, hipStream_t stream) {
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
   return hip_status(lbsr::launch_split_attention(geo, fp8, l.num_workers, q_out, kc, vc, bt,
                                                  plan_ptrs(ws, l), out, lse_out,
                                                  score_scale_log2(params, shape->kv_dtype),
-                                                 fp8 ? params->v_scale : 1.0f, stream),
+                                                 fp8 ? params->v_scale : 1.0f, trace, stream),
                     "split attention launch");
 }
 
@@ -398,7 +398,7 @@ lbsr_status lbsr_attention(const lbsr_shape* shape, const lbsr_params* params, i
   LBSR_CHECK(current_device(&d));
   const hipStream_t s = (hipStream_t)stream;
   LBSR_CHECK(run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
-                       lse_out, s));
+                       lse_out, nullptr, s));
   return run_combine(shape, batch, l, workspace, out, lse_out, s);
 }
 
@@ -409,7 +409,7 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
                                     const int32_t* block_table, void* k_cache, void* v_cache,
                                     void* q_out, const lbsr_sched_cfg* cfg, void* workspace,
                                     size_t ws_bytes, void* out, float* lse_out, void* stream,
-                                    float* kernel_ms) {
+                                    float* kernel_ms, int64_t* trace) {
   g_last_error[0] = 0;
   LBSR_CHECK(validate_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
                                block_table, k_cache, v_cache, q_out, nullptr));
@@ -448,7 +448,7 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
   mark(2);
   if (st == LBSR_OK)
     st = run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
-                   lse_out, s);
+                   lse_out, trace, s);
   mark(3);
   if (st == LBSR_OK) st = run_combine(shape, batch, l, workspace, out, lse_out, s);
   mark(4);
@@ -469,7 +469,7 @@ lbsr_status lbsr_decode_step(const lbsr_shape* shape, const lbsr_params* params,
                              float* lse_out, void* stream) {
   return decode_step_impl(shape, params, batch, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
                           block_table, k_cache, v_cache, q_out, cfg, workspace, ws_bytes, out,
-                          lse_out, stream, nullptr);
+                          lse_out, stream, nullptr, nullptr);
 }
 
 lbsr_status lbsr_decode_step_timed(const lbsr_shape* shape, const lbsr_params* params,
@@ -479,11 +479,12 @@ lbsr_status lbsr_decode_step_timed(const lbsr_shape* shape, const lbsr_params* p
                                    const int32_t* block_table, void* k_cache, void* v_cache,
                                    void* q_out, const lbsr_sched_cfg* cfg, void* workspace,
                                    size_t ws_bytes, void* out, float* lse_out, void* stream,
-                                   float* kernel_ms) {
+                                   float* kernel_ms, int64_t* trace) {
   if (!kernel_ms) return fail(LBSR_E_INVALID, "kernel_ms is NULL");
+  if (trace && !aligned(trace, 8)) return fail(LBSR_E_INVALID, "trace is not 8-byte aligned");
   return decode_step_impl(shape, params, batch, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
                           block_table, k_cache, v_cache, q_out, cfg, workspace, ws_bytes, out,
-                          lse_out, stream, kernel_ms);
+                          lse_out, stream, kernel_ms, trace);
 }
 
 }  // extern "C"

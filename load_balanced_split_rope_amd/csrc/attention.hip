@@ -233,12 +233,14 @@ __device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
   }
 }
 
+// One worker of the schedule (this workgroup): all chunks of worker
+// blockIdx.x, every KV head (one wave per head, looping if Hkv > 8).
 template <bool kFp8>
-__global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
-    Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
-    const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table, PlanPtrs plan,
-    uint16_t* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
-    float out_scale) {
+__device__ __forceinline__ void split_worker(
+    const Geometry& geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const PlanPtrs& plan, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+    float score_scale_log2, float out_scale) {
   constexpr int kElemBytes = kFp8 ? 1 : 2;
   const int worker = blockIdx.x;
   const int c_begin = wave_uniform(plan.worker_chunk[worker]);
@@ -327,6 +329,31 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
           if (kc == 0) plan.partial_lse[(size_t)c * Hq + h] = lse2;
         }
       }
+    }
+  }
+}
+
+// The kernel: one workgroup per worker.  With a trace buffer it records, per
+// workgroup, [start, end] of the 100 MHz constant clock and the hardware ids
+// of the compute unit it ran on (HW_ID, XCC_ID), for load-balance analysis.
+template <bool kFp8>
+__global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
+    Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table, PlanPtrs plan,
+    uint16_t* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
+    float out_scale, int64_t* __restrict__ trace) {
+  int64_t t_start = 0;
+  if (trace != nullptr && threadIdx.x == 0) t_start = (int64_t)wall_clock64();
+  split_worker<kFp8>(geo, q_out, k_pool, v_pool, block_table, plan, out, lse_out,
+                     score_scale_log2, out_scale);
+  if (trace != nullptr) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t* tr = trace + 4 * (size_t)blockIdx.x;
+      tr[0] = t_start;
+      tr[1] = (int64_t)wall_clock64();
+      tr[2] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_REG_HW_ID
+      tr[3] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID
     }
   }
 }
@@ -459,16 +486,16 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
                                   const void* q_out, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const PlanPtrs& plan, void* out,
                                   float* lse_out, float score_scale_log2, float out_scale,
-                                  hipStream_t stream) {
+                                  int64_t* trace, hipStream_t stream) {
   const int waves = geo.num_kv_heads < kMaxAttnWaves ? geo.num_kv_heads : kMaxAttnWaves;
   if (fp8) {
     split_attention_kernel<true><<<num_workers, waves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
-        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale);
+        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale, trace);
   } else {
     split_attention_kernel<false><<<num_workers, waves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
-        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale);
+        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale, trace);
   }
   return hipGetLastError();
 }

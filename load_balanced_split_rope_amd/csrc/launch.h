@@ -22,7 +22,7 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
                                   const void* q_out, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const PlanPtrs& plan, void* out,
                                   float* lse_out, float score_scale_log2, float out_scale,
-                                  hipStream_t stream);
+                                  int64_t* trace, hipStream_t stream);
 
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
                           int max_chunks_per_seq, hipStream_t stream);

@@ -171,3 +171,24 @@ def test_bad_inputs_are_flagged_not_faulted():
     g = to_device(inp, dev)
     res = run_step(w, g, lb.Schedule("dynamic", num_workers=2))
     assert res["error"] & lb._binding.DEV_ERR_PAGE
+
+
+def test_worker_trace_records_every_worker():
+    dev = device()
+    w = wl.custom([3000, 130, 64, 9000], num_q_heads=64, num_kv_heads=8, seed=17)
+    g = to_device(wl.make_inputs(w), dev)
+    from gpu_util import config_for
+    cfg = config_for(w, g)
+    sched = lb.Schedule("dynamic", num_workers=37)
+    ws = lb.alloc_workspace(cfg, w.batch, sched, device=dev)
+    q_out, out = torch.empty_like(g["q"]), torch.empty_like(g["q"])
+    tr = torch.zeros(37, 4, dtype=torch.int64, device=dev)
+    ms = lb.decode_step_timed(cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"],
+                              g["q_norm_w"], g["k_norm_w"], g["block_table"], g["k_cache"],
+                              g["v_cache"], q_out, sched, ws, out, None, trace=tr)
+    t = tr.cpu().numpy()
+    assert len(ms) == 4 and all(x > 0 for x in ms)
+    assert np.all(t[:, 0] > 0) and np.all(t[:, 1] >= t[:, 0])
+    # the split kernel's span, in the 100 MHz clock, fits inside its event time
+    span_us = (t[:, 1].max() - t[:, 0].min()) / 100.0
+    assert span_us <= ms[2] * 1e3 * 1.5 + 5
