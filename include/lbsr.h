@@ -13,9 +13,8 @@
  *   3. lbsr_attention           split attention over the scheduled tiles with
  *                               an online softmax, then a log-sum-exp merge of
  *                               the pieces of sequences that were split;
- *   4. lbsr_decode_step         2 -> 1 -> 3 on one stream (the plan does not
- *                               depend on the prologue and clears the error
- *                               word, so it runs first).
+ *   4. lbsr_decode_step         1 + 2 as one launch (they are independent),
+ *                               then 3, on one stream.
  *
  * Sources (titles translated from Korean):
  *   [A] 24-ai.news, "vLLM and Tencent Hunyuan upstream two HPC backends for
@@ -135,6 +134,7 @@ typedef struct {
   size_t chunks;       /* int32[C_max][4]: (sequence, first tile, end tile, worker) */
   size_t seq_chunk;    /* int32[batch + 1]: sequence b owns chunks [sc[b], sc[b+1]) */
   size_t seq_len_eff;  /* int32[batch]: lengths after clamping */
+  size_t token_status; /* int32[batch]: prologue error bits per token (decode step) */
   size_t partial_o;    /* float[C_max][Hq][128]: normalised partial outputs */
   size_t partial_lse;  /* float[C_max][Hq]: partial log2-sum-exp (internal) */
   size_t total;        /* bytes the workspace needs */
@@ -235,11 +235,12 @@ lbsr_status lbsr_attention(const lbsr_shape *shape, const lbsr_params *params, i
                            void *stream);
 
 /*
- * One whole decode step: lbsr_plan, lbsr_rope_norm_kv_write, lbsr_attention
- * on `stream`, in that order (arguments as there; the prologue's error bits
- * go to the workspace's error word, which the plan cleared).  Requires
- * positions[b] = seq_lens[b] - 1 for the new token to be part of its own
- * attention.
+ * One whole decode step on `stream` (arguments as for the three calls above):
+ * the schedule and the prologue in one launch, then split attention and the
+ * merge.  Same results as lbsr_plan, lbsr_rope_norm_kv_write and
+ * lbsr_attention in turn; the prologue's error bits end up in the
+ * workspace's error word.  Requires positions[b] = seq_lens[b] - 1 for the
+ * new token to be part of its own attention.
  */
 lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
                              int32_t batch, const void *q, const void *k, const void *v,
@@ -251,9 +252,9 @@ lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
 
 /*
  * Benchmark helper: lbsr_decode_step with a HIP event recorded on `stream`
- * around each of its four kernels (plan, prologue, split attention, merge, in
- * that order); waits for the stream and writes the four durations in
- * milliseconds to kernel_ms[4] (host).  If `trace` (device, nullable,
+ * around each of its three launches (schedule + prologue, split attention,
+ * merge, in that order); waits for the stream and writes the three durations
+ * in milliseconds to kernel_ms[3] (host).  If `trace` (device, nullable,
  * int64[W][4], W = lbsr_ws_layout.num_workers) is given, the split-attention
  * workgroup of worker w writes {start, end, HW_ID, XCC_ID}: start and end of
  * the device's constant wall clock (hipDeviceAttributeWallClockRate) and the

@@ -70,7 +70,7 @@ class WsLayout(ctypes.Structure):
     _fields_ = [("error_word", ctypes.c_size_t), ("cu_tiles", ctypes.c_size_t),
                 ("worker_chunk", ctypes.c_size_t), ("chunks", ctypes.c_size_t),
                 ("seq_chunk", ctypes.c_size_t), ("seq_len_eff", ctypes.c_size_t),
-                ("partial_o", ctypes.c_size_t), ("partial_lse", ctypes.c_size_t),
+                ("token_status", ctypes.c_size_t), ("partial_o", ctypes.c_size_t), ("partial_lse", ctypes.c_size_t),
                 ("total", ctypes.c_size_t), ("num_workers", ctypes.c_int32),
                 ("max_chunks", ctypes.c_int32), ("static_splits", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]

@@ -174,6 +174,7 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
   out->chunks = off;       off = align256(off + 16 * (size_t)cmax);
   out->seq_chunk = off;    off = align256(off + 4 * (size_t)(batch + 1));
   out->seq_len_eff = off;  off = align256(off + 4 * (size_t)batch);
+  out->token_status = off; off = align256(off + 4 * (size_t)batch);
   out->partial_o = off;    off = align256(off + 4 * (size_t)cmax * Hq * LBSR_HEAD_DIM);
   out->partial_lse = off;  off = align256(off + 4 * (size_t)cmax * Hq);
   out->total = off;
@@ -192,6 +193,7 @@ lbsr::PlanPtrs plan_ptrs(void* ws, const lbsr_ws_layout& l) {
   p.chunks = (int32_t*)(base + l.chunks);
   p.seq_chunk = (int32_t*)(base + l.seq_chunk);
   p.seq_len_eff = (int32_t*)(base + l.seq_len_eff);
+  p.token_status = (int32_t*)(base + l.token_status);
   p.partial_o = (float*)(base + l.partial_o);
   p.partial_lse = (float*)(base + l.partial_lse);
   return p;
@@ -281,6 +283,23 @@ lbsr_status run_plan(const lbsr_shape* shape, int32_t batch, const int32_t* seq_
                     "plan launch");
 }
 
+lbsr_status run_plan_prologue(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                              const int32_t* seq_lens, const lbsr_sched_cfg* cfg,
+                              const lbsr_ws_layout& l, void* ws, const void* q, const void* k,
+                              const void* v, const int32_t* positions, const void* wq,
+                              const void* wk, const int32_t* bt, void* kc, void* vc, void* q_out,
+                              hipStream_t stream) {
+  const lbsr::Geometry geo = geometry(shape, batch);
+  const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
+  return hip_status(
+      lbsr::launch_plan_prologue(seq_lens, cfg->sched == LBSR_SCHED_DYNAMIC, l.num_workers,
+                                 l.static_splits, plan_ptrs(ws, l), geo, fp8, q, k, v, positions,
+                                 wq, wk, bt, kc, vc, q_out, params->rope_theta,
+                                 (double)params->rms_eps, params->norm_before_rope,
+                                 fp8 ? params->k_scale : 1.0, fp8 ? params->v_scale : 1.0, stream),
+      "plan + prologue launch");
+}
+
 float score_scale_log2(const lbsr_params* p, int32_t kv_dtype) {
   const double sm = p->sm_scale > 0 ? (double)p->sm_scale : 1.0 / sqrt((double)LBSR_HEAD_DIM);
   const double ks = kv_dtype == LBSR_KV_FP8_E4M3 ? (double)p->k_scale : 1.0;
@@ -301,13 +320,14 @@ lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_
 }
 
 lbsr_status run_combine(const lbsr_shape* shape, int32_t batch, const lbsr_ws_layout& l, void* ws,
-                        void* out, float* lse_out, hipStream_t stream) {
+                        void* out, float* lse_out, bool fold_token_status, hipStream_t stream) {
   const lbsr::Geometry geo = geometry(shape, batch);
   // a sequence has at most one chunk per worker (dynamic) or split (static),
   // and at most one per tile: the merge stages that many rows' lse in LDS
   const int per_seq = l.static_splits ? l.static_splits : l.num_workers;
   const int bound = per_seq < shape->max_blocks_per_seq ? per_seq : shape->max_blocks_per_seq;
-  return hip_status(lbsr::launch_combine(geo, plan_ptrs(ws, l), out, lse_out, bound, stream),
+  return hip_status(lbsr::launch_combine(geo, plan_ptrs(ws, l), out, lse_out, bound,
+                                         fold_token_status, stream),
                     "merge launch");
 }
 
@@ -399,7 +419,7 @@ lbsr_status lbsr_attention(const lbsr_shape* shape, const lbsr_params* params, i
   const hipStream_t s = (hipStream_t)stream;
   LBSR_CHECK(run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
                        lse_out, nullptr, s));
-  return run_combine(shape, batch, l, workspace, out, lse_out, s);
+  return run_combine(shape, batch, l, workspace, out, lse_out, false, s);
 }
 
 static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
@@ -422,11 +442,10 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
   DeviceInfo d;
   LBSR_CHECK(current_device(&d));
   const hipStream_t s = (hipStream_t)stream;
-  int32_t* err = plan_ptrs(workspace, l).error_word;
 
-  hipEvent_t ev[5] = {};
+  hipEvent_t ev[4] = {};
   if (kernel_ms) {
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const hipError_t e = hipEventCreate(&ev[i]);
       if (e != hipSuccess) {
         for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
@@ -438,25 +457,23 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
   auto mark = [&](int i) {
     if (kernel_ms && st == LBSR_OK) st = hip_status(hipEventRecord(ev[i], s), "hipEventRecord");
   };
-  // The plan clears the error word, so it runs first; it does not depend on the prologue.
+  // One launch computes the schedule and the prologue; they are independent.
   mark(0);
-  if (st == LBSR_OK) st = run_plan(shape, batch, seq_lens, cfg, l, workspace, s);
-  mark(1);
   if (st == LBSR_OK)
-    st = run_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w, block_table,
-                      k_cache, v_cache, q_out, err, s);
-  mark(2);
+    st = run_plan_prologue(shape, params, batch, seq_lens, cfg, l, workspace, q, k, v, positions,
+                           q_norm_w, k_norm_w, block_table, k_cache, v_cache, q_out, s);
+  mark(1);
   if (st == LBSR_OK)
     st = run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
                    lse_out, trace, s);
+  mark(2);
+  if (st == LBSR_OK) st = run_combine(shape, batch, l, workspace, out, lse_out, true, s);
   mark(3);
-  if (st == LBSR_OK) st = run_combine(shape, batch, l, workspace, out, lse_out, s);
-  mark(4);
   if (kernel_ms) {
-    if (st == LBSR_OK) st = hip_status(hipEventSynchronize(ev[4]), "hipEventSynchronize");
-    for (int i = 0; i < 4 && st == LBSR_OK; ++i)
+    if (st == LBSR_OK) st = hip_status(hipEventSynchronize(ev[3]), "hipEventSynchronize");
+    for (int i = 0; i < 3 && st == LBSR_OK; ++i)
       st = hip_status(hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]), "hipEventElapsedTime");
-    for (int i = 0; i < 5; ++i) (void)hipEventDestroy(ev[i]);
+    for (int i = 0; i < 4; ++i) (void)hipEventDestroy(ev[i]);
   }
   return st;
 }

@@ -233,16 +233,28 @@ __device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
   }
 }
 
-// One worker of the schedule (this workgroup): all chunks of worker
-// blockIdx.x, every KV head (one wave per head, looping if Hkv > 8).
+// Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD
+// b % 8).  Give each XCD a contiguous run of workers instead: neighbouring
+// workers' tile counts differ by at most one in a periodic pattern, and a
+// contiguous run averages that pattern out, so every XCD gets the same work
+// to within one tile per workgroup.
+__device__ __forceinline__ int xcd_worker(int block, int num_blocks) {
+  constexpr int kXcds = 8;
+  const int x = block % kXcds, j = block / kXcds;
+  int start = 0;
+  for (int i = 0; i < x; ++i) start += (num_blocks - i + kXcds - 1) / kXcds;
+  return start + j;
+}
+
+// One worker of the schedule (this workgroup): all chunks of `worker`, every
+// KV head (one wave per head, looping if Hkv > 8).
 template <bool kFp8>
 __device__ __forceinline__ void split_worker(
-    const Geometry& geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
+    int worker, const Geometry& geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const PlanPtrs& plan, uint16_t* __restrict__ out, float* __restrict__ lse_out,
     float score_scale_log2, float out_scale) {
   constexpr int kElemBytes = kFp8 ? 1 : 2;
-  const int worker = blockIdx.x;
   const int c_begin = wave_uniform(plan.worker_chunk[worker]);
   const int c_end = wave_uniform(plan.worker_chunk[worker + 1]);
   if (c_begin >= c_end) return;
@@ -323,9 +335,14 @@ __device__ __forceinline__ void split_worker(
           }
           if (kc == 0 && lse_out) lse_out[(size_t)b * Hq + h] = lse2 * kLn2;
         } else {
-          float* po = plan.partial_o + ((size_t)c * Hq + h) * kHeadDim + 4 * kc;
+          // partial row layout of (chunk c, KV group g): [16 slices of 8
+          // channels][G heads][8 channels], so that any run of slices is
+          // contiguous for the merge
+          float* po = plan.partial_o + ((size_t)c * Hq + (size_t)g * G) * kHeadDim +
+                      col * 8 + 4 * (kc & 1);
 #pragma unroll
-          for (int db = 0; db < 8; ++db) *(f32x4*)(po + 16 * db) = O[db] * scale;
+          for (int db = 0; db < 8; ++db)
+            *(f32x4*)(po + (2 * db + (kc >> 1)) * 8 * G) = O[db] * scale;
           if (kc == 0) plan.partial_lse[(size_t)c * Hq + h] = lse2;
         }
       }
@@ -334,8 +351,8 @@ __device__ __forceinline__ void split_worker(
 }
 
 // The kernel: one workgroup per worker.  With a trace buffer it records, per
-// workgroup, [start, end] of the 100 MHz constant clock and the hardware ids
-// of the compute unit it ran on (HW_ID, XCC_ID), for load-balance analysis.
+// worker, [start, end] of the 100 MHz constant clock and the hardware ids of
+// the compute unit it ran on (HW_ID, XCC_ID), for load-balance analysis.
 template <bool kFp8>
 __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
     Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
@@ -344,12 +361,13 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
     float out_scale, int64_t* __restrict__ trace) {
   int64_t t_start = 0;
   if (trace != nullptr && threadIdx.x == 0) t_start = (int64_t)wall_clock64();
-  split_worker<kFp8>(geo, q_out, k_pool, v_pool, block_table, plan, out, lse_out,
+  const int worker = xcd_worker(blockIdx.x, gridDim.x);
+  split_worker<kFp8>(worker, geo, q_out, k_pool, v_pool, block_table, plan, out, lse_out,
                      score_scale_log2, out_scale);
   if (trace != nullptr) {
     __syncthreads();
     if (threadIdx.x == 0) {
-      int64_t* tr = trace + 4 * (size_t)blockIdx.x;
+      int64_t* tr = trace + 4 * (size_t)worker;
       tr[0] = t_start;
       tr[1] = (int64_t)wall_clock64();
       tr[2] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_REG_HW_ID
@@ -360,9 +378,11 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
 
 // Merge of the chunks of every sequence that has more than one.
 //
-// A sequence's n chunk rows (partial_o[c][g*G .. g*G+G) plus their log2-sum-
-// exp) are read in parallel: workgroup (s, g, b) owns channel slice s (128/S
-// channels of every head of KV group g, S slices) of sequence b.  A slice is
+// A sequence's n chunk rows (the G heads of KV group g in partial_o[c], laid
+// out as 16 slices of 8 channels x G heads, plus their log2-sum-exp) are read
+// in parallel: workgroup (s, g, b) owns slice run s of sequence b -- 16/S of
+// the 16 slices, one contiguous 128G*4/S-byte piece of every row -- where S
+// grows with n so that every row's piece is read in one round.  A piece is
 // 32G/S float4 (at most 64), so one wave instruction covers 64/(32G/S) rows,
 // and each lane keeps kMergeUnroll rows in flight.  The first round of row
 // reads is issued before the lse are staged in LDS and turned into weights
@@ -377,18 +397,34 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
 #ifndef LBSR_MERGE_MIN_SLICES
 #define LBSR_MERGE_MIN_SLICES 4
 #endif
+#ifndef LBSR_MERGE_MAX_SLICES
+#define LBSR_MERGE_MAX_SLICES 4
+#endif
 constexpr int kMergeWaves = LBSR_MERGE_WAVES;
 constexpr int kMergeUnroll = LBSR_MERGE_UNROLL;
 
 __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(Geometry geo, PlanPtrs plan,
                                                                     uint16_t* __restrict__ out,
-                                                                    float* __restrict__ lse_out) {
+                                                                    float* __restrict__ lse_out,
+                                                                    int min_slices,
+                                                                    int fold_token_status) {
   constexpr int kThreads = kMergeWaves * kWave;
-  const int slice = blockIdx.x, nslices = gridDim.x, g = blockIdx.y, b = blockIdx.z;
+  const int slice = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (fold_token_status && slice == 0 && g == 0 && threadIdx.x == 0) {
+    const int32_t st = plan.token_status[b];
+    if (st) atomicOr(plan.error_word, st);
+  }
   const int c0 = plan.seq_chunk[b], c1 = plan.seq_chunk[b + 1];
   const int count = c1 - c0;
   if (count <= 1) return;  // written directly by the split kernel
   const int Hq = geo.num_q_heads, G = geo.group;
+  // Slices for this sequence: the fewest (from min_slices) whose rows all fit
+  // in one round of reads, at most gridDim.x; surplus workgroups leave.
+  int nslices = min_slices;
+  while (nslices < (int)gridDim.x &&
+         count > kMergeWaves * (kWave / (G * 32 / nslices)) * kMergeUnroll)
+    nslices *= 2;
+  if (slice >= nslices) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const size_t head0 = (size_t)g * G;
   extern __shared__ float s_w[];                           // [count][G]: lse, then weights
@@ -396,24 +432,22 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(Geometry geo
 
   // Loads below are unconditional (indices clamped into range, results of the
   // clamped ones discarded) so that a thread's loads issue back to back.
-  const int head_vec = 32 / nslices;      // float4 of one head in a slice
-  const int per_row = G * head_vec;       // float4 of one row's slice (<= 64)
+  const int per_row = G * 32 / nslices;   // float4 of one row's piece (<= 64)
   const int rows_per_inst = kWave / per_row;
   const int r_sub_raw = lane / per_row;
   const bool active = r_sub_raw < rows_per_inst;
   const int r_sub = active ? r_sub_raw : 0;
-  const int e = lane - r_sub_raw * per_row;
-  const int hh = active ? e / head_vec : 0;
-  const int q = slice * head_vec + (active ? e - hh * head_vec : 0);
+  const int e = active ? lane - r_sub_raw * per_row : 0;   // float4 inside the piece
+  const int hh = (e % (2 * G)) >> 1;                       // head of that float4
+  const f32x4* po = (const f32x4*)plan.partial_o + head0 * 32 + slice * per_row + e;
   const int rows_per_round = kMergeWaves * rows_per_inst * kMergeUnroll;
-  const f32x4* po = (const f32x4*)plan.partial_o + (head0 + hh) * 32 + q;
   auto row_of = [&](int base, int u) { return base + (u * kMergeWaves + wave) * rows_per_inst + r_sub; };
   f32x4 o[kMergeUnroll];
   auto load_round = [&](int base) {
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const int i = min(row_of(base, u), count - 1);
-      o[u] = po[(size_t)(c0 + i) * Hq * 32];
+      o[u] = po[(size_t)(c0 + i) * Hq * 32];   // row c0 + i of this piece
     }
   };
 
@@ -473,8 +507,10 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(Geometry geo
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < kMergeWaves; ++w)
       for (int r = 0; r < rows_per_inst; ++r) sum += s_acc[w * kWave + r * per_row + t];
-    const int h3 = t / head_vec;
-    const int d = (slice * head_vec + (t - h3 * head_vec)) * 4;
+    // float4 t of the piece: 8-channel slice slice*(16/S) + t/(2G), head (t%2G)/2
+    const int bs = slice * (16 / nslices) + t / (2 * G);
+    const int h3 = (t % (2 * G)) >> 1;
+    const int d = bs * 8 + (t & 1) * 4;
     bf16x4 rr;
 #pragma unroll
     for (int x = 0; x < 4; ++x) rr[x] = (__bf16)sum[x];
@@ -501,13 +537,15 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
 }
 
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
-                          int max_chunks_per_seq, hipStream_t stream) {
+                          int max_chunks_per_seq, bool fold_token_status, hipStream_t stream) {
   // S slices: a power of two dividing 32 with 32G/S <= 64 float4 per row slice
   int slices = LBSR_MERGE_MIN_SLICES;
   while (slices < 32 && 32 * geo.group / slices > kWave) slices *= 2;
-  dim3 grid(slices, geo.num_kv_heads, geo.batch);
+  const int max_slices = slices > LBSR_MERGE_MAX_SLICES ? slices : LBSR_MERGE_MAX_SLICES;
+  dim3 grid(max_slices, geo.num_kv_heads, geo.batch);
   const size_t lds = (size_t)max_chunks_per_seq * geo.group * sizeof(float);
-  merge_kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, (uint16_t*)out, lse_out);
+  merge_kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, (uint16_t*)out, lse_out,
+                                                           slices, fold_token_status ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ struct PlanPtrs {
   int32_t* chunks;        // [C_max][4] = seq, first tile, end tile, worker
   int32_t* seq_chunk;     // [B+1]
   int32_t* seq_len_eff;   // [B]
+  int32_t* token_status;  // [B] the fused prologue's per-token error bits
   float* partial_o;       // [C_max][Hq][128]
   float* partial_lse;     // [C_max][Hq], log2 domain
 };

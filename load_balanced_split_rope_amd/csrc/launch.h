@@ -24,7 +24,17 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
                                   float* lse_out, float score_scale_log2, float out_scale,
                                   int64_t* trace, hipStream_t stream);
 
+// fold_token_status: also OR plan.token_status (written by the fused
+// plan + prologue launch of the same step) into the error word.
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
-                          int max_chunks_per_seq, hipStream_t stream);
+                          int max_chunks_per_seq, bool fold_token_status, hipStream_t stream);
+
+hipError_t launch_plan_prologue(const int32_t* seq_lens, bool dynamic, int num_workers,
+                                int static_splits, const PlanPtrs& plan, const Geometry& geo,
+                                bool fp8, const void* q, const void* k, const void* v,
+                                const int32_t* positions, const void* wq, const void* wk,
+                                const int32_t* block_table, void* k_cache, void* v_cache,
+                                void* q_out, double theta, double eps, int norm_first,
+                                double k_scale, double v_scale, hipStream_t stream);
 
 }  // namespace lbsr

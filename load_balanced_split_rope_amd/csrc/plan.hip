@@ -1,156 +1,24 @@
-// Per-step tile schedule, computed on the device in one workgroup.
-//
-// [A] "Why does dynamic scheduling matter in attention?": tiles of 64 tokens
-// are dealt to the compute units in proportion to each sequence's current
-// length, every step, instead of a static split-KV that assumes equal
-// lengths.  Reading of "proportional": all tiles of the batch are laid end to
-// end (T in total) and worker w of P takes flat tiles
-// [floor(w*T/P), floor((w+1)*T/P)), so loads differ by at most one tile; a
-// worker's range is cut at sequence ends into chunks.  The static baseline
-// cuts every sequence into the same S parts of its own length.
-//
-// One 1024-thread workgroup: per-sequence prefix sums live in LDS (batch <=
-// 16384), counts per worker are scanned in 1024-wide rounds with a carry.
-// Everything is integer arithmetic; products w*T are 64-bit.
+// The tile schedule as its own kernel (lbsr_plan); the code is in plan.h.
 
-#include "common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace lbsr {
 
-// Inclusive block scan of one int per thread (1024 threads = 16 waves).
-__device__ static int block_inclusive_scan(int x, int* s_wave, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < kPlanThreads / kWave; ++i) {
-      const int t = s_wave[i];
-      s_wave[i] = acc;  // exclusive offsets of each wave
-      acc += t;
-    }
-    s_wave[kPlanThreads / kWave] = acc;
-  }
-  __syncthreads();
-  x += s_wave[wave];
-  total = s_wave[kPlanThreads / kWave];
-  __syncthreads();  // s_wave is reused by the next call
-  return x;
-}
-
-// Index of the sequence that holds flat tile t: the largest b with cu[b] <= t.
-__device__ static int seq_of_tile(const int* cu, int batch, int t) {
-  int lo = 0, hi = batch;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seq_lens,
                                                             int batch, int max_blocks,
-                                                            int dynamic,
-                                                            int num_workers, int splits,
-                                                            PlanPtrs plan) {
-  __shared__ int s_cu[kMaxBatch + 1];
-  __shared__ int s_wave[kPlanThreads / kWave + 1];
-  const int tid = threadIdx.x;
-  if (tid == 0) plan.error_word[0] = 0;
-
-  // 1. clamped lengths, tiles per sequence, prefix sums
-  const int max_len = max_blocks * kPage;
-  int bad = 0;
-  int carry = 0;
-  if (tid == 0) s_cu[0] = 0;
-  for (int base = 0; base < batch; base += kPlanThreads) {
-    const int b = base + tid;
-    int n = 0;
-    if (b < batch) {
-      const int L = seq_lens[b];
-      const int Lc = L < 1 ? 1 : (L > max_len ? max_len : L);
-      bad |= (Lc != L);
-      plan.seq_len_eff[b] = Lc;
-      n = (Lc + kPage - 1) / kPage;
-    }
-    int total;
-    const int incl = block_inclusive_scan(n, s_wave, total);
-    if (b < batch) s_cu[b + 1] = carry + incl;
-    carry += total;
-  }
-  if (bad) atomicOr(plan.error_word, (int32_t)kErrSeqLen);
-  __syncthreads();
-  for (int b = tid; b <= batch; b += kPlanThreads) plan.cu_tiles[b] = s_cu[b];
-  const int T = s_cu[batch];
-
-  // 2. chunk counts per worker, their prefix sums, and the chunks themselves
-  const int W = dynamic ? num_workers : batch * splits;
-  carry = 0;
-  for (int base = 0; base < W; base += kPlanThreads) {
-    const int w = base + tid;
-    int cnt = 0, first = 0;
-    int s = 0, e = 0;
-    if (w < W) {
-      if (dynamic) {
-        s = (int)(((int64_t)w * T) / W);
-        e = (int)(((int64_t)(w + 1) * T) / W);
-        if (s < e) {
-          first = seq_of_tile(s_cu, batch, s);
-          cnt = seq_of_tile(s_cu, batch, e - 1) - first + 1;
-        }
-      } else {
-        const int b = w / splits, sp = w - b * splits;
-        const int n = s_cu[b + 1] - s_cu[b];
-        s = (int)(((int64_t)sp * n) / splits);
-        e = (int)(((int64_t)(sp + 1) * n) / splits);
-        first = b;
-        cnt = e > s ? 1 : 0;
-      }
-    }
-    int total;
-    const int c0 = carry + block_inclusive_scan(cnt, s_wave, total) - cnt;
-    if (w < W) {
-      plan.worker_chunk[w] = c0;
-      for (int i = 0; i < cnt; ++i) {
-        const int c = c0 + i;
-        const int b = first + i;
-        int t0, t1;
-        if (dynamic) {
-          const int a = s > s_cu[b] ? s : s_cu[b];
-          const int z = e < s_cu[b + 1] ? e : s_cu[b + 1];
-          t0 = a - s_cu[b];
-          t1 = z - s_cu[b];
-        } else {
-          t0 = s;
-          t1 = e;
-        }
-        int32_t* ch = plan.chunks + 4 * (size_t)c;
-        ch[0] = b;
-        ch[1] = t0;
-        ch[2] = t1;
-        ch[3] = w;
-        if (t0 == 0) plan.seq_chunk[b] = c;  // a sequence's first chunk starts at its tile 0
-      }
-    }
-    carry += total;
-  }
-  if (tid == 0) {
-    plan.worker_chunk[W] = carry;
-    plan.seq_chunk[batch] = carry;
-  }
+                                                            int dynamic, int num_workers,
+                                                            int splits, PlanPtrs plan) {
+  extern __shared__ int s_cu[];
+  plan_body(seq_lens, batch, max_blocks, dynamic, num_workers, splits, plan, s_cu);
 }
 
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, bool dynamic,
                        int num_workers, int static_splits, const PlanPtrs& plan,
                        hipStream_t stream) {
-  plan_kernel<<<1, kPlanThreads, 0, stream>>>(seq_lens, batch, max_blocks, dynamic ? 1 : 0,
-                                               num_workers, static_splits, plan);
+  const size_t lds = sizeof(int) * (size_t)(batch + 1);
+  plan_kernel<<<1, kPlanThreads, lds, stream>>>(seq_lens, batch, max_blocks, dynamic ? 1 : 0,
+                                                 num_workers, static_splits, plan);
   return hipGetLastError();
 }
 

@@ -204,14 +204,14 @@ def decode_step_timed(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w,
                       lse_out=None, stream=None, trace=None):
     """lbsr_decode_step_timed: the step with HIP events around each kernel (synchronises).
 
-    Returns milliseconds of (plan, prologue, split attention, merge).  ``trace``
+    Returns milliseconds of (schedule + prologue, split attention, merge).  ``trace``
     (int64 [W, 4] on the GPU) receives per-worker {start, end, HW_ID, XCC_ID}."""
     args, keep = _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table,
                             k_cache, v_cache, q_out, sched, workspace, out, lse_out)
     if trace is not None:
         W = workspace_layout(cfg, q.shape[0], sched).num_workers
         _need(trace, "trace", torch.int64, shape=(W, 4))
-    ms = (ctypes.c_float * 4)()
+    ms = (ctypes.c_float * 3)()
     B._check(B.lib().lbsr_decode_step_timed(*args, B._stream(stream), ms, B._ptr(trace)))
     del keep
     return list(ms)

@@ -50,7 +50,7 @@ def test_workspace_layout_dynamic_and_static():
     lay = workspace_layout(cfg_mix(), 32, Schedule("dynamic", num_workers=256))
     assert lay.num_workers == 256 and lay.max_chunks == 256 + 31
     offs = [lay.error_word, lay.cu_tiles, lay.worker_chunk, lay.chunks, lay.seq_chunk,
-            lay.seq_len_eff, lay.partial_o, lay.partial_lse, lay.total]
+            lay.seq_len_eff, lay.token_status, lay.partial_o, lay.partial_lse, lay.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.partial_lse - lay.partial_o >= 4 * 287 * 64 * 128
     st = workspace_layout(cfg_mix(), 32, Schedule("static", num_workers=256))
