@@ -139,6 +139,12 @@ class Case:
         return (time.perf_counter() - t0) * 1e3 / steps
 
 
+WORKLOAD_TEXT = {
+    "mix": "mix: 1 x 131072 + 31 x 4096 tokens",
+    "mix_fp8": "mix_fp8: 1 x 131072 + 31 x 4096 tokens, FP8 E4M3 cache",
+    "uniform": "uniform: 32 x 4096 tokens",
+    "loguniform": "loguniform: 64 sequences, lengths log-uniform in [512, 262144], FP8 cache",
+}
 WALL_CLOCK_MHZ = 100.0   # the constant clock the trace stamps (100 MHz on MI300-class GPUs)
 
 
@@ -250,7 +256,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mix", choices=["mix", "uniform"])
+    ap.add_argument("--workload", default="mix",
+                    choices=["mix", "mix_fp8", "uniform", "loguniform"],
+                    help="headline workload (the metric is quoted on mix)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (a known-size kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true",
                     help="headline workload only: no graph, static sweep, FP8 or CPU legs")
@@ -261,6 +272,14 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": 5}))
+        return
     P = lb.device_workers(0)
     full = not args.quick
 
@@ -275,10 +294,10 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 cache, bf16 q/out",
         "data": "synthetic",
-        "config": {"workload": (f"{w.name}: 1 x 131072 + 31 x 4096 tokens" if w.name == "mix"
-                                else f"{w.name}: 32 x 4096 tokens"),
+        "config": {"workload": WORKLOAD_TEXT[w.name],
                    "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": 128, "page": 64, "kv_cache": w.kv_dtype,
                    "schedule": f"dynamic, {P} workers", "parallelism": "1 GPU"},
@@ -289,7 +308,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, w.kv_dtype),
-                     "kernel": "split_attention_kernel<bf16>",
+                     "kernel": f"split_attention_kernel<{w.kv_dtype}>",
                      "algorithmic_bytes": split_kernel_bytes(w)},
         "cpu_baseline": None,
         "load_balance": r["balance"],
