@@ -61,16 +61,17 @@ def split_kernel_bytes(w):
 class Case:
     """Two independent input sets of one workload on the GPU, plus outputs."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, kv_interleave=False):
         self.w = w
         self.sets = []
         for copy in range(2):
-            g = wl.make_inputs(w, device=dev)
+            g = wl.make_inputs(w, device=dev, kv_interleave=kv_interleave)
             self.sets.append(g)
         g = self.sets[0]
         self.cfg = lb.DecodeConfig(w.num_q_heads, w.num_kv_heads, w.kv_dtype, g["max_blocks"],
-                                   g["num_pages"], rope_theta=w.rope_theta, rms_eps=w.rms_eps,
-                                   k_scale=w.k_scale, v_scale=w.v_scale)
+                                   g["num_pages"], page_stride=g["page_stride"],
+                                   head_stride=g["head_stride"], rope_theta=w.rope_theta,
+                                   rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale)
         self.q_out = torch.empty_like(g["q"])
         self.out = torch.empty_like(g["q"])
         self.lse = torch.empty(w.batch, w.num_q_heads, dtype=torch.float32, device=dev)

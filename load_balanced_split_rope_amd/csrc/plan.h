@@ -20,8 +20,10 @@
 
 namespace lbsr {
 
-// Inclusive block scan of one int per thread (1024 threads = 16 waves).
+// Inclusive block scan of one int per thread (1024 threads = 16 waves): a
+// shuffle scan inside each wave, then wave 0 scans the 16 wave totals.
 __device__ inline int block_inclusive_scan(int x, int* s_wave, int& total) {
+  constexpr int kWaves = kPlanThreads / kWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -30,18 +32,19 @@ __device__ inline int block_inclusive_scan(int x, int* s_wave, int& total) {
   }
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < kPlanThreads / kWave; ++i) {
-      const int t = s_wave[i];
-      s_wave[i] = acc;  // exclusive offsets of each wave
-      acc += t;
+  if (wave == 0) {
+    int t = lane < kWaves ? s_wave[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < kWaves; d <<= 1) {
+      const int y = __shfl_up(t, d, kWave);
+      if (lane >= d) t += y;
     }
-    s_wave[kPlanThreads / kWave] = acc;
+    if (lane < kWaves) s_wave[lane + 1] = t;  // inclusive totals, shifted: exclusive offsets
+    if (lane == 0) s_wave[0] = 0;
   }
   __syncthreads();
   x += s_wave[wave];
-  total = s_wave[kPlanThreads / kWave];
+  total = s_wave[kWaves];
   __syncthreads();  // s_wave is reused by the next call
   return x;
 }

@@ -46,8 +46,10 @@ class DecodeConfig:
         return torch.bfloat16 if self.kv_dtype == "bf16" else torch.uint8
 
     def pool_elems(self):
+        """Elements a pool must hold: one past the last element of the last tile."""
         s = self.shape()
-        return max(s.num_pages * s.page_stride, s.num_kv_heads * s.head_stride)
+        return ((s.num_pages - 1) * s.page_stride + (s.num_kv_heads - 1) * s.head_stride
+                + B.TILE_ELEMS)
 
 
 @dataclass

@@ -113,13 +113,17 @@ def _fill_pool(out, children, scale, kv_dtype, device):
             out[s:s + m].copy_((v / scale).clamp_(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8))
 
 
-def make_inputs(w: Workload, device="cpu", spare_pages=None):
+def make_inputs(w: Workload, device="cpu", spare_pages=None, kv_interleave=False):
     """Draw one step's inputs for workload ``w`` on ``device``.
 
     Returns a dict of tensors: q [B,Hq,D] bf16, k/v [B,Hkv,D] bf16,
     q_norm_w/k_norm_w [D] bf16, positions [B] int32, seq_lens [B] int32,
     block_table [B, max_blocks] int32, k_cache/v_cache flat pools (bf16 or
     uint8 E4M3 codes) of num_pages * Hkv * 8192 elements, and metadata.
+
+    kv_interleave: K and V share one allocation, the V tile of every (page,
+    KV head) right after its K tile (head stride 16384, page stride
+    Hkv * 16384 elements); k_cache and v_cache are views 8192 elements apart.
     """
     device = torch.device(device)
     ss = np.random.SeedSequence(w.seed).spawn(9)
@@ -142,10 +146,24 @@ def make_inputs(w: Workload, device="cpu", spare_pages=None):
     wk = 1 + 0.1 * np.random.default_rng(ss[5]).standard_normal(D, dtype=np.float32)
     pool_elems = num_pages * Hkv * TILE
     cache_dtype = torch.bfloat16 if w.kv_dtype == "bf16" else torch.uint8
-    k_cache = torch.empty(pool_elems, dtype=cache_dtype, device=device)
-    v_cache = torch.empty(pool_elems, dtype=cache_dtype, device=device)
-    _fill_pool(k_cache, ss[7], w.k_scale, w.kv_dtype, device)
-    _fill_pool(v_cache, ss[8], w.v_scale, w.kv_dtype, device)
+    if kv_interleave:
+        both = torch.empty(2 * pool_elems, dtype=cache_dtype, device=device)
+        tiles = both.view(num_pages * Hkv, 2, TILE)
+        k_tmp = torch.empty(pool_elems, dtype=cache_dtype, device=device)
+        _fill_pool(k_tmp, ss[7], w.k_scale, w.kv_dtype, device)
+        tiles[:, 0].copy_(k_tmp.view(-1, TILE))
+        _fill_pool(k_tmp, ss[8], w.v_scale, w.kv_dtype, device)
+        tiles[:, 1].copy_(k_tmp.view(-1, TILE))
+        del k_tmp
+        k_cache = both[:2 * pool_elems - TILE]
+        v_cache = both[TILE:]
+        page_stride, head_stride = 2 * Hkv * TILE, 2 * TILE
+    else:
+        k_cache = torch.empty(pool_elems, dtype=cache_dtype, device=device)
+        v_cache = torch.empty(pool_elems, dtype=cache_dtype, device=device)
+        _fill_pool(k_cache, ss[7], w.k_scale, w.kv_dtype, device)
+        _fill_pool(v_cache, ss[8], w.v_scale, w.kv_dtype, device)
+        page_stride, head_stride = Hkv * TILE, TILE
     return {
         "q": _bf16(q).to(device), "k": _bf16(k).to(device), "v": _bf16(v).to(device),
         "q_norm_w": _bf16(wq).to(device), "k_norm_w": _bf16(wk).to(device),
@@ -153,7 +171,7 @@ def make_inputs(w: Workload, device="cpu", spare_pages=None):
         "seq_lens": torch.from_numpy(lens.astype(np.int32)).to(device),
         "block_table": torch.from_numpy(bt).to(device),
         "k_cache": k_cache, "v_cache": v_cache,
-        "num_pages": num_pages, "page_stride": Hkv * TILE, "head_stride": TILE,
+        "num_pages": num_pages, "page_stride": page_stride, "head_stride": head_stride,
         "max_blocks": max_blocks, "total_tiles": T,
     }
 
