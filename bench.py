@@ -115,6 +115,22 @@ class Case:
         lb.decode_step_timed(*self.args(0, sched), trace=tr)
         return tr.cpu().numpy()
 
+    def plan(self, sched):
+        """The schedule the last step under `sched` used, read back from its workspace."""
+        torch.cuda.synchronize()
+        return lb.read_plan(self.cfg, self.w.batch, sched, self.workspace(sched))
+
+    def calibrate(self, P, reps=8):
+        """Per-XCD weights from traced steps: a round with equal shares, then a
+        round under the first estimate; the two rounds' rates are averaged."""
+        rates, wts = [], None
+        for _ in range(2):
+            sched = lb.Schedule("dynamic", num_workers=P, xcd_weights=wts)
+            traces = [self.trace(sched) for _ in range(reps)]
+            rates.append(lb.xcd_rates(traces, self.plan(sched)))
+            wts = lb.xcd_weights_from_rates(np.mean(rates, axis=0))
+        return wts, np.mean(rates, axis=0)
+
     def graph_ms(self, sched, steps):
         """Step time with the step captured once in a graph and replayed."""
         s = torch.cuda.Stream()
@@ -190,7 +206,7 @@ def measured_traffic(workload, kv_dtype):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def cpu_baseline(w, dev):
+def cpu_baseline(w, dev, min_seconds=10.0):
     """The fp64 oracle on the host: the whole step (plan, prologue, attention over
     every sequence and head) on a fresh input set of the workload, drawn by the
     seeded generator on the device and copied to the host untouched."""
@@ -214,31 +230,48 @@ def cpu_baseline(w, dev):
     cfg = {"kv_dtype": w.kv_dtype, "k_scale": w.k_scale, "v_scale": w.v_scale,
            "sm_scale": 1 / np.sqrt(128.0), "page_stride": page_stride,
            "head_stride": head_stride, "num_kv_heads": w.num_kv_heads}
+    reps, dt = 0, 0.0
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        oracle.plan_dynamic(lens, 256)
-        pro = oracle.prologue(bits["q"], bits["k"], bits["v"], host["positions"].numpy(),
-                              bits["q_norm_w"], bits["k_norm_w"], bt, theta=w.rope_theta,
-                              eps=w.rms_eps, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
-                              v_scale=w.v_scale)
-        oracle.decode_attention(pro["q_out"], (kp, vp), pro, lens, bt, cfg)
-        dt = time.perf_counter() - t0
-    nbytes = compulsory_bytes(w)["total"]
+        while dt < min_seconds:       # repeat the whole step for ~10 s of CPU work
+            t0 = time.perf_counter()
+            oracle.plan_dynamic(lens, 256)
+            pro = oracle.prologue(bits["q"], bits["k"], bits["v"], host["positions"].numpy(),
+                                  bits["q_norm_w"], bits["k_norm_w"], bt, theta=w.rope_theta,
+                                  eps=w.rms_eps, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
+                                  v_scale=w.v_scale)
+            oracle.decode_attention(pro["q_out"], (kp, vp), pro, lens, bt, cfg)
+            dt += time.perf_counter() - t0
+            reps += 1
+    nbytes = compulsory_bytes(w)["total"] * reps
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole {w.name} step (plan, prologue for {w.batch} tokens, "
                       f"full-softmax attention for all {w.batch} sequences x "
-                      f"{w.num_q_heads} heads), fp64 numpy, BLAS limited to 1 thread",
+                      f"{w.num_q_heads} heads), fp64 numpy, BLAS limited to 1 thread, "
+                      f"repeated {reps} times",
             "seconds": round(dt, 2)}
 
 
-def measure(w, dev, P, steps, warmup, full):
-    """Dynamic step time, per-kernel times, and (full) graph time and static sweep."""
-    dyn = lb.Schedule("dynamic")
+def measure(w, dev, P, steps, warmup, full, weighted=True):
+    """Dynamic step time (XCD-weighted shares unless weighted=False, and with
+    equal shares), per-kernel times, and (full) graph time and static sweep."""
+    equal = lb.Schedule("dynamic", num_workers=P)
     case = Case(w, dev)
-    r = {"ms": case.timed_steps(dyn, steps, warmup)}
+    for i in range(warmup):
+        case.step(i, equal)
+    r = {}
+    if weighted:
+        wts, rates = case.calibrate(P)
+        r["xcd_weights"], r["xcd_rates"] = list(wts), [round(float(x), 5) for x in rates]
+        dyn = lb.Schedule("dynamic", num_workers=P, xcd_weights=wts)
+    else:
+        dyn = equal
+    r["ms"] = case.timed_steps(dyn, steps, warmup)
+    r["ms_equal_shares"] = case.timed_steps(equal, steps, warmup) if weighted else r["ms"]
     _, kmean = case.kernel_times(dyn, max(20, min(steps, 100)))
     r["kernel_ms"] = kmean
     r["balance"] = {"dynamic": load_balance(case.trace(dyn))}
+    if weighted:
+        r["balance"]["dynamic_equal_shares"] = load_balance(case.trace(equal))
     if full:
         r["balance"]["static_default"] = load_balance(case.trace(lb.Schedule("static", num_workers=P)))
         r["graph_ms"] = case.graph_ms(dyn, steps)
@@ -264,6 +297,8 @@ def main():
                     help="only run a plain 1 GiB device copy 5 times (a known-size kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-xcd-weights", action="store_true",
+                    help="equal worker shares only (skip the per-XCD rate calibration)")
     ap.add_argument("--quick", action="store_true",
                     help="headline workload only: no graph, static sweep, FP8 or CPU legs")
     args = ap.parse_args()
@@ -285,7 +320,8 @@ def main():
     full = not args.quick
 
     w = wl.named(args.workload)
-    r = measure(w, dev, P, args.steps, args.warmup, full)
+    weighted = not args.no_xcd_weights
+    r = measure(w, dev, P, args.steps, args.warmup, full, weighted)
     ms = r["ms"]
     cb = compulsory_bytes(w)
     value = cb["total"] / (ms * 1e-3) / 1e9
@@ -301,8 +337,13 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[w.name],
                    "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": 128, "page": 64, "kv_cache": w.kv_dtype,
-                   "schedule": f"dynamic, {P} workers", "parallelism": "1 GPU"},
+                   "schedule": f"dynamic, {P} workers" + (", XCD-weighted shares" if weighted
+                                                             else ", equal shares"),
+                   "parallelism": "1 GPU"},
         "us_per_step": round(ms * 1e3, 2),
+        "us_per_step_equal_shares": round(r["ms_equal_shares"] * 1e3, 2),
+        "xcd_weights": r.get("xcd_weights"),
+        "xcd_rates_tiles_per_us": r.get("xcd_rates"),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "compulsory_bytes": cb["total"],
         "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, r["kernel_ms"])},
@@ -323,7 +364,7 @@ def main():
                                                "best_S": round(best / ms, 3)}
         if w.name == "mix":
             w8 = wl.named("mix_fp8")
-            r8 = measure(w8, dev, P, args.steps, args.warmup, full)
+            r8 = measure(w8, dev, P, args.steps, args.warmup, full, weighted)
             ms8 = r8["ms"]
             cb8 = compulsory_bytes(w8)["total"]
             sp8 = split_kernel_bytes(w8) / (float(r8["kernel_ms"][1]) * 1e-3) / 1e9
@@ -333,6 +374,8 @@ def main():
                 "workload": "mix_fp8: the same mix with an FP8 E4M3 cache "
                             "(k scale 2^-5, v scale 2^-4)",
                 "us_per_step": round(ms8 * 1e3, 2),
+                "us_per_step_equal_shares": round(r8["ms_equal_shares"] * 1e3, 2),
+                "xcd_weights": r8.get("xcd_weights"),
                 "us_per_step_graph": round(r8["graph_ms"] * 1e3, 2),
                 "value_GBs": round(cb8 / (ms8 * 1e-3) / 1e9, 1),
                 "hbm_frac_step": round(cb8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

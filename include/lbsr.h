@@ -54,7 +54,9 @@
 extern "C" {
 #endif
 
-#define LBSR_ABI_VERSION 1
+#define LBSR_ABI_VERSION 2
+#define LBSR_NUM_XCDS 8     /* accelerator complex dies of an MI355X */
+#define LBSR_MAX_XCD_WEIGHT 65536
 #define LBSR_HEAD_DIM 128
 #define LBSR_PAGE_SIZE 64
 #define LBSR_TILE_ELEMS (LBSR_HEAD_DIM * LBSR_PAGE_SIZE) /* 8192 elements */
@@ -124,6 +126,10 @@ typedef struct {
   int32_t num_workers;   /* dynamic: P workers in [1, 1024]; 0 -> the device's CU count */
   int32_t static_splits; /* static: S splits per sequence in [1, 1024]; 0 -> max(1, P / batch) */
   int32_t reserved;      /* must be 0 */
+  /* dynamic only: relative streaming speed of the compute units of each XCD
+   * (see lbsr_plan).  All 0 -> every worker gets an equal share; else every
+   * entry in [1, LBSR_MAX_XCD_WEIGHT].  Ignored (must be 0) for static. */
+  int32_t xcd_weight[LBSR_NUM_XCDS];
 } lbsr_sched_cfg;
 
 /* Byte offsets of the arrays inside a workspace (all 256-byte aligned). */
@@ -202,8 +208,16 @@ lbsr_status lbsr_rope_norm_kv_write(const lbsr_shape *shape, const lbsr_params *
  * Tile schedule ([A] "Why does dynamic scheduling matter in attention?").
  * A sequence of length L (the new token included) has n = ceil(L/64) tiles.
  *   dynamic: all tiles laid end to end (T in total); worker w of P owns flat
- *            tiles [floor(w*T/P), floor((w+1)*T/P)), cut at sequence ends
- *            into chunks, numbered in flat order.
+ *            tiles [floor(T*C(w)/C(P)), floor(T*C(w+1)/C(P))), cut at
+ *            sequence ends into chunks, numbered in flat order.  C(w) is the
+ *            summed weight of workers 0..w-1.  Unweighted, every worker
+ *            weighs 1 and C(w) = w.  Weighted, a worker weighs
+ *            xcd_weight[x] of the XCD x it runs on: the attention launch
+ *            (workgroup i runs on XCD i mod 8) gives XCD x the contiguous
+ *            workers [s(x), s(x) + n(x)), n(x) = ceil((P - x) / 8),
+ *            s(x) = n(0) + ... + n(x-1).  MI355X's XCDs stream HBM at
+ *            measurably different rates; weights proportional to those
+ *            rates let all workers finish together.
  *   static:  every sequence is cut into the same S parts of its own tiles,
  *            [floor(s*n/S), floor((s+1)*n/S)); worker b*S+s; empty parts skipped.
  * Writes the arrays of lbsr_ws_layout into `workspace` (one workgroup, no

@@ -16,9 +16,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # LBSR_LIB may name another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("LBSR_LIB") or os.path.join(HERE, "liblbsr.so")
 
+ABI_VERSION = 2
 HEAD_DIM = 128
 PAGE_SIZE = 64
 TILE_ELEMS = HEAD_DIM * PAGE_SIZE
+NUM_XCDS = 8
+MAX_XCD_WEIGHT = 65536
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 KV_BF16, KV_FP8_E4M3 = 0, 1
@@ -63,7 +66,8 @@ class Params(ctypes.Structure):
 
 class SchedCfg(ctypes.Structure):
     _fields_ = [("sched", ctypes.c_int32), ("num_workers", ctypes.c_int32),
-                ("static_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("static_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("xcd_weight", ctypes.c_int32 * NUM_XCDS)]
 
 
 class WsLayout(ctypes.Structure):
@@ -125,6 +129,11 @@ def lib():
                         "(hipcc, gfx950); there is no fallback implementation")
                 handle = ctypes.CDLL(LIB_PATH)
                 _declare(handle)
+                got = handle.lbsr_abi_version()
+                if got != ABI_VERSION:
+                    raise LibraryNotBuilt(
+                        f"{LIB_PATH} has ABI version {got}, this binding needs {ABI_VERSION}: "
+                        "rebuild it with __graft_entry__.build()")
                 _lib = handle
     return _lib
 

@@ -148,6 +148,17 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
     return fail(LBSR_E_INVALID, "num_workers %d out of [0, 1024]", cfg->num_workers);
   if (cfg->static_splits < 0 || cfg->static_splits > 1024)
     return fail(LBSR_E_INVALID, "static_splits %d out of [0, 1024]", cfg->static_splits);
+  int nonzero = 0;
+  for (int x = 0; x < LBSR_NUM_XCDS; ++x) {
+    const int32_t wt = cfg->xcd_weight[x];
+    if (wt < 0 || wt > LBSR_MAX_XCD_WEIGHT)
+      return fail(LBSR_E_INVALID, "xcd_weight[%d] = %d out of [0, %d]", x, wt, LBSR_MAX_XCD_WEIGHT);
+    nonzero += wt != 0;
+  }
+  if (nonzero != 0 && nonzero != LBSR_NUM_XCDS)
+    return fail(LBSR_E_INVALID, "xcd_weight must be all 0 or all in [1, %d]", LBSR_MAX_XCD_WEIGHT);
+  if (nonzero != 0 && cfg->sched != LBSR_SCHED_DYNAMIC)
+    return fail(LBSR_E_INVALID, "xcd_weight applies to the dynamic schedule only");
   int32_t P = cfg->num_workers;
   if (P == 0) {
     DeviceInfo d;
@@ -275,11 +286,20 @@ lbsr_status run_prologue(const lbsr_shape* shape, const lbsr_params* params, int
                     "prologue launch");
 }
 
+lbsr::SchedParams sched_params(const lbsr_sched_cfg* cfg, const lbsr_ws_layout& l) {
+  lbsr::SchedParams sp{};
+  sp.dynamic = cfg->sched == LBSR_SCHED_DYNAMIC;
+  sp.num_workers = l.num_workers;
+  sp.splits = l.static_splits;
+  sp.weighted = sp.dynamic && cfg->xcd_weight[0] != 0;  // validated: all zero or all positive
+  for (int x = 0; x < lbsr::kXcds; ++x) sp.xcd_weight[x] = sp.weighted ? cfg->xcd_weight[x] : 1;
+  return sp;
+}
+
 lbsr_status run_plan(const lbsr_shape* shape, int32_t batch, const int32_t* seq_lens,
                      const lbsr_sched_cfg* cfg, const lbsr_ws_layout& l, void* ws, hipStream_t stream) {
   return hip_status(lbsr::launch_plan(seq_lens, batch, shape->max_blocks_per_seq,
-                                      cfg->sched == LBSR_SCHED_DYNAMIC, l.num_workers,
-                                      l.static_splits, plan_ptrs(ws, l), stream),
+                                      sched_params(cfg, l), plan_ptrs(ws, l), stream),
                     "plan launch");
 }
 
@@ -292,8 +312,8 @@ lbsr_status run_plan_prologue(const lbsr_shape* shape, const lbsr_params* params
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
   return hip_status(
-      lbsr::launch_plan_prologue(seq_lens, cfg->sched == LBSR_SCHED_DYNAMIC, l.num_workers,
-                                 l.static_splits, plan_ptrs(ws, l), geo, fp8, q, k, v, positions,
+      lbsr::launch_plan_prologue(seq_lens, sched_params(cfg, l), plan_ptrs(ws, l), geo, fp8, q,
+                                 k, v, positions,
                                  wq, wk, bt, kc, vc, q_out, params->rope_theta,
                                  (double)params->rms_eps, params->norm_before_rope,
                                  fp8 ? params->k_scale : 1.0, fp8 ? params->v_scale : 1.0, stream),

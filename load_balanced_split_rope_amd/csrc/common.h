@@ -15,7 +15,26 @@ constexpr int kMaxBatch = 16384;   // the plan keeps per-sequence prefix sums in
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxAttnWaves = 8;   // waves (KV heads in flight) per attention workgroup
 
+constexpr int kXcds = 8;           // an MI355X has 8 XCDs; workgroup i is dispatched to XCD i % 8
+constexpr int kMaxXcdWeight = 65536;
+
 enum : int32_t { kErrSeqLen = 1, kErrPage = 2, kErrPosition = 4 };
+
+// Number of the P attention workgroups that land on XCD x (those i < P with
+// i % 8 == x).  Workers are handed out so that XCD x runs a contiguous range
+// of this many workers, XCD 0's first.
+__host__ __device__ inline int xcd_run_size(int x, int num_workers) {
+  return (num_workers - x + kXcds - 1) / kXcds;
+}
+
+// The schedule's parameters, passed by value.
+struct SchedParams {
+  int32_t dynamic;       // 1: length-proportional, 0: static split
+  int32_t num_workers;   // P (dynamic)
+  int32_t splits;        // S (static)
+  int32_t weighted;      // dynamic: 1 if xcd_weight is used
+  int32_t xcd_weight[kXcds];
+};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -14,9 +14,8 @@ hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const v
                            double eps, int norm_first, double k_scale, double v_scale,
                            hipStream_t stream);
 
-hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, bool dynamic,
-                       int num_workers, int static_splits, const PlanPtrs& plan,
-                       hipStream_t stream);
+hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, const SchedParams& sp,
+                       const PlanPtrs& plan, hipStream_t stream);
 
 hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers,
                                   const void* q_out, const void* k_cache, const void* v_cache,
@@ -29,8 +28,8 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
                           int max_chunks_per_seq, bool fold_token_status, hipStream_t stream);
 
-hipError_t launch_plan_prologue(const int32_t* seq_lens, bool dynamic, int num_workers,
-                                int static_splits, const PlanPtrs& plan, const Geometry& geo,
+hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
+                                const PlanPtrs& plan, const Geometry& geo,
                                 bool fp8, const void* q, const void* k, const void* v,
                                 const int32_t* positions, const void* wq, const void* wk,
                                 const int32_t* block_table, void* k_cache, void* v_cache,

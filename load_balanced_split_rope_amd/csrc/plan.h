@@ -9,10 +9,17 @@
 // worker's range is cut at sequence ends into chunks.  The static baseline
 // cuts every sequence into the same S parts of its own length.
 //
+// Weighted variant (an MI355X refinement; equal weights give the rule above
+// exactly): MI355X's XCDs stream HBM at different rates (about 10% apart
+// between the fastest and slowest under a full-chip stream), so equal shares
+// leave the fast XCDs idle at the end.  With per-XCD weights, worker w takes
+// [floor(T*C(w)/C(P)), floor(T*C(w+1)/C(P))) where C(w) sums the weights of
+// workers 0..w-1 and a worker weighs the weight of the XCD that runs it.
+//
 // One 1024-thread workgroup: per-sequence prefix sums live in LDS (s_cu holds
 // batch + 1 ints, batch <= 16384); counts per worker are scanned in
 // 1024-wide rounds with a carry.
-// Everything is integer arithmetic; products w*T are 64-bit.
+// Everything is integer arithmetic; products T*C(w) are 64-bit.
 
 #pragma once
 
@@ -59,11 +66,26 @@ __device__ inline int seq_of_tile(const int* cu, int batch, int t) {
   return lo;
 }
 
+// C(w): summed weight of workers 0..w-1 (w itself when unweighted).  XCD x
+// runs the contiguous workers that follow XCD x-1's.
+__device__ inline int64_t cumulative_weight(const SchedParams& sp, int w) {
+  if (!sp.weighted) return w;
+  int64_t c = 0;
+  int start = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const int n = xcd_run_size(x, sp.num_workers);
+    if (w < start + n) return c + (int64_t)(w - start) * sp.xcd_weight[x];
+    c += (int64_t)n * sp.xcd_weight[x];
+    start += n;
+  }
+  return c;
+}
+
 // The whole schedule, computed by one 1024-thread workgroup; s_cu is LDS of
 // at least batch + 1 ints.
 __device__ inline void plan_body(const int32_t* __restrict__ seq_lens, int batch, int max_blocks,
-                                 int dynamic, int num_workers, int splits, const PlanPtrs& plan,
-                                 int* s_cu) {
+                                 const SchedParams& sp, const PlanPtrs& plan, int* s_cu) {
+  const int dynamic = sp.dynamic, num_workers = sp.num_workers, splits = sp.splits;
   __shared__ int s_wave[kPlanThreads / kWave + 1];
   const int tid = threadIdx.x;
   if (tid == 0) plan.error_word[0] = 0;
@@ -95,6 +117,7 @@ __device__ inline void plan_body(const int32_t* __restrict__ seq_lens, int batch
 
   // 2. chunk counts per worker, their prefix sums, and the chunks themselves
   const int W = dynamic ? num_workers : batch * splits;
+  const int64_t c_total = dynamic ? cumulative_weight(sp, W) : 1;  // <= 1024 * 65536
   carry = 0;
   for (int base = 0; base < W; base += kPlanThreads) {
     const int w = base + tid;
@@ -102,17 +125,18 @@ __device__ inline void plan_body(const int32_t* __restrict__ seq_lens, int batch
     int s = 0, e = 0;
     if (w < W) {
       if (dynamic) {
-        s = (int)(((int64_t)w * T) / W);
-        e = (int)(((int64_t)(w + 1) * T) / W);
+        // T < 2^31 and C(w) <= 2^26: the products fit in 64 bits
+        s = (int)(((int64_t)T * cumulative_weight(sp, w)) / c_total);
+        e = (int)(((int64_t)T * cumulative_weight(sp, w + 1)) / c_total);
         if (s < e) {
           first = seq_of_tile(s_cu, batch, s);
           cnt = seq_of_tile(s_cu, batch, e - 1) - first + 1;
         }
       } else {
-        const int b = w / splits, sp = w - b * splits;
+        const int b = w / splits, part = w - b * splits;
         const int n = s_cu[b + 1] - s_cu[b];
-        s = (int)(((int64_t)sp * n) / splits);
-        e = (int)(((int64_t)(sp + 1) * n) / splits);
+        s = (int)(((int64_t)part * n) / splits);
+        e = (int)(((int64_t)(part + 1) * n) / splits);
         first = b;
         cnt = e > s ? 1 : 0;
       }

@@ -14,8 +14,7 @@ namespace lbsr {
 
 template <bool kFp8>
 __global__ __launch_bounds__(kPlanThreads) void plan_prologue_kernel(
-    const int32_t* __restrict__ seq_lens, int dynamic, int num_workers, int splits,
-    PlanPtrs plan, Geometry geo, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ seq_lens, SchedParams sp, PlanPtrs plan, Geometry geo, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ positions,
     const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
     const int32_t* __restrict__ block_table, void* __restrict__ k_cache,
@@ -23,7 +22,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prologue_kernel(
     int norm_first, double k_scale, double v_scale) {
   extern __shared__ int s_cu[];
   if (blockIdx.x == 0) {
-    plan_body(seq_lens, geo.batch, geo.max_blocks, dynamic, num_workers, splits, plan, s_cu);
+    plan_body(seq_lens, geo.batch, geo.max_blocks, sp, plan, s_cu);
     return;
   }
   const int rows = geo.num_q_heads + 2 * geo.num_kv_heads;
@@ -37,8 +36,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prologue_kernel(
                      v_scale);
 }
 
-hipError_t launch_plan_prologue(const int32_t* seq_lens, bool dynamic, int num_workers,
-                                int static_splits, const PlanPtrs& plan, const Geometry& geo,
+hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
+                                const PlanPtrs& plan, const Geometry& geo,
                                 bool fp8, const void* q, const void* k, const void* v,
                                 const int32_t* positions, const void* wq, const void* wk,
                                 const int32_t* block_table, void* k_cache, void* v_cache,
@@ -52,12 +51,12 @@ hipError_t launch_plan_prologue(const int32_t* seq_lens, bool dynamic, int num_w
   auto* vv = (const uint16_t*)v;
   if (fp8)
     plan_prologue_kernel<true><<<blocks, kPlanThreads, lds, stream>>>(
-        seq_lens, dynamic ? 1 : 0, num_workers, static_splits, plan, geo, qq, kk, vv, positions,
+        seq_lens, sp, plan, geo, qq, kk, vv, positions,
         (const uint16_t*)wq, (const uint16_t*)wk, block_table, k_cache, v_cache,
         (uint16_t*)q_out, theta, eps, norm_first, k_scale, v_scale);
   else
     plan_prologue_kernel<false><<<blocks, kPlanThreads, lds, stream>>>(
-        seq_lens, dynamic ? 1 : 0, num_workers, static_splits, plan, geo, qq, kk, vv, positions,
+        seq_lens, sp, plan, geo, qq, kk, vv, positions,
         (const uint16_t*)wq, (const uint16_t*)wk, block_table, k_cache, v_cache,
         (uint16_t*)q_out, theta, eps, norm_first, k_scale, v_scale);
   return hipGetLastError();

@@ -54,16 +54,25 @@ class DecodeConfig:
 
 @dataclass
 class Schedule:
-    """lbsr_sched_cfg: "dynamic" (P workers, 0 = CU count) or "static" (S splits, 0 = P/B)."""
+    """lbsr_sched_cfg: "dynamic" (P workers, 0 = CU count) or "static" (S splits, 0 = P/B).
+
+    xcd_weights: None (equal shares) or 8 integer weights in [1, 65536], the
+    relative streaming rate of each XCD's compute units (dynamic only).
+    """
     kind: str = "dynamic"
     num_workers: int = 0
     static_splits: int = 0
+    xcd_weights: tuple = None
 
     def cfg(self):
         if self.kind not in ("dynamic", "static"):
             raise ValueError(f"unknown schedule {self.kind!r}")
+        wts = [0] * B.NUM_XCDS if self.xcd_weights is None else [int(x) for x in self.xcd_weights]
+        if len(wts) != B.NUM_XCDS:
+            raise ValueError(f"xcd_weights needs {B.NUM_XCDS} entries, got {len(wts)}")
         return B.SchedCfg(B.SCHED_DYNAMIC if self.kind == "dynamic" else B.SCHED_STATIC,
-                          self.num_workers, self.static_splits, 0)
+                          self.num_workers, self.static_splits, 0,
+                          (ctypes.c_int32 * B.NUM_XCDS)(*wts))
 
 
 def device_workers(device=0):
@@ -246,3 +255,41 @@ def read_error(cfg: DecodeConfig, batch: int, sched: Schedule, workspace):
     """The workspace's sticky device error bits (synchronises)."""
     lay = workspace_layout(cfg, batch, sched)
     return int(workspace[lay.error_word:lay.error_word + 4].cpu().numpy().view(np.int32)[0])
+
+
+def xcd_rates(traces, plans):
+    """Measured tile rate (tiles per microsecond of busy time) of each XCD.
+
+    traces: per-worker records of split-attention launches, int64 [W, 4] =
+    (start, end) of the 100 MHz constant clock, HW_ID, XCC_ID, as written by
+    decode_step_timed(trace=...); plans: the matching read_plan() dicts (one
+    per trace, or a single one for all).  XCD x's rate is the tiles its
+    workers processed over the sum of their busy times.
+    """
+    if isinstance(plans, dict):
+        plans = [plans] * len(traces)
+    tiles = np.zeros(B.NUM_XCDS)
+    busy = np.zeros(B.NUM_XCDS)
+    for tr, pl in zip(traces, plans):
+        tr = np.asarray(tr)
+        per_worker = np.zeros(tr.shape[0])
+        ch = np.asarray(pl["chunks"])
+        np.add.at(per_worker, ch[:, 3], ch[:, 2] - ch[:, 1])
+        x = tr[:, 3] & 0xF
+        dur = (tr[:, 1] - tr[:, 0]) / 100.0
+        for i in range(B.NUM_XCDS):
+            m = x == i
+            tiles[i] += per_worker[m].sum()
+            busy[i] += dur[m].sum()
+    if np.any(busy <= 0):
+        raise ValueError("every XCD must have run a worker with work")
+    return tiles / busy
+
+
+def xcd_weights_from_rates(rates, scale=4096):
+    """Integer weights for Schedule.xcd_weights: scale * rate / max(rate), at least 1."""
+    r = np.asarray(rates, dtype=np.float64)
+    if r.shape != (B.NUM_XCDS,) or not np.all(r > 0):
+        raise ValueError("need 8 positive rates")
+    w = np.clip(np.rint(scale * r / r.max()), 1, B.MAX_XCD_WEIGHT).astype(np.int64)
+    return tuple(int(v) for v in w)

@@ -15,6 +15,13 @@ Readings:
   [floor(w*T/P), floor((w+1)*T/P)).  A worker's range is cut where a sequence
   ends; each piece is a *chunk* (sequence, first tile, end tile, worker), with
   tile indices local to the sequence.  Chunks are numbered in flat order.
+* R11w (weighted dynamic, an MI355X refinement; the pages assume equal
+  compute units) -- worker w weighs the weight of the XCD that runs it and
+  owns flat tiles [floor(T*C(w)/C(P)), floor(T*C(w+1)/C(P))), C(w) being the
+  summed weight of workers 0..w-1.  The attention launch deals workgroup i to
+  XCD i mod 8 and gives each XCD a contiguous run of workers, XCD 0's first,
+  so XCD x runs as many workers as there are i < P with i mod 8 == x.  Equal
+  weights give R11 exactly.
 * R12 (static) -- every sequence gets the same number of splits S
   (default max(1, floor(P/B))); split s of sequence b covers its tiles
   [floor(s*n_b/S), floor((s+1)*n_b/S)) and is worker b*S + s; empty splits
@@ -65,8 +72,29 @@ def _seq_chunk(chunks, batch):
     return seq_chunk
 
 
-def plan_dynamic(seq_lens, num_workers):
-    """Length-proportional schedule over flat 64-token tiles (R11)."""
+NUM_XCDS = 8
+
+
+def workers_per_xcd(num_workers):
+    """How many of the P workgroups each XCD receives when workgroup i goes to XCD i mod 8 (R11w)."""
+    return [len(range(x, int(num_workers), NUM_XCDS)) for x in range(NUM_XCDS)]
+
+
+def worker_weights(num_workers, xcd_weights=None):
+    """Weight of every worker: 1 each, or its XCD's weight, XCD 0's run first (R11w)."""
+    P = int(num_workers)
+    if xcd_weights is None:
+        return [1] * P
+    if len(xcd_weights) != NUM_XCDS or any(int(x) < 1 for x in xcd_weights):
+        raise ValueError("xcd_weights: 8 positive integers")
+    out = []
+    for x, count in enumerate(workers_per_xcd(P)):
+        out += [int(xcd_weights[x])] * count
+    return out
+
+
+def plan_dynamic(seq_lens, num_workers, xcd_weights=None):
+    """Length-proportional schedule over flat 64-token tiles (R11; R11w with weights)."""
     n = tiles_per_sequence(seq_lens)
     batch = n.size
     cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
@@ -74,11 +102,14 @@ def plan_dynamic(seq_lens, num_workers):
     P = int(num_workers)
     if P < 1:
         raise ValueError("need at least one worker")
+    cum = [0]
+    for wt in worker_weights(P, xcd_weights):
+        cum.append(cum[-1] + wt)
     chunks = []
     worker_chunk = [0]
     for w in range(P):
-        start = (w * total) // P
-        end = ((w + 1) * total) // P
+        start = (total * cum[w]) // cum[P]
+        end = (total * cum[w + 1]) // cum[P]
         t = start
         while t < end:
             b = int(np.searchsorted(cu, t, side="right") - 1)   # sequence holding flat tile t

@@ -194,9 +194,9 @@ def split_attention(q_out_bits, pools, pro, seq_lens, block_table, cfg, plan):
     return o, lse, partials
 
 
-def make_plan(seq_lens, sched, num_workers, static_splits=0):
-    """Dynamic or static plan (static_splits 0 -> the default S)."""
+def make_plan(seq_lens, sched, num_workers, static_splits=0, xcd_weights=None):
+    """Dynamic (optionally XCD-weighted) or static plan (static_splits 0 -> the default S)."""
     if sched == "dynamic":
-        return plan_dynamic(seq_lens, num_workers)
+        return plan_dynamic(seq_lens, num_workers, xcd_weights)
     S = static_splits or max(1, int(num_workers) // len(seq_lens))
     return plan_static(seq_lens, S)

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lbsr_abi_version() == 1
+    assert lib.lbsr_abi_version() == 2
     for st in range(5):
         assert lib.lbsr_status_string(st).startswith(b"LBSR_")
     assert lib.lbsr_status_string(99) == b"unknown lbsr_status"
@@ -88,6 +88,31 @@ def test_batch_and_schedule_validation(lib):
     ]:
         assert lib.lbsr_workspace_layout(ctypes.byref(s), batch, ctypes.byref(cfg),
                                          ctypes.byref(out)) == status
+
+
+@pytest.mark.parametrize("kind,weights,status", [
+    ("dynamic", None, B.OK),
+    ("dynamic", (1,) * 8, B.OK),
+    ("dynamic", (B.MAX_XCD_WEIGHT,) * 8, B.OK),
+    ("dynamic", (9, 10, 9, 10, 9, 10, 9, 10), B.OK),
+    ("dynamic", (1, 1, 1, 1, 1, 1, 1, 0), B.E_INVALID),        # some zero, some not
+    ("dynamic", (1, 1, 1, 1, 1, 1, 1, -3), B.E_INVALID),
+    ("dynamic", (1, 1, 1, 1, 1, 1, 1, B.MAX_XCD_WEIGHT + 1), B.E_INVALID),
+    ("static", (1,) * 8, B.E_INVALID),                         # weights are dynamic-only
+    ("static", None, B.OK),
+])
+def test_xcd_weight_validation(lib, kind, weights, status):
+    s = cfg_mix().shape()
+    c = Schedule(kind, num_workers=256, xcd_weights=weights).cfg()
+    out = B.WsLayout()
+    got = lib.lbsr_workspace_layout(ctypes.byref(s), 32, ctypes.byref(c), ctypes.byref(out))
+    assert got == status, lib.lbsr_last_error()
+
+
+def test_sched_cfg_struct_matches_header():
+    """lbsr_sched_cfg is 4 int32 fields and the 8 XCD weights: 48 bytes."""
+    assert ctypes.sizeof(B.SchedCfg) == 48
+    assert B.SchedCfg.xcd_weight.offset == 16
 
 
 def test_entry_points_reject_bad_pointers_before_any_launch(lib):

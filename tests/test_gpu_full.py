@@ -49,13 +49,15 @@ def test_full_workload(name):
                           h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
                           kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
     P = lb.device_workers(0)
-    for sched in (lb.Schedule("dynamic"), lb.Schedule("static")):
+    for sched in (lb.Schedule("dynamic"), lb.Schedule("static"),
+                  lb.Schedule("dynamic", xcd_weights=(9, 10, 9, 10, 9, 10, 9, 10))):
         # the pools keep the pre-step contents the oracle reads: run on a copy
         gg = dict(g)
         gg["k_cache"], gg["v_cache"] = g["k_cache"].clone(), g["v_cache"].clone()
         res = run_step(w, gg, sched)
         assert res["error"] == 0
-        ref_plan = (oracle.plan_dynamic(w.seq_lens, P) if sched.kind == "dynamic"
+        ref_plan = (oracle.plan_dynamic(w.seq_lens, P, sched.xcd_weights)
+                    if sched.kind == "dynamic"
                     else oracle.plan_static(w.seq_lens, max(1, P // w.batch)))
         got = res["plan"]
         for key in ("cu_tiles", "worker_chunk", "chunks", "seq_chunk"):
@@ -63,7 +65,7 @@ def test_full_workload(name):
         assert np.array_equal(bits_u16(res["q_out"]), pro["q_out"]) or \
             np.mean(bits_u16(res["q_out"]) != pro["q_out"]) < 1e-6
         n = sampled_checks(w, gg, res, h, pro)
-        print(f"  {sched.kind}: plan exact, {n} sampled heads match", flush=True)
+        print(f"  {sched}: plan exact, {n} sampled heads match", flush=True)
         del gg, res
         torch.cuda.empty_cache()
 

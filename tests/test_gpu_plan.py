@@ -72,3 +72,38 @@ def test_out_of_range_lengths_are_clamped_and_flagged():
     assert got["error_word"] & lb._binding.DEV_ERR_SEQ_LEN
     assert got["seq_len_eff"].tolist() == [1, 5, 256]
     assert_same(got, oracle.plan_dynamic([1, 5, 256], 4))
+
+
+WEIGHT_SETS = [(1,) * 8, (9, 10, 9, 10, 9, 10, 9, 10), (1, 65536, 3, 700, 2, 1, 65536, 5),
+               (65536,) * 8, (10, 9, 10, 9, 10, 9, 10, 9)]
+
+
+@pytest.mark.parametrize("name", wl.NAMES)
+@pytest.mark.parametrize("P", [1, 7, 256, 1000])
+@pytest.mark.parametrize("wi", range(len(WEIGHT_SETS)))
+def test_named_workloads_weighted(name, P, wi):
+    lens = wl.named(name).seq_lens
+    wts = WEIGHT_SETS[wi]
+    got = device_plan(lens, lb.Schedule("dynamic", num_workers=P, xcd_weights=wts))
+    assert got["error_word"] == 0
+    assert_same(got, oracle.plan_dynamic(lens, P, wts))
+
+
+def test_random_weighted_batches():
+    rng = np.random.default_rng(321)
+    for i in range(150):
+        B = int(rng.integers(1, 300)) if i % 3 else int(rng.integers(1, 3000))
+        lens = rng.integers(1, int(rng.choice([100, 5000, 300_000])), B)
+        P = int(rng.integers(1, 1025))
+        wts = tuple(int(x) for x in rng.integers(1, int(rng.choice([3, 1000, 65537])), 8))
+        assert_same(device_plan(lens, lb.Schedule("dynamic", num_workers=P, xcd_weights=wts)),
+                    oracle.plan_dynamic(lens, P, wts))
+
+
+def test_largest_weighted():
+    """Largest sizes: 16384 sequences of up to 262144 tokens, 1024 workers,
+    maximal weights (T * C(P) near 2^53)."""
+    lens = np.random.default_rng(6).integers(1, 262_145, 16384)
+    wts = (65536, 65535, 65536, 65535, 65534, 65536, 65533, 65536)
+    assert_same(device_plan(lens, lb.Schedule("dynamic", num_workers=1024, xcd_weights=wts)),
+                oracle.plan_dynamic(lens, 1024, wts))

@@ -63,7 +63,9 @@ SMALL = [
 ]
 SCHEDS = [lb.Schedule("dynamic", num_workers=1), lb.Schedule("dynamic", num_workers=5),
           lb.Schedule("dynamic", num_workers=256), lb.Schedule("static", num_workers=256),
-          lb.Schedule("static", num_workers=8, static_splits=3)]
+          lb.Schedule("static", num_workers=8, static_splits=3),
+          lb.Schedule("dynamic", num_workers=256, xcd_weights=(9, 10, 9, 10, 9, 10, 9, 10)),
+          lb.Schedule("dynamic", num_workers=13, xcd_weights=(1, 5, 2, 9, 1, 1, 7, 3))]
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))

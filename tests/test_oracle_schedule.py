@@ -1,5 +1,9 @@
 """Pins for the oracle's schedule: brute force, invariants, property tests."""
 
+import math
+import os
+from fractions import Fraction
+
 import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
@@ -127,3 +131,83 @@ def test_uniform_batch_dynamic_equals_static():
 def test_rejects_empty_sequences():
     with pytest.raises(ValueError):
         plan_dynamic([5, 0], 4)
+
+
+# ---- XCD-weighted dynamic schedule ----
+
+def _golden_weighted():
+    path = os.path.join(os.path.dirname(__file__), "golden", "weighted_schedule_examples.txt")
+    cases = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, tail = line.split(":")
+        nums = [int(x) for x in head.split()]
+        cases.append((nums[0], nums[1], tuple(nums[2:]), [int(x) for x in tail.split()]))
+    return cases
+
+
+def _tiles_per_worker(plan):
+    out = np.zeros(plan.num_workers, dtype=np.int64)
+    for b, t0, t1, w in plan.chunks:
+        out[w] += t1 - t0
+    return out
+
+
+@pytest.mark.parametrize("T,P,weights,expect", _golden_weighted())
+def test_weighted_hand_examples(T, P, weights, expect):
+    # T tiles as T one-tile sequences (any split of T gives the same counts)
+    plan = plan_dynamic([64] * T, P, weights)
+    assert _tiles_per_worker(plan).tolist() == expect
+    check_plan_invariants(plan, [64] * T)
+
+
+def _dispatch_sim(P):
+    """Simulate the launch: workgroup i goes to XCD i % 8; XCDs take worker ids
+    in turn, XCD 0's whole run first.  Returns the XCD of every worker."""
+    per_xcd = [[i for i in range(P) if i % 8 == x] for x in range(8)]
+    xcd_of = []
+    for x in range(8):
+        xcd_of += [x] * len(per_xcd[x])
+    return xcd_of
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.integers(1, 3000), min_size=1, max_size=40), st.integers(1, 300),
+       st.lists(st.integers(1, 65536), min_size=8, max_size=8))
+def test_weighted_shares_and_invariants(lens, P, weights):
+    plan = plan_dynamic(lens, P, weights)
+    check_plan_invariants(plan, lens)
+    T = int(tiles_per_sequence(lens).sum())
+    xcd_of = _dispatch_sim(P)
+    wts = [weights[x] for x in xcd_of]
+    total = sum(wts)
+    got = _tiles_per_worker(plan)
+    for w in range(P):
+        # floor of a running share: within one tile of the exact share
+        assert abs(Fraction(int(got[w])) - Fraction(T * wts[w], total)) < 1
+    # exact bounds from fractions
+    run = 0
+    for w in range(P):
+        lo = math.floor(Fraction(T * run, total))
+        run += wts[w]
+        hi = math.floor(Fraction(T * run, total))
+        assert got[w] == hi - lo
+
+
+@pytest.mark.parametrize("c", [1, 7, 65536])
+def test_equal_weights_are_the_unweighted_plan(c):
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        lens = rng.integers(1, 20000, size=int(rng.integers(1, 50))).tolist()
+        P = int(rng.integers(1, 400))
+        a, b = plan_dynamic(lens, P), plan_dynamic(lens, P, [c] * 8)
+        assert np.array_equal(a.chunks, b.chunks) and np.array_equal(a.worker_chunk, b.worker_chunk)
+
+
+def test_weighted_rejects_bad_weights():
+    with pytest.raises(ValueError):
+        plan_dynamic([100], 8, [1] * 7)
+    with pytest.raises(ValueError):
+        plan_dynamic([100], 8, [1] * 7 + [0])
