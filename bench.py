@@ -266,7 +266,15 @@ def measure(w, dev, P, steps, warmup, full, weighted=True):
     else:
         dyn = equal
     r["ms"] = case.timed_steps(dyn, steps, warmup)
-    r["ms_equal_shares"] = case.timed_steps(equal, steps, warmup) if weighted else r["ms"]
+    if weighted:
+        # A/B of weighted vs equal shares: interleaved short loops, medians
+        tw, te = [], []
+        for _ in range(5):
+            tw.append(case.timed_steps(dyn, 40, 2))
+            te.append(case.timed_steps(equal, 40, 2))
+        r["ab"] = {"weighted_us": round(float(np.median(tw)) * 1e3, 2),
+                   "equal_shares_us": round(float(np.median(te)) * 1e3, 2),
+                   "pairs": 5, "steps_each": 40}
     _, kmean = case.kernel_times(dyn, max(20, min(steps, 100)))
     r["kernel_ms"] = kmean
     r["balance"] = {"dynamic": load_balance(case.trace(dyn))}
@@ -341,9 +349,9 @@ def main():
                                                              else ", equal shares"),
                    "parallelism": "1 GPU"},
         "us_per_step": round(ms * 1e3, 2),
-        "us_per_step_equal_shares": round(r["ms_equal_shares"] * 1e3, 2),
         "xcd_weights": r.get("xcd_weights"),
         "xcd_rates_tiles_per_us": r.get("xcd_rates"),
+        "xcd_weighting_ab": r.get("ab"),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "compulsory_bytes": cb["total"],
         "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, r["kernel_ms"])},
@@ -374,8 +382,8 @@ def main():
                 "workload": "mix_fp8: the same mix with an FP8 E4M3 cache "
                             "(k scale 2^-5, v scale 2^-4)",
                 "us_per_step": round(ms8 * 1e3, 2),
-                "us_per_step_equal_shares": round(r8["ms_equal_shares"] * 1e3, 2),
                 "xcd_weights": r8.get("xcd_weights"),
+                "xcd_weighting_ab": r8.get("ab"),
                 "us_per_step_graph": round(r8["graph_ms"] * 1e3, 2),
                 "value_GBs": round(cb8 / (ms8 * 1e-3) / 1e9, 1),
                 "hbm_frac_step": round(cb8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

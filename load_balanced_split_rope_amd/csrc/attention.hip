@@ -380,9 +380,10 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
 // out as 16 slices of 8 channels x G heads, plus their log2-sum-exp) are read
 // in parallel: workgroup (s, g, b) owns slice run s of sequence b -- 16/S of
 // the 16 slices, one contiguous 128G*4/S-byte piece of every row -- where S
-// grows with n so that every row's piece is read in one round.  A piece is
-// 32G/S float4 (at most 64), so one wave instruction covers 64/(32G/S) rows,
-// and each lane keeps kMergeUnroll rows in flight.  The first round of row
+// grows with n up to the grid's slice count, and rows beyond one round are
+// read in further rounds.  A piece is 32G/S float4 (at most 64), so one wave
+// instruction covers 64/(32G/S) rows, and each lane keeps kMergeUnroll rows
+// in flight.  The first round of row
 // reads is issued before the lse are staged in LDS and turned into weights
 // 2^(lse - max) / sum per head, so the two overlap.  Per-(wave, row-lane)
 // sums are added in a fixed order: deterministic.
@@ -390,7 +391,10 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
 #define LBSR_MERGE_WAVES 4
 #endif
 #ifndef LBSR_MERGE_UNROLL
-#define LBSR_MERGE_UNROLL 16
+#define LBSR_MERGE_UNROLL 8
+#endif
+#ifndef LBSR_MERGE_LSE_UNROLL
+#define LBSR_MERGE_LSE_UNROLL 8
 #endif
 #ifndef LBSR_MERGE_MIN_SLICES
 #define LBSR_MERGE_MIN_SLICES 4
@@ -400,8 +404,13 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
 #endif
 constexpr int kMergeWaves = LBSR_MERGE_WAVES;
 constexpr int kMergeUnroll = LBSR_MERGE_UNROLL;
+constexpr int kMergeLseUnroll = LBSR_MERGE_LSE_UNROLL;
 
-__global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(Geometry geo, PlanPtrs plan,
+// The grid has slices x Hkv x batch workgroups (1024 for 32 sequences of 8 KV
+// heads), most of them short-lived; 4 of them per CU (<= 128 VGPRs per wave)
+// keep the whole grid resident at once, which measured faster than deeper
+// per-thread unrolling at lower occupancy.
+__global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry geo, PlanPtrs plan,
                                                                     uint16_t* __restrict__ out,
                                                                     float* __restrict__ lse_out,
                                                                     int min_slices,
@@ -449,22 +458,22 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(Geometry geo
     }
   };
 
-  // 1. lse of every row, 16 loads per thread per pass, with the first round of
+  // 1. lse of every row, kMergeLseUnroll loads per thread per pass, with the first round of
   //    row reads issued right behind them.  idx = i*G + h: i by a float divide,
   //    exact since idx < 2^14 and the quotient is at least 0.5/G from an integer.
   const int nval = count * G;
   const float inv_g = 1.0f / (float)G;
-  for (int base = 0; base < nval; base += 16 * kThreads) {
-    float v[16];
+  for (int base = 0; base < nval; base += kMergeLseUnroll * kThreads) {
+    float v[kMergeLseUnroll];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kMergeLseUnroll; ++u) {
       const int idx = min(base + tid + u * kThreads, nval - 1);
       const int i = (int)(((float)idx + 0.5f) * inv_g);
       v[u] = plan.partial_lse[(size_t)(c0 + i) * Hq + head0 + (idx - i * G)];
     }
     if (base == 0) load_round(0);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kMergeLseUnroll; ++u) {
       const int idx = base + tid + u * kThreads;
       if (idx < nval) s_w[idx] = v[u];
     }
