@@ -13,6 +13,8 @@ head dim 128; 64-token pages):
 * ``mix``         1 x 131072 + 31 x 4096, 64/8 heads, BF16
 * ``mix_fp8``     the same mix with an FP8 E4M3 cache (k scale 2**-5, v scale 2**-4)
 * ``loguniform``  batch 64, lengths log-uniform in [512, 262144], FP8 E4M3
+* ``mix_mtp2``    the BF16 mix with 2 new tokens per sequence (multi-token
+                  decode, as when one drafted token is verified)
 
 Recipe (per workload, seed s): ``numpy.random.SeedSequence(s)`` spawns child
 streams, in order: 0 lengths, 1 q, 2 k, 3 v, 4 q-norm weight, 5 k-norm weight,
@@ -21,6 +23,9 @@ cache values are N(0, 1); norm weights are 1 + 0.1 N(0, 1); all rounded to
 BF16 (the cache to E4M3 after dividing by its scale).  The pool has
 T + max(16, ceil(T/16)) pages; sequence b gets pages perm[cu[b]:cu[b+1]] of a
 random permutation; unused block-table entries are -1; positions[b] = L_b - 1.
+With Tq > 1 new tokens per sequence, q, k and v gain a token axis after the
+batch axis (drawn as [B, Tq, H, D], so Tq = 1 draws the same values) and
+positions[b, j] = L_b - Tq + j.
 On a GPU the cache contents (up to 5.7 GB) are drawn on the device with a
 torch generator seeded from children 7 and 8, in fixed 2**26-element blocks.
 """
@@ -48,6 +53,7 @@ class Workload:
     rms_eps: float = 1e-6
     norm_before_rope: bool = False
     seed: int = 0
+    tokens: int = 1            # new tokens per sequence (multi-token decode)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -79,10 +85,13 @@ def named(name):
     if name == "loguniform":
         return Workload("loguniform", loguniform_lengths(5), kv_dtype="fp8",
                         k_scale=2.0 ** -5, v_scale=2.0 ** -4, seed=5)
+    if name == "mix_mtp2":
+        return Workload("mix_mtp2", [131072] + [4096] * 31, seed=6, tokens=2)
     raise KeyError(name)
 
 
 NAMES = ("tiny", "uniform", "mix", "mix_fp8", "loguniform")
+MULTI_TOKEN_NAMES = ("mix_mtp2",)
 
 
 def _bf16(x):
@@ -116,8 +125,9 @@ def _fill_pool(out, children, scale, kv_dtype, device):
 def make_inputs(w: Workload, device="cpu", spare_pages=None, kv_interleave=False):
     """Draw one step's inputs for workload ``w`` on ``device``.
 
-    Returns a dict of tensors: q [B,Hq,D] bf16, k/v [B,Hkv,D] bf16,
-    q_norm_w/k_norm_w [D] bf16, positions [B] int32, seq_lens [B] int32,
+    Returns a dict of tensors: q [B,Hq,D] bf16, k/v [B,Hkv,D] bf16 (with a
+    token axis, [B,Tq,H,D], when w.tokens > 1), q_norm_w/k_norm_w [D] bf16,
+    positions [B] int32 ([B,Tq] when w.tokens > 1), seq_lens [B] int32,
     block_table [B, max_blocks] int32, k_cache/v_cache flat pools (bf16 or
     uint8 E4M3 codes) of num_pages * Hkv * 8192 elements, and metadata.
 
@@ -139,9 +149,14 @@ def make_inputs(w: Workload, device="cpu", spare_pages=None, kv_interleave=False
     bt = np.full((B, max_blocks), -1, dtype=np.int32)
     for b in range(B):
         bt[b, :n[b]] = perm[cu[b]:cu[b + 1]]
-    q = np.random.default_rng(ss[1]).standard_normal((B, Hq, D), dtype=np.float32)
-    k = np.random.default_rng(ss[2]).standard_normal((B, Hkv, D), dtype=np.float32)
-    v = np.random.default_rng(ss[3]).standard_normal((B, Hkv, D), dtype=np.float32)
+    Tq = int(w.tokens)
+    if Tq < 1 or np.any(lens < Tq):
+        raise ValueError("every sequence must hold its new tokens")
+    shape = (lambda H: (B, H, D)) if Tq == 1 else (lambda H: (B, Tq, H, D))
+    q = np.random.default_rng(ss[1]).standard_normal((B, Tq, Hq, D), dtype=np.float32).reshape(shape(Hq))
+    k = np.random.default_rng(ss[2]).standard_normal((B, Tq, Hkv, D), dtype=np.float32).reshape(shape(Hkv))
+    v = np.random.default_rng(ss[3]).standard_normal((B, Tq, Hkv, D), dtype=np.float32).reshape(shape(Hkv))
+    positions = (lens - 1) if Tq == 1 else lens[:, None] - Tq + np.arange(Tq)[None, :]
     wq = 1 + 0.1 * np.random.default_rng(ss[4]).standard_normal(D, dtype=np.float32)
     wk = 1 + 0.1 * np.random.default_rng(ss[5]).standard_normal(D, dtype=np.float32)
     pool_elems = num_pages * Hkv * TILE
@@ -167,12 +182,12 @@ def make_inputs(w: Workload, device="cpu", spare_pages=None, kv_interleave=False
     return {
         "q": _bf16(q).to(device), "k": _bf16(k).to(device), "v": _bf16(v).to(device),
         "q_norm_w": _bf16(wq).to(device), "k_norm_w": _bf16(wk).to(device),
-        "positions": torch.from_numpy((lens - 1).astype(np.int32)).to(device),
+        "positions": torch.from_numpy(np.ascontiguousarray(positions, dtype=np.int32)).to(device),
         "seq_lens": torch.from_numpy(lens.astype(np.int32)).to(device),
         "block_table": torch.from_numpy(bt).to(device),
         "k_cache": k_cache, "v_cache": v_cache,
         "num_pages": num_pages, "page_stride": page_stride, "head_stride": head_stride,
-        "max_blocks": max_blocks, "total_tiles": T,
+        "max_blocks": max_blocks, "total_tiles": T, "tokens": Tq,
     }
 
 

@@ -42,6 +42,7 @@ from .schedule import (tiles_per_sequence, plan_dynamic, plan_static,
 from .attention import attend_full, attend_chunk, combine_lse
 from .step import (prologue, cache_slot, gather_kv, decode_attention,
                    split_attention)
+from . import multitoken   # several new tokens per sequence (R20)
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "e4m3_to_f64", "f64_to_e4m3",
@@ -50,5 +51,5 @@ __all__ = [
     "tiles_per_sequence", "plan_dynamic", "plan_static",
     "default_static_splits", "Plan", "attend_full", "attend_chunk",
     "combine_lse", "prologue", "cache_slot", "gather_kv", "decode_attention",
-    "split_attention",
+    "split_attention", "multitoken",
 ]

@@ -49,9 +49,10 @@ def poison_indices(inp, w, kind, spare_pages=True):
     """Pool indices (one pool) of every element the step must not read.
 
     Pages no sequence owns, the rows at or past L_b of each sequence's last
-    page, and the new token's own slot (the prologue must overwrite it before
-    attention reads it).
+    page, and the new tokens' own slots (the prologue must overwrite them
+    before attention reads them).
     """
+    Tq = int(getattr(w, "tokens", 1))
     bt = inp["block_table"].cpu().numpy()
     lens = [int(L) for L in w.seq_lens]
     Hkv, ps, hs = w.num_kv_heads, inp["page_stride"], inp["head_stride"]
@@ -64,11 +65,13 @@ def poison_indices(inp, w, kind, spare_pages=True):
     d = np.arange(128)
     for b, L in enumerate(lens):
         t = (L - 1) // PAGE_SIZE
-        rows = np.array(list(range(L - t * PAGE_SIZE, PAGE_SIZE)) + [(L - 1) % PAGE_SIZE])
-        page = int(bt[b, t])
-        for g in range(Hkv):
-            off = tile_offset(kind, w.kv_dtype, rows[:, None], d[None, :]).reshape(-1)
-            idx.append(page * ps + g * hs + off)
+        slots = [(t, r) for r in range(L - t * PAGE_SIZE, PAGE_SIZE)]
+        slots += [(pos // PAGE_SIZE, pos % PAGE_SIZE) for pos in range(L - Tq, L)]
+        for tile, r in slots:
+            page = int(bt[b, tile])
+            for g in range(Hkv):
+                off = tile_offset(kind, w.kv_dtype, np.array([[r]]), d[None, :]).reshape(-1)
+                idx.append(page * ps + g * hs + off)
     return np.concatenate(idx)
 
 
