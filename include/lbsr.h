@@ -100,6 +100,19 @@ typedef enum { LBSR_SCHED_DYNAMIC = 0, LBSR_SCHED_STATIC = 1 } lbsr_sched;
  * block_table[b * max_blocks_per_seq + t].
  */
 
+/*
+ * Multi-token decode ([A] "Two new HPC backends in the vLLM ecosystem": the
+ * model carries a speculative-decoding (MTP) layer, whose drafted tokens are
+ * verified by a step with several new tokens per sequence).  With
+ * tokens_per_seq = Tq, every array of new tokens gets a token axis after the
+ * batch axis -- q, q_out, out [batch][Tq][Hq][128], k, v [batch][Tq][Hkv][128],
+ * positions [batch][Tq], lse_out [batch][Tq][Hq] -- and seq_lens[b] counts all
+ * Tq of them.  New token j of sequence b sits at position L_b - Tq + j and
+ * attends rows [0, L_b - Tq + j]: the cached prefix and new tokens 0..j.
+ * The Tq * G queries of one KV head share each KV read.  Tq = 1 is the
+ * ordinary step and the layouts reduce to the ones written below.
+ */
+
 typedef struct {
   int32_t num_q_heads;        /* Hq >= 1, a multiple of Hkv */
   int32_t num_kv_heads;       /* Hkv >= 1; group G = Hq / Hkv must be <= 16 */
@@ -107,6 +120,9 @@ typedef struct {
   int32_t page_size;          /* must be 64 */
   int32_t kv_dtype;           /* lbsr_kv_dtype */
   int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
+  int32_t tokens_per_seq;     /* Tq: new tokens per sequence, >= 1 with G * Tq <= 16
+                                 (multi-token decode, see below); 1 = one-token step */
+  int32_t reserved;           /* must be 0 */
   int64_t num_pages;          /* pages in each pool, >= 1 */
   int64_t page_stride;        /* elements; multiple of 8192 */
   int64_t head_stride;        /* elements; multiple of 8192 */
@@ -230,7 +246,8 @@ lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq
 /*
  * Split attention + merge over the schedule in `workspace` (run lbsr_plan
  * first with the same shape, batch and cfg).  For sequence b, q head h and
- * KV head g = h / (Hq/Hkv), over the rows j < L_b:
+ * KV head g = h / (Hq/Hkv), over the rows j < L_b (with Tq > 1: new token t
+ * over the rows j <= L_b - Tq + t, and [b] below reads [b][t]):
  *   out[b][h] = sum_j softmax_j(sm_scale * <q_out[b][h], K_j>) V_j      (BF16)
  *   lse_out[b][h] = ln sum_j exp(sm_scale * <q_out[b][h], K_j>)        (fp32)
  * with K_j = code*k_scale and V_j = code*v_scale for an FP8 cache.  Each
@@ -253,8 +270,9 @@ lbsr_status lbsr_attention(const lbsr_shape *shape, const lbsr_params *params, i
  * the schedule and the prologue in one launch, then split attention and the
  * merge.  Same results as lbsr_plan, lbsr_rope_norm_kv_write and
  * lbsr_attention in turn; the prologue's error bits end up in the
- * workspace's error word.  Requires positions[b] = seq_lens[b] - 1 for the
- * new token to be part of its own attention.
+ * workspace's error word.  Requires positions[b] = seq_lens[b] - 1 (with
+ * Tq > 1: positions[b][t] = seq_lens[b] - Tq + t) for the new tokens to be
+ * part of the attention that follows.
  */
 lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
                              int32_t batch, const void *q, const void *k, const void *v,

@@ -54,6 +54,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("tokens_per_seq", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("num_pages", ctypes.c_int64), ("page_stride", ctypes.c_int64),
                 ("head_stride", ctypes.c_int64)]
 

@@ -92,6 +92,12 @@ lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
   if (s->num_q_heads / s->num_kv_heads > lbsr::kMaxGroup)
     return fail(LBSR_E_UNSUPPORTED, "group size %d > 16", s->num_q_heads / s->num_kv_heads);
   if (s->num_q_heads > 4096) return fail(LBSR_E_UNSUPPORTED, "Hq %d > 4096", s->num_q_heads);
+  if (s->tokens_per_seq < 1)
+    return fail(LBSR_E_INVALID, "tokens_per_seq %d < 1", s->tokens_per_seq);
+  if ((int64_t)s->tokens_per_seq * (s->num_q_heads / s->num_kv_heads) > lbsr::kMaxGroup)
+    return fail(LBSR_E_UNSUPPORTED, "tokens_per_seq %d x group %d > 16", s->tokens_per_seq,
+                s->num_q_heads / s->num_kv_heads);
+  if (s->reserved != 0) return fail(LBSR_E_INVALID, "shape.reserved must be 0");
   if (s->kv_dtype != LBSR_KV_BF16 && s->kv_dtype != LBSR_KV_FP8_E4M3)
     return fail(LBSR_E_INVALID, "kv_dtype %d unknown", s->kv_dtype);
   if (s->max_blocks_per_seq < 1)
@@ -177,6 +183,7 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
   }
   if (W > (1 << 22)) return fail(LBSR_E_UNSUPPORTED, "%lld workers is too many", (long long)W);
   const int64_t Hq = shape->num_q_heads;
+  const int64_t Tq = shape->tokens_per_seq;
   size_t off = 0;
   memset(out, 0, sizeof *out);
   out->error_word = off;   off = align256(off + 4);
@@ -185,9 +192,9 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
   out->chunks = off;       off = align256(off + 16 * (size_t)cmax);
   out->seq_chunk = off;    off = align256(off + 4 * (size_t)(batch + 1));
   out->seq_len_eff = off;  off = align256(off + 4 * (size_t)batch);
-  out->token_status = off; off = align256(off + 4 * (size_t)batch);
-  out->partial_o = off;    off = align256(off + 4 * (size_t)cmax * Hq * LBSR_HEAD_DIM);
-  out->partial_lse = off;  off = align256(off + 4 * (size_t)cmax * Hq);
+  out->token_status = off; off = align256(off + 4 * (size_t)batch * Tq);
+  out->partial_o = off;    off = align256(off + 4 * (size_t)cmax * Tq * Hq * LBSR_HEAD_DIM);
+  out->partial_lse = off;  off = align256(off + 4 * (size_t)cmax * Tq * Hq);
   out->total = off;
   out->num_workers = (int32_t)W;
   out->max_chunks = (int32_t)cmax;
@@ -217,7 +224,7 @@ lbsr::Geometry geometry(const lbsr_shape* s, int32_t batch) {
   g.num_kv_heads = s->num_kv_heads;
   g.group = s->num_q_heads / s->num_kv_heads;
   g.max_blocks = s->max_blocks_per_seq;
-  g.pad = 0;
+  g.tokens = s->tokens_per_seq;
   g.num_pages = s->num_pages;
   g.page_stride = s->page_stride;
   g.head_stride = s->head_stride;
@@ -286,8 +293,10 @@ lbsr_status run_prologue(const lbsr_shape* shape, const lbsr_params* params, int
                     "prologue launch");
 }
 
-lbsr::SchedParams sched_params(const lbsr_sched_cfg* cfg, const lbsr_ws_layout& l) {
+lbsr::SchedParams sched_params(const lbsr_shape* shape, const lbsr_sched_cfg* cfg,
+                               const lbsr_ws_layout& l) {
   lbsr::SchedParams sp{};
+  sp.min_len = shape->tokens_per_seq;
   sp.dynamic = cfg->sched == LBSR_SCHED_DYNAMIC;
   sp.num_workers = l.num_workers;
   sp.splits = l.static_splits;
@@ -299,7 +308,7 @@ lbsr::SchedParams sched_params(const lbsr_sched_cfg* cfg, const lbsr_ws_layout& 
 lbsr_status run_plan(const lbsr_shape* shape, int32_t batch, const int32_t* seq_lens,
                      const lbsr_sched_cfg* cfg, const lbsr_ws_layout& l, void* ws, hipStream_t stream) {
   return hip_status(lbsr::launch_plan(seq_lens, batch, shape->max_blocks_per_seq,
-                                      sched_params(cfg, l), plan_ptrs(ws, l), stream),
+                                      sched_params(shape, cfg, l), plan_ptrs(ws, l), stream),
                     "plan launch");
 }
 
@@ -312,7 +321,7 @@ lbsr_status run_plan_prologue(const lbsr_shape* shape, const lbsr_params* params
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
   return hip_status(
-      lbsr::launch_plan_prologue(seq_lens, sched_params(cfg, l), plan_ptrs(ws, l), geo, fp8, q,
+      lbsr::launch_plan_prologue(seq_lens, sched_params(shape, cfg, l), plan_ptrs(ws, l), geo, fp8, q,
                                  k, v, positions,
                                  wq, wk, bt, kc, vc, q_out, params->rope_theta,
                                  (double)params->rms_eps, params->norm_before_rope,

@@ -12,8 +12,11 @@
 // Mapping on CDNA4 (wave64, matrix cores):
 //   * workgroup = one worker of the schedule; wave = one KV head of it.
 //   * S^T[64 tokens][16 cols] = K[64][128] . Q^T[128][16] with
-//     v_mfma_f32_16x16x32_bf16 (the 8 q heads of the group fill 8 of the 16
-//     columns; the rest are zero): 4 token blocks x 4 channel steps.
+//     v_mfma_f32_16x16x32_bf16: column j*G + h is q head h of the group for
+//     new token j, so the 8 heads of the pages' model fill 8 of the 16
+//     columns in a one-token step and all 16 with two new tokens per
+//     sequence (multi-token decode) at no extra KV traffic; unused columns
+//     are zero.  4 token blocks x 4 channel steps.
 //   * O^T[128][16] += V^T[128][64] . P^T[64][16]: 8 channel blocks x 2 token
 //     steps.  The score accumulator's lane layout is reused as the P^T operand
 //     without moving data: the V page layout orders tokens to match it.
@@ -103,18 +106,20 @@ struct SoftmaxState {
   float lsum;   // this lane's share of the running sum
 };
 
-// One 64-token tile: scores, online softmax update, P.V.  When kPrefetch, the
+// One 64-token tile: scores, online softmax update, P.V.  `rem` = rows of the
+// tile before the sequence end (1..64); the lane's column attends rows below
+// rem - lag (lag = Tq - 1 - new-token index), and `tail` = Tq - 1 is the
+// largest lag.  When kPrefetch, the
 // next tile's K and V fragments are requested together once P.V has consumed
 // this tile's registers, so they stream while the tile that follows is waited
 // for and computed; with 8 waves per CU, every wave's arithmetic hides behind
 // the others' loads.  (Requesting K early, right after the scores, splits each
 // wave's 32 KiB request into two bursts and measured ~12% slower for BF16.)
-// `rem` = valid rows of this tile (1..64).
 template <bool kFp8, bool kPrefetch>
 __device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
-                                            const bf16x8 (&qB)[4], int rem, int kc, int lane,
-                                            float score_scale_log2, const u32x4* next_k,
-                                            const u32x4* next_v) {
+                                            const bf16x8 (&qB)[4], int rem, int lag, int tail,
+                                            int kc, int lane, float score_scale_log2,
+                                            const u32x4* next_k, const u32x4* next_v) {
   constexpr int NF = TileRegs<kFp8>::kFrags;
   // ---- scores: S^T[token][col], lane holds tokens 16*tb + 4*kc + e ----
   f32x4 S[4];
@@ -141,23 +146,28 @@ __device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[4 * tb + e] = S[tb][e] * score_scale_log2;
-  if (rem < kPage) {
+  if (rem - tail < kPage) {   // some column's last row falls in this tile
+    const int lim = rem - lag;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (16 * tb + 4 * kc + e >= rem) p[4 * tb + e] = -__builtin_inff();
+        if (16 * tb + 4 * kc + e >= lim) p[4 * tb + e] = -__builtin_inff();
   }
   float mx = p[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, p[i]);
   mx = max_xor32(max_xor16(mx));
   const float m_new = fmaxf(st.m, mx);
-  const float alpha = fast_exp2(st.m - m_new);
+  // With several new tokens a column can have no row yet (its limit lies
+  // before this chunk's rows so far): its max stays -inf, and 0 serves as
+  // the exponent base so that alpha and p come out 0 instead of NaN.
+  const float m_base = m_new == -__builtin_inff() ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_base);
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    p[i] = fast_exp2(p[i] - m_new);
+    p[i] = fast_exp2(p[i] - m_base);
     psum += p[i];
   }
   st.lsum = st.lsum * alpha + psum;
@@ -258,10 +268,14 @@ __device__ __forceinline__ void split_worker(
   if (c_begin >= c_end) return;
 
   const int lane = threadIdx.x & 63;
-  const int col = lane & 15;  // matrix column = q head inside the group
+  const int col = lane & 15;  // matrix column = (new token, q head inside the group)
   const int kc = lane >> 4;   // which 8-element slice of the contraction this lane feeds
   const int nwaves = blockDim.x >> 6;
-  const int Hq = geo.num_q_heads, G = geo.group;
+  const int Hq = geo.num_q_heads, G = geo.group, T = geo.tokens;
+  const int GT = G * T;                      // columns in use
+  const int tok = col < GT ? col / G : 0;    // this column's new token
+  const int hl = col - tok * G;              // and its head inside the group
+  const int lag = T - 1 - tok;               // it attends rows < L - lag
 
   for (int g = threadIdx.x >> 6; g < geo.num_kv_heads; g += nwaves) {
     for (int c = c_begin; c < c_end; ++c) {
@@ -273,12 +287,13 @@ __device__ __forceinline__ void split_worker(
       const bool single = wave_uniform(plan.seq_chunk[b + 1] - plan.seq_chunk[b]) == 1;
       const int32_t* bt_row = block_table + (size_t)b * geo.max_blocks;
 
-      // Q^T operand: column col = q head g*G + col (zero past the group), channels
-      // 32*s + 8*kc .. +8 for contraction step s.
+      // Q^T operand: column col = q head g*G + hl of new token tok (zero past
+      // the G*Tq columns in use), channels 32*s + 8*kc .. +8 for step s.
       bf16x8 qB[4];
-      if (col < G) {
+      if (col < GT) {
         const u32x4* qp =
-            (const u32x4*)(q_out + ((size_t)b * Hq + (size_t)g * G + col) * kHeadDim) + kc;
+            (const u32x4*)(q_out + (((size_t)b * T + tok) * Hq + (size_t)g * G + hl) * kHeadDim) +
+            kc;
 #pragma unroll
         for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(qp[4 * s]);
       } else {
@@ -306,24 +321,28 @@ __device__ __forceinline__ void split_worker(
       // so the loop body has no conditional loads
       for (int t = t0; t < t1 - 1; ++t) {
         const int next = fetch_page(bt_row, t + 1, geo.num_pages, bad_page);
-        attend_tile<kFp8, true>(R, st, qB, L - t * kPage, kc, lane, score_scale_log2,
-                                tile_ptr(k_pool, next), tile_ptr(v_pool, next));
+        attend_tile<kFp8, true>(R, st, qB, L - t * kPage, lag, T - 1, kc, lane,
+                                score_scale_log2, tile_ptr(k_pool, next), tile_ptr(v_pool, next));
       }
-      attend_tile<kFp8, false>(R, st, qB, L - (t1 - 1) * kPage, kc, lane, score_scale_log2,
-                               nullptr, nullptr);
+      attend_tile<kFp8, false>(R, st, qB, L - (t1 - 1) * kPage, lag, T - 1, kc, lane,
+                               score_scale_log2, nullptr, nullptr);
       if (bad_page && lane == 0) atomicOr(plan.error_word, (int32_t)kErrPage);
       const float m = st.m;
       const float lsum = st.lsum;
       const f32x4* O = st.O;
 
       // ---- finish the chunk ----
+      // l = 0: no row of this chunk is visible to the column (an early new
+      // token whose limit lies before the chunk): an empty partial, o = 0 and
+      // lse = -inf, which the merge weighs 0.  A sequence's first chunk
+      // holds row 0, so a single-chunk sequence never gets here with l = 0.
       const float l = sum_xor32(sum_xor16(lsum));
-      const float scale = out_scale / l;
-      const float lse2 = m + __builtin_amdgcn_logf(l);  // log2
-      if (col < G) {
-        const int h = g * G + col;
+      const float scale = l > 0.f ? out_scale / l : 0.f;
+      const float lse2 = l > 0.f ? m + __builtin_amdgcn_logf(l) : -__builtin_inff();  // log2
+      if (col < GT) {
+        const size_t orow = ((size_t)b * T + tok) * Hq + (size_t)g * G + hl;  // out / lse_out row
         if (single) {
-          uint16_t* o = out + ((size_t)b * Hq + h) * kHeadDim + 4 * kc;
+          uint16_t* o = out + orow * kHeadDim + 4 * kc;
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             bf16x4 v4;
@@ -331,17 +350,18 @@ __device__ __forceinline__ void split_worker(
             for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(O[db][e] * scale);
             *(bf16x4*)(o + 16 * db) = v4;
           }
-          if (kc == 0 && lse_out) lse_out[(size_t)b * Hq + h] = lse2 * kLn2;
+          if (kc == 0 && lse_out) lse_out[orow] = lse2 * kLn2;
         } else {
           // partial row layout of (chunk c, KV group g): [16 slices of 8
-          // channels][G heads][8 channels], so that any run of slices is
-          // contiguous for the merge
-          float* po = plan.partial_o + ((size_t)c * Hq + (size_t)g * G) * kHeadDim +
+          // channels][G*Tq columns][8 channels], so that any run of slices is
+          // contiguous for the merge; chunk c's rows are Hq*Tq long
+          const size_t HqT = (size_t)Hq * T;
+          float* po = plan.partial_o + ((size_t)c * HqT + (size_t)g * GT) * kHeadDim +
                       col * 8 + 4 * (kc & 1);
 #pragma unroll
           for (int db = 0; db < 8; ++db)
-            *(f32x4*)(po + (2 * db + (kc >> 1)) * 8 * G) = O[db] * scale;
-          if (kc == 0) plan.partial_lse[(size_t)c * Hq + h] = lse2;
+            *(f32x4*)(po + (2 * db + (kc >> 1)) * 8 * GT) = O[db] * scale;
+          if (kc == 0) plan.partial_lse[(size_t)c * HqT + (size_t)g * GT + col] = lse2;
         }
       }
     }
@@ -417,14 +437,22 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
                                                                     int fold_token_status) {
   constexpr int kThreads = kMergeWaves * kWave;
   const int slice = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  if (fold_token_status && slice == 0 && g == 0 && threadIdx.x == 0) {
-    const int32_t st = plan.token_status[b];
+  const int T = geo.tokens, G0 = geo.group;
+  if (fold_token_status && slice == 0 && g == 0 && threadIdx.x < T) {
+    const int32_t st = plan.token_status[(size_t)b * T + threadIdx.x];
     if (st) atomicOr(plan.error_word, st);
   }
   const int c0 = plan.seq_chunk[b], c1 = plan.seq_chunk[b + 1];
   const int count = c1 - c0;
   if (count <= 1) return;  // written directly by the split kernel
-  const int Hq = geo.num_q_heads, G = geo.group;
+  // A chunk row holds, per KV group, G = G0 * Tq columns (new token j, head
+  // h of the group at column j*G0 + h); partial rows are Hq = Hq0 * Tq long.
+  const int Hq = geo.num_q_heads * T, G = G0 * T;
+  // out / lse_out row of column v of this group
+  auto out_row = [&](int v) {
+    const int j = v / G0;
+    return ((size_t)b * T + j) * geo.num_q_heads + (size_t)g * G0 + (v - j * G0);
+  };
   // Slices for this sequence: the fewest (from min_slices) whose rows all fit
   // in one round of reads, at most gridDim.x; surplus workgroups leave.
   int nslices = min_slices;
@@ -493,7 +521,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
     const float inv = 1.0f / sum;
     for (int i = sub; i < count; i += 16) s_w[i * G + h2] = fast_exp2(s_w[i * G + h2] - mx) * inv;
     if (sub == 0 && slice == 0 && lse_out)
-      lse_out[(size_t)b * Hq + head0 + h2] = (mx + __builtin_amdgcn_logf(sum)) * kLn2;
+      lse_out[out_row(h2)] = (mx + __builtin_amdgcn_logf(sum)) * kLn2;
   }
   __syncthreads();
 
@@ -521,7 +549,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
     bf16x4 rr;
 #pragma unroll
     for (int x = 0; x < 4; ++x) rr[x] = (__bf16)sum[x];
-    *(bf16x4*)(out + ((size_t)b * Hq + head0 + h3) * kHeadDim + d) = rr;
+    *(bf16x4*)(out + out_row(h3) * kHeadDim + d) = rr;
   }
 }
 
@@ -545,12 +573,14 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
 
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
                           int max_chunks_per_seq, bool fold_token_status, hipStream_t stream) {
-  // S slices: a power of two dividing 32 with 32G/S <= 64 float4 per row slice
+  // S slices: a power of two dividing 32 with 32G/S <= 64 float4 per row
+  // slice, G = group * Tq columns per (chunk, KV group)
+  const int cols = geo.group * geo.tokens;
   int slices = LBSR_MERGE_MIN_SLICES;
-  while (slices < 32 && 32 * geo.group / slices > kWave) slices *= 2;
+  while (slices < 32 && 32 * cols / slices > kWave) slices *= 2;
   const int max_slices = slices > LBSR_MERGE_MAX_SLICES ? slices : LBSR_MERGE_MAX_SLICES;
   dim3 grid(max_slices, geo.num_kv_heads, geo.batch);
-  const size_t lds = (size_t)max_chunks_per_seq * geo.group * sizeof(float);
+  const size_t lds = (size_t)max_chunks_per_seq * cols * sizeof(float);
   merge_kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, (uint16_t*)out, lse_out,
                                                            slices, fold_token_status ? 1 : 0);
   return hipGetLastError();

@@ -29,6 +29,7 @@ __host__ __device__ inline int xcd_run_size(int x, int num_workers) {
 
 // The schedule's parameters, passed by value.
 struct SchedParams {
+  int32_t min_len;       // shorter lengths are clamped up and flagged (a sequence holds its new tokens)
   int32_t dynamic;       // 1: length-proportional, 0: static split
   int32_t num_workers;   // P (dynamic)
   int32_t splits;        // S (static)
@@ -64,7 +65,7 @@ struct Geometry {
   int32_t num_kv_heads;
   int32_t group;          // Hq / Hkv
   int32_t max_blocks;     // block_table row stride
-  int32_t pad;
+  int32_t tokens;         // new tokens per sequence (Tq); group * tokens <= kMaxGroup
   int64_t num_pages;
   int64_t page_stride;    // elements
   int64_t head_stride;    // elements

@@ -100,7 +100,7 @@ __device__ inline void plan_body(const int32_t* __restrict__ seq_lens, int batch
     int n = 0;
     if (b < batch) {
       const int L = seq_lens[b];
-      const int Lc = L < 1 ? 1 : (L > max_len ? max_len : L);
+      const int Lc = L < sp.min_len ? sp.min_len : (L > max_len ? max_len : L);
       bad |= (Lc != L);
       plan.seq_len_eff[b] = Lc;
       n = (Lc + kPage - 1) / kPage;

@@ -84,14 +84,15 @@ __device__ inline double wave_sum_f64(double x) {
   return x;
 }
 
-// Row `row` of token b: rows [0, Hq) are q heads, [Hq, Hq+Hkv) k heads, then
-// v heads.  Called by a whole wave.  A k/v row whose position or page is out
-// of range skips its cache write and reports LBSR_DEV_ERR_* bits: OR-ed into
-// `error_word` if given, and/or stored (0 when fine) to `token_status[b]` if
-// given -- every k/v row of a token stores the same value.
+// Row `row` of new token `tok` (tok = b * Tq + j for new token j of sequence
+// b = seq): rows [0, Hq) are q heads, [Hq, Hq+Hkv) k heads, then v heads.
+// Called by a whole wave.  A k/v row whose position or page is out of range
+// skips its cache write and reports LBSR_DEV_ERR_* bits: OR-ed into
+// `error_word` if given, and/or stored (0 when fine) to `token_status[tok]`
+// if given -- every k/v row of a token stores the same value.
 template <bool kFp8>
 __device__ inline void prologue_row(
-    int b, int row, const Geometry& geo, const uint16_t* __restrict__ q,
+    int tok, int seq, int row, const Geometry& geo, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ positions, const uint16_t* __restrict__ wq,
     const uint16_t* __restrict__ wk, const int32_t* __restrict__ block_table,
@@ -101,7 +102,7 @@ __device__ inline void prologue_row(
 #pragma clang fp contract(off)
   const int Hq = geo.num_q_heads, Hkv = geo.num_kv_heads;
   const int lane = threadIdx.x & 63;
-  const int pos = positions[b];
+  const int pos = positions[tok];
 
   const uint16_t* src;
   const uint16_t* w = nullptr;
@@ -109,17 +110,17 @@ __device__ inline void prologue_row(
   int g = 0;
   if (row < Hq) {
     kind = 0;
-    src = q + ((size_t)b * Hq + row) * kHeadDim;
+    src = q + ((size_t)tok * Hq + row) * kHeadDim;
     w = wq;
   } else if (row < Hq + Hkv) {
     kind = 1;
     g = row - Hq;
-    src = k + ((size_t)b * Hkv + g) * kHeadDim;
+    src = k + ((size_t)tok * Hkv + g) * kHeadDim;
     w = wk;
   } else {
     kind = 2;
     g = row - Hq - Hkv;
-    src = v + ((size_t)b * Hkv + g) * kHeadDim;
+    src = v + ((size_t)tok * Hkv + g) * kHeadDim;
   }
   const uint16_t raw0 = src[lane], raw1 = src[lane + 64];
   double y0 = bf16_to_f64(raw0), y1 = bf16_to_f64(raw1);
@@ -147,7 +148,7 @@ __device__ inline void prologue_row(
   }
 
   if (kind == 0) {
-    uint16_t* dst = q_out + ((size_t)b * Hq + row) * kHeadDim;
+    uint16_t* dst = q_out + ((size_t)tok * Hq + row) * kHeadDim;
     dst[lane] = f64_to_bf16_rne(y0);
     dst[lane + 64] = f64_to_bf16_rne(y1);
     return;
@@ -159,11 +160,11 @@ __device__ inline void prologue_row(
   if (pos < 0 || pos >= geo.max_blocks * kPage) {
     flags = kErrPosition;
   } else {
-    page = block_table[(size_t)b * geo.max_blocks + (pos >> 6)];
+    page = block_table[(size_t)seq * geo.max_blocks + (pos >> 6)];
     if (page < 0 || page >= geo.num_pages) flags = kErrPage;
   }
   if (lane == 0) {
-    if (token_status) token_status[b] = flags;
+    if (token_status) token_status[tok] = flags;
     if (error_word && flags) atomicOr(error_word, flags);
   }
   if (flags) return;

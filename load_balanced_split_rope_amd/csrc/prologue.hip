@@ -1,7 +1,8 @@
 // The fused prologue as its own kernel (lbsr_rope_norm_kv_write).  The row
 // code is in prologue.h.
 //
-// Launch: grid (ceil(rows / 4), batch), 256 threads; rows = Hq + 2 * Hkv.
+// Launch: ceil(tokens * rows / 4) blocks of 256 threads, one wave per row;
+// rows = Hq + 2 * Hkv, tokens = batch * Tq.
 
 #include "launch.h"
 #include "prologue.h"
@@ -16,11 +17,13 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     const int32_t* __restrict__ block_table, void* __restrict__ k_cache,
     void* __restrict__ v_cache, uint16_t* __restrict__ q_out, int32_t* __restrict__ error_word,
     double theta, double eps, int norm_first, double k_scale, double v_scale) {
-  const int b = blockIdx.y;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= geo.num_q_heads + 2 * geo.num_kv_heads) return;
-  prologue_row<kFp8>(b, row, geo, q, k, v, positions, wq, wk, block_table, k_cache, v_cache,
-                     q_out, error_word, nullptr, theta, eps, norm_first, k_scale, v_scale);
+  const int rows = geo.num_q_heads + 2 * geo.num_kv_heads;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= geo.batch * geo.tokens * rows) return;
+  const int tok = r / rows;
+  prologue_row<kFp8>(tok, tok / geo.tokens, r - tok * rows, geo, q, k, v, positions, wq, wk,
+                     block_table, k_cache, v_cache, q_out, error_word, nullptr, theta, eps,
+                     norm_first, k_scale, v_scale);
 }
 
 hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const void* k,
@@ -30,7 +33,7 @@ hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const v
                            double eps, int norm_first, double k_scale, double v_scale,
                            hipStream_t stream) {
   const int rows = geo.num_q_heads + 2 * geo.num_kv_heads;
-  dim3 grid((rows + 3) / 4, geo.batch);
+  const int grid = (geo.batch * geo.tokens * rows + 3) / 4;
   if (fp8) {
     prologue_kernel<true><<<grid, 256, 0, stream>>>(
         geo, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, positions,

@@ -3,7 +3,7 @@
 // block 0 computes the schedule while the other blocks run the prologue rows,
 // saving a launch and letting the two overlap.
 //
-// Launch: 1 + ceil(batch * rows / 16) blocks of 1024 threads, rows = Hq + 2 Hkv;
+// Launch: 1 + ceil(batch * Tq * rows / 16) blocks of 1024 threads, rows = Hq + 2 Hkv;
 // dynamic LDS of batch + 1 ints (the schedule's prefix sums).
 
 #include "launch.h"
@@ -27,13 +27,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prologue_kernel(
   }
   const int rows = geo.num_q_heads + 2 * geo.num_kv_heads;
   const int r = (blockIdx.x - 1) * (kPlanThreads / kWave) + (threadIdx.x >> 6);
-  if (r >= geo.batch * rows) return;
+  if (r >= geo.batch * geo.tokens * rows) return;
+  const int tok = r / rows;
   // Block 0 clears the error word concurrently, so the prologue rows do not
   // touch it: each token's status is stored (overwritten every step) and the
   // merge kernel, which runs after both, folds it into the error word.
-  prologue_row<kFp8>(r / rows, r % rows, geo, q, k, v, positions, wq, wk, block_table, k_cache,
-                     v_cache, q_out, nullptr, plan.token_status, theta, eps, norm_first, k_scale,
-                     v_scale);
+  prologue_row<kFp8>(tok, tok / geo.tokens, r - tok * rows, geo, q, k, v, positions, wq, wk,
+                     block_table, k_cache, v_cache, q_out, nullptr, plan.token_status, theta,
+                     eps, norm_first, k_scale, v_scale);
 }
 
 hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
@@ -44,7 +45,8 @@ hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 void* q_out, double theta, double eps, int norm_first,
                                 double k_scale, double v_scale, hipStream_t stream) {
   const int rows = geo.num_q_heads + 2 * geo.num_kv_heads;
-  const int blocks = 1 + (geo.batch * rows + kPlanThreads / kWave - 1) / (kPlanThreads / kWave);
+  const int blocks =
+      1 + (geo.batch * geo.tokens * rows + kPlanThreads / kWave - 1) / (kPlanThreads / kWave);
   const size_t lds = sizeof(int) * (size_t)(geo.batch + 1);
   auto* qq = (const uint16_t*)q;
   auto* kk = (const uint16_t*)k;

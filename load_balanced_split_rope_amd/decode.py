@@ -29,13 +29,19 @@ class DecodeConfig:
     k_scale: float = 1.0
     v_scale: float = 1.0
     sm_scale: float = 0.0         # 0 -> 1/sqrt(128)
+    tokens_per_seq: int = 1       # new tokens per sequence (multi-token decode)
 
     def shape(self):
         return B.Shape(self.num_q_heads, self.num_kv_heads, B.HEAD_DIM, B.PAGE_SIZE,
                        B.KV_BF16 if self.kv_dtype == "bf16" else B.KV_FP8_E4M3,
-                       self.max_blocks_per_seq, self.num_pages,
+                       self.max_blocks_per_seq, self.tokens_per_seq, 0, self.num_pages,
                        self.page_stride or self.num_kv_heads * B.TILE_ELEMS,
                        self.head_stride or B.TILE_ELEMS)
+
+    def tokens_shape(self, batch, *rest):
+        """Shape of a per-new-token array: (batch, *rest), or (batch, Tq, *rest) when Tq > 1."""
+        Tq = self.tokens_per_seq
+        return (batch,) + rest if Tq == 1 else (batch, Tq) + rest
 
     def params(self):
         return B.Params(self.rope_theta, self.rms_eps, int(self.norm_before_rope),
@@ -127,11 +133,11 @@ def rope_norm_kv_write(cfg: DecodeConfig, q, k, v, positions, q_norm_w, k_norm_w
     """lbsr_rope_norm_kv_write: RoPE + QK-Norm + cache write of the new tokens."""
     batch = q.shape[0]
     Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, B.HEAD_DIM
-    _need(q, "q", torch.bfloat16, shape=(batch, Hq, D))
-    _need(k, "k", torch.bfloat16, shape=(batch, Hkv, D))
-    _need(v, "v", torch.bfloat16, shape=(batch, Hkv, D))
-    _need(q_out, "q_out", torch.bfloat16, shape=(batch, Hq, D))
-    _need(positions, "positions", torch.int32, shape=(batch,))
+    _need(q, "q", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(k, "k", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
+    _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(positions, "positions", torch.int32, shape=cfg.tokens_shape(batch))
     _need(q_norm_w, "q_norm_w", torch.bfloat16, shape=(D,))
     _need(k_norm_w, "k_norm_w", torch.bfloat16, shape=(D,))
     _check_table(cfg, block_table, batch)
@@ -160,10 +166,10 @@ def attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, sched: Sc
     """lbsr_attention: split attention + merge over the planned schedule."""
     batch = q_out.shape[0]
     Hq, D = cfg.num_q_heads, B.HEAD_DIM
-    _need(q_out, "q_out", torch.bfloat16, shape=(batch, Hq, D))
-    _need(out, "out", torch.bfloat16, shape=(batch, Hq, D))
+    _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(out, "out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
     if lse_out is not None:
-        _need(lse_out, "lse_out", torch.float32, shape=(batch, Hq))
+        _need(lse_out, "lse_out", torch.float32, shape=cfg.tokens_shape(batch, Hq))
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
     _need(workspace, "workspace", torch.uint8)
@@ -178,17 +184,17 @@ def _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_tabl
                v_cache, q_out, sched, workspace, out, lse_out):
     batch = q.shape[0]
     Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, B.HEAD_DIM
-    _need(q, "q", torch.bfloat16, shape=(batch, Hq, D))
-    _need(k, "k", torch.bfloat16, shape=(batch, Hkv, D))
-    _need(v, "v", torch.bfloat16, shape=(batch, Hkv, D))
-    _need(q_out, "q_out", torch.bfloat16, shape=(batch, Hq, D))
-    _need(out, "out", torch.bfloat16, shape=(batch, Hq, D))
-    _need(positions, "positions", torch.int32, shape=(batch,))
+    _need(q, "q", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(k, "k", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
+    _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(out, "out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(positions, "positions", torch.int32, shape=cfg.tokens_shape(batch))
     _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
     _need(q_norm_w, "q_norm_w", torch.bfloat16, shape=(D,))
     _need(k_norm_w, "k_norm_w", torch.bfloat16, shape=(D,))
     if lse_out is not None:
-        _need(lse_out, "lse_out", torch.float32, shape=(batch, Hq))
+        _need(lse_out, "lse_out", torch.float32, shape=cfg.tokens_shape(batch, Hq))
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
     _need(workspace, "workspace", torch.uint8)

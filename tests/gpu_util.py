@@ -23,7 +23,8 @@ def config_for(w, inp):
                            inp["num_pages"], page_stride=inp["page_stride"],
                            head_stride=inp["head_stride"], rope_theta=w.rope_theta,
                            rms_eps=w.rms_eps, norm_before_rope=w.norm_before_rope,
-                           k_scale=w.k_scale, v_scale=w.v_scale)
+                           k_scale=w.k_scale, v_scale=w.v_scale,
+                           tokens_per_seq=getattr(w, "tokens", 1))
 
 
 def run_step(w, g, sched, lse=True, cfg=None):
@@ -34,7 +35,8 @@ def run_step(w, g, sched, lse=True, cfg=None):
     ws = lb.alloc_workspace(cfg, w.batch, sched, device=dev)
     q_out = torch.empty_like(g["q"])
     out = torch.empty_like(g["q"])
-    lse_t = torch.empty(w.batch, w.num_q_heads, dtype=torch.float32, device=dev) if lse else None
+    lse_t = (torch.empty(cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+             if lse else None)
     lb.decode_step(cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"], g["q_norm_w"],
                    g["k_norm_w"], g["block_table"], g["k_cache"], g["v_cache"], q_out, sched, ws,
                    out, lse_t)

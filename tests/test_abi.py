@@ -172,3 +172,43 @@ def test_binding_signatures_match_header(lib):
         assert len(getattr(lib, name).argtypes) == n, name
         seen += 1
     assert seen == len(B.EXPORTS)
+
+
+def test_shape_struct_matches_header():
+    """lbsr_shape: 8 int32 fields (tokens_per_seq and reserved after
+    max_blocks_per_seq), then the three int64: 56 bytes."""
+    assert ctypes.sizeof(B.Shape) == 56
+    assert B.Shape.tokens_per_seq.offset == 24 and B.Shape.num_pages.offset == 32
+
+
+@pytest.mark.parametrize("Hq,Hkv,tokens,reserved,status", [
+    (64, 8, 1, 0, B.OK), (64, 8, 2, 0, B.OK), (16, 4, 4, 0, B.OK), (8, 8, 16, 0, B.OK),
+    (64, 8, 0, 0, B.E_INVALID), (64, 8, -1, 0, B.E_INVALID),
+    (64, 8, 3, 0, B.E_UNSUPPORTED),          # 8 heads x 3 tokens > 16 columns
+    (8, 8, 17, 0, B.E_UNSUPPORTED),
+    (64, 8, 1, 5, B.E_INVALID),
+])
+def test_tokens_per_seq_validation(lib, Hq, Hkv, tokens, reserved, status):
+    s = DecodeConfig(Hq, Hkv, "bf16", 2048, 4300, tokens_per_seq=tokens).shape()
+    s.reserved = reserved
+    c = Schedule("dynamic", num_workers=256).cfg()
+    out = B.WsLayout()
+    got = lib.lbsr_workspace_layout(ctypes.byref(s), 32, ctypes.byref(c), ctypes.byref(out))
+    assert got == status, lib.lbsr_last_error()
+
+
+def test_workspace_grows_with_tokens(lib):
+    """Partials, their lse and the per-token status scale with the new tokens."""
+    c = Schedule("dynamic", num_workers=256).cfg()
+    lays = []
+    for tokens in (1, 2):
+        s = DecodeConfig(64, 8, "bf16", 2048, 4300, tokens_per_seq=tokens).shape()
+        out = B.WsLayout()
+        assert lib.lbsr_workspace_layout(ctypes.byref(s), 32, ctypes.byref(c),
+                                         ctypes.byref(out)) == B.OK
+        lays.append(out)
+    one, two = lays
+    cmax = one.max_chunks
+    assert two.partial_lse - two.partial_o >= 2 * cmax * 64 * 128 * 4
+    assert two.total - two.partial_lse >= 2 * cmax * 64 * 4
+    assert two.total > one.total

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import multitoken as mt
 import load_balanced_split_rope_amd as lb
 from load_balanced_split_rope_amd import workloads as wl
 from checks import (poison_cache, host_step_inputs, oracle_cfg, check_output, to_f64, bits_u16)
@@ -15,7 +16,7 @@ from gpu_util import device, run_step, compact_pools, remap_slots
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-FULL = ["uniform", "mix", "mix_fp8", "loguniform"]
+FULL = ["uniform", "mix", "mix_fp8", "loguniform", "mix_mtp2"]
 
 
 def sampled_checks(w, g, res, h, pro):
@@ -27,13 +28,20 @@ def sampled_checks(w, g, res, h, pro):
     kp, vp, bt, pmap = compact_pools(g, w, seqs)
     cfg = oracle_cfg(g, w)
     pro_c = remap_slots(pro, pmap)
-    ref = oracle.decode_attention(pro["q_out"], (kp, vp), pro_c, h["seq_lens"], bt, cfg,
-                                  seqs=seqs, heads=heads)
     out = to_f64(res["out"])
     lse = to_f64(res["lse"])
-    for (b, hh), (o, l) in ref.items():
-        check_output(out[b, hh], o, w.kv_dtype, f"output seq {b} head {hh}")
-        assert abs(lse[b, hh] - l) <= 1e-4 + 1e-5 * abs(l), (b, hh, lse[b, hh], l)
+    if w.tokens == 1:
+        ref = oracle.decode_attention(pro["q_out"], (kp, vp), pro_c, h["seq_lens"], bt, cfg,
+                                      seqs=seqs, heads=heads)
+        ref = {(b, 0, hh): v for (b, hh), v in ref.items()}
+        out, lse = out[:, None], lse[:, None]
+    else:
+        q_out = pro["q_out"].reshape(w.batch, w.tokens, w.num_q_heads, 128)
+        ref = mt.decode_attention_tokens(q_out, (kp, vp), pro_c, h["seq_lens"], bt, cfg,
+                                         seqs=seqs, heads=heads)
+    for (b, j, hh), (o, l) in ref.items():
+        check_output(out[b, j, hh], o, w.kv_dtype, f"output seq {b} token {j} head {hh}")
+        assert abs(lse[b, j, hh] - l) <= 1e-4 + 1e-5 * abs(l), (b, j, hh, lse[b, j, hh], l)
     return len(ref)
 
 
@@ -45,9 +53,14 @@ def test_full_workload(name):
     g = wl.make_inputs(w, device=dev)
     poison_cache(g, w, spare_pages=False)
     h = host_step_inputs(g)
-    pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
-                          h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
-                          kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    kw = dict(theta=w.rope_theta, eps=w.rms_eps, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
+              v_scale=w.v_scale)
+    if w.tokens == 1:
+        pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                              h["block_table"], **kw)
+    else:
+        pro = mt.prologue_tokens(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                                 h["block_table"], **kw)
     P = lb.device_workers(0)
     for sched in (lb.Schedule("dynamic"), lb.Schedule("static"),
                   lb.Schedule("dynamic", xcd_weights=(9, 10, 9, 10, 9, 10, 9, 10))):
@@ -62,24 +75,29 @@ def test_full_workload(name):
         got = res["plan"]
         for key in ("cu_tiles", "worker_chunk", "chunks", "seq_chunk"):
             assert np.array_equal(got[key], getattr(ref_plan, key)), key
-        assert np.array_equal(bits_u16(res["q_out"]), pro["q_out"]) or \
-            np.mean(bits_u16(res["q_out"]) != pro["q_out"]) < 1e-6
+        got_q = bits_u16(res["q_out"]).reshape(pro["q_out"].shape)
+        assert np.array_equal(got_q, pro["q_out"]) or np.mean(got_q != pro["q_out"]) < 1e-6
         n = sampled_checks(w, gg, res, h, pro)
         print(f"  {sched}: plan exact, {n} sampled heads match", flush=True)
         del gg, res
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["mix", "mix_fp8", "loguniform"])
+@pytest.mark.parametrize("name", ["mix", "mix_fp8", "loguniform", "mix_mtp2"])
 def test_full_zero_query_lse(name):
-    """Every (sequence, head) at full size: with q = 0 the lse is ln L."""
+    """Every (sequence, head) at full size: with q = 0 the lse is ln of the
+    number of rows attended (L, or L - Tq + j + 1 for new token j)."""
     dev = device()
     w = wl.named(name)
     g = wl.make_inputs(w, device=dev)
     g["q_norm_w"].zero_()
     res = run_step(w, g, lb.Schedule("dynamic"))
     lse = to_f64(res["lse"])
-    want = np.log(np.asarray(w.seq_lens, dtype=np.float64))[:, None]
+    lens = np.asarray(w.seq_lens, dtype=np.float64)
+    if w.tokens == 1:
+        want = np.log(lens)[:, None]
+    else:
+        want = np.log(lens[:, None] - w.tokens + np.arange(w.tokens)[None, :] + 1)[:, :, None]
     err = np.abs(lse - want)
     print(f"{name}: max |lse - ln L| = {err.max():.2e}", flush=True)
     assert np.all(err <= 16 * np.finfo(np.float32).eps * np.maximum(want, 1))

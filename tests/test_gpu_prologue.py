@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import multitoken as mt
 import load_balanced_split_rope_amd as lb
 from load_balanced_split_rope_amd import workloads as wl
 from checks import host_pools, host_step_inputs, bits_u16, poison_cache
@@ -48,6 +49,10 @@ CASES = [
     ("custom", dict(seq_lens=[77, 5000], num_q_heads=32, num_kv_heads=4, norm_before_rope=True)),
     ("custom", dict(seq_lens=[300, 1, 64], num_q_heads=8, num_kv_heads=2, kv_dtype="fp8",
                     k_scale=0.0371, v_scale=0.0113)),
+    # several new tokens per sequence, some pairs straddling a page boundary
+    ("custom", dict(seq_lens=[2, 64, 65, 130, 4096], num_q_heads=64, num_kv_heads=8, tokens=2)),
+    ("custom", dict(seq_lens=[4, 66, 1000, 129], num_q_heads=16, num_kv_heads=4, kv_dtype="fp8",
+                    tokens=4)),
 ]
 
 
@@ -61,16 +66,20 @@ def test_prologue_matches_oracle(case):
     before_k, before_v = host_pools(inp, w)
     h = host_step_inputs(inp)
     print(f"prologue case {case}: lens {w.seq_lens} {w.num_q_heads}q/{w.num_kv_heads}kv "
-          f"{w.kv_dtype}", flush=True)
+          f"{w.kv_dtype} tokens {w.tokens}", flush=True)
     g, q_out = run_prologue(w, inp, dev)
 
-    pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
-                          h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
-                          kv_dtype=w.kv_dtype, k_scale=np.float32(w.k_scale).item(),
-                          v_scale=np.float32(w.v_scale).item(),
-                          norm_before_rope=w.norm_before_rope)
-    # q_out: the fp64 result's BF16 rounding, except at near-ties
-    got_q = bits_u16(q_out)
+    kw = dict(theta=w.rope_theta, eps=w.rms_eps, kv_dtype=w.kv_dtype,
+              k_scale=np.float32(w.k_scale).item(), v_scale=np.float32(w.v_scale).item(),
+              norm_before_rope=w.norm_before_rope)
+    if w.tokens == 1:
+        pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                              h["block_table"], **kw)
+    else:
+        pro = mt.prologue_tokens(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                                 h["block_table"], **kw)
+    # q_out: the fp64 result's BF16 rounding, except at near-ties (token-major flat)
+    got_q = bits_u16(q_out).reshape(pro["q_out"].shape)
     diff = got_q != pro["q_out"]
     assert not np.any(diff & ~near_tie(pro["q_f64"], "bf16")), int(diff.sum())
 

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import multitoken as mt
 import load_balanced_split_rope_amd as lb
 from load_balanced_split_rope_amd import workloads as wl
 from checks import (poison_cache, host_pools, host_step_inputs, oracle_cfg, check_output,
@@ -18,20 +19,32 @@ pytestmark = pytest.mark.gpu
 
 
 def oracle_step(w, inp):
+    """The oracle's step; outputs [B, Hq, D] / [B, Hq], or [B, Tq, Hq, D] /
+    [B, Tq, Hq] with several new tokens per sequence."""
     h = host_step_inputs(inp)
     pools = host_pools(inp, w)
-    pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
-                          h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
-                          kv_dtype=w.kv_dtype, k_scale=np.float32(w.k_scale).item(),
-                          v_scale=np.float32(w.v_scale).item(),
-                          norm_before_rope=w.norm_before_rope)
+    kw = dict(theta=w.rope_theta, eps=w.rms_eps, kv_dtype=w.kv_dtype,
+              k_scale=np.float32(w.k_scale).item(), v_scale=np.float32(w.v_scale).item(),
+              norm_before_rope=w.norm_before_rope)
     cfg = oracle_cfg(inp, w)
     cfg["k_scale"] = np.float32(w.k_scale).item()
     cfg["v_scale"] = np.float32(w.v_scale).item()
-    ref = oracle.decode_attention(pro["q_out"], pools, pro, h["seq_lens"], h["block_table"], cfg)
-    B, Hq = w.batch, w.num_q_heads
-    o = np.stack([np.stack([ref[(b, hh)][0] for hh in range(Hq)]) for b in range(B)])
-    lse = np.array([[ref[(b, hh)][1] for hh in range(Hq)] for b in range(B)])
+    B, Hq, Tq = w.batch, w.num_q_heads, w.tokens
+    if Tq == 1:
+        pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                              h["block_table"], **kw)
+        ref = oracle.decode_attention(pro["q_out"], pools, pro, h["seq_lens"], h["block_table"],
+                                      cfg)
+        o = np.stack([np.stack([ref[(b, hh)][0] for hh in range(Hq)]) for b in range(B)])
+        lse = np.array([[ref[(b, hh)][1] for hh in range(Hq)] for b in range(B)])
+        return pro, o, lse
+    pro = mt.prologue_tokens(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                             h["block_table"], **kw)
+    q_out = pro["q_out"].reshape(B, Tq, Hq, 128)
+    ref = mt.decode_attention_tokens(q_out, pools, pro, h["seq_lens"], h["block_table"], cfg)
+    o = np.array([[[ref[(b, j, hh)][0] for hh in range(Hq)] for j in range(Tq)] for b in range(B)])
+    lse = np.array([[[ref[(b, j, hh)][1] for hh in range(Hq)] for j in range(Tq)]
+                    for b in range(B)])
     return pro, o, lse
 
 
@@ -40,7 +53,8 @@ def check_step(w, sched, seed_note=""):
     inp = wl.make_inputs(w)
     poison_cache(inp, w)
     print(f"step: lens {w.seq_lens[:8]}{'...' if w.batch > 8 else ''} B={w.batch} "
-          f"{w.num_q_heads}q/{w.num_kv_heads}kv {w.kv_dtype} {sched} {seed_note}", flush=True)
+          f"{w.num_q_heads}q/{w.num_kv_heads}kv {w.kv_dtype} tokens {w.tokens} {sched} "
+          f"{seed_note}", flush=True)
     g = to_device(inp, dev)
     res = run_step(w, g, sched)
     pro, ro, rl = oracle_step(w, inp)
@@ -73,6 +87,52 @@ SCHEDS = [lb.Schedule("dynamic", num_workers=1), lb.Schedule("dynamic", num_work
 def test_small_steps(case, si):
     w = wl.custom(seed=200 + case, **SMALL[case])
     check_step(w, SCHEDS[si])
+
+
+# Several new tokens per sequence (multi-token decode).  Lengths 64k + 1 and
+# 64k + 2 leave the last tile with fewer rows than new tokens, so with many
+# workers the last chunk holds no row of the early tokens (empty partials).
+MULTI = [
+    dict(seq_lens=[2, 65, 129, 1000, 4097], num_q_heads=64, num_kv_heads=8, tokens=2),
+    dict(seq_lens=[4, 66, 700, 130], num_q_heads=16, num_kv_heads=4, tokens=4, kv_dtype="fp8"),
+    dict(seq_lens=[3, 2000, 193], num_q_heads=8, num_kv_heads=2, tokens=3),
+    dict(seq_lens=[16, 64 * 9 + 1], num_q_heads=8, num_kv_heads=8, tokens=16),   # group 1
+    dict(seq_lens=[300, 65], num_q_heads=32, num_kv_heads=4, tokens=2, norm_before_rope=True,
+         kv_dtype="fp8"),
+]
+MULTI_SCHEDS = [lb.Schedule("dynamic", num_workers=1), lb.Schedule("dynamic", num_workers=7),
+                lb.Schedule("dynamic", num_workers=256), lb.Schedule("static", num_workers=256),
+                lb.Schedule("dynamic", num_workers=256, xcd_weights=(9, 10, 9, 10, 9, 10, 9, 10))]
+
+
+@pytest.mark.parametrize("case", range(len(MULTI)))
+@pytest.mark.parametrize("si", range(len(MULTI_SCHEDS)))
+def test_multi_token_steps(case, si):
+    w = wl.custom(seed=600 + case, **MULTI[case])
+    res, ro, rl = check_step(w, MULTI_SCHEDS[si])
+    assert res["out"].shape == (w.batch, w.tokens, w.num_q_heads, 128)
+
+
+def test_multi_token_last_token_matches_one_token_step():
+    """The last new token attends the whole sequence: its output equals a
+    one-token step's on the same cache contents and query."""
+    dev = device()
+    w = wl.custom([1000, 65, 4100], num_q_heads=64, num_kv_heads=8, tokens=2, seed=650)
+    inp = wl.make_inputs(w)
+    g = to_device(inp, dev)
+    r2 = run_step(w, g, lb.Schedule("dynamic", num_workers=256))
+    # the one-token step over the caches the first step wrote, with the last
+    # token's inputs: its prologue rewrites that token's slot with the same bits
+    w1 = wl.custom([1000, 65, 4100], num_q_heads=64, num_kv_heads=8, seed=650)
+    g1 = dict(g)
+    for key in ("q", "k", "v"):
+        g1[key] = g[key][:, 1].contiguous()
+    g1["positions"] = g["positions"][:, 1].contiguous()
+    r1 = run_step(w1, g1, lb.Schedule("dynamic", num_workers=256))
+    assert torch.equal(r1["q_out"], r2["q_out"][:, 1])
+    d = (r1["out"].float() - r2["out"][:, 1].float()).abs().max().item()
+    assert d <= 2 ** -7, d                  # same math, other chunk boundaries in P.V rounding
+    assert (r1["lse"] - r2["lse"][:, 1]).abs().max().item() < 1e-5
 
 
 def test_tiny_named_workload():
