@@ -62,7 +62,7 @@ def split_kernel_bytes(w):
 class Case:
     """Two independent input sets of one workload on the GPU, plus outputs."""
 
-    def __init__(self, w, dev, kv_interleave=False):
+    def __init__(self, w, dev, kv_interleave=False, out_dtype="bf16", out_scale=1.0):
         self.w = w
         self.sets = []
         for copy in range(2):
@@ -73,9 +73,10 @@ class Case:
                                    g["num_pages"], page_stride=g["page_stride"],
                                    head_stride=g["head_stride"], rope_theta=w.rope_theta,
                                    rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale,
-                                   tokens_per_seq=w.tokens)
+                                   tokens_per_seq=w.tokens, out_dtype=out_dtype,
+                                   out_scale=out_scale)
         self.q_out = torch.empty_like(g["q"])
-        self.out = torch.empty_like(g["q"])
+        self.out = torch.empty(g["q"].shape, dtype=self.cfg.out_torch_dtype, device=dev)
         self.lse = torch.empty(self.cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32,
                                device=dev)
         self.ws = {}
@@ -255,14 +256,14 @@ def cpu_baseline(w, dev, min_seconds=10.0):
             "seconds": round(dt, 2)}
 
 
-def measure(w, dev, P, steps, warmup, full, weighted=True):
+def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16"):
     """Dynamic step time, per-kernel times, and (full) graph time and static sweep.
 
     weighted: calibrate per-XCD weights from traced steps, compare weighted and
     equal shares with interleaved untimed-for-the-headline loops, and time the
     headline with the faster of the two (both figures are reported)."""
     equal = lb.Schedule("dynamic", num_workers=P)
-    case = Case(w, dev)
+    case = Case(w, dev, out_dtype=out_dtype, out_scale=2.0 ** -7)
     for i in range(warmup):
         case.step(i, equal)
     r = {}
@@ -419,6 +420,14 @@ def main():
                 "split_attention_frac": round(spm / HBM_PEAK_GBS, 4),
                 "step_time_vs_one_token": round(rm["ms"] / ms, 4),
                 "xcd_weights": rm.get("xcd_weights"),
+            }
+            ro = measure(w, dev, P, args.steps, args.warmup, False, weighted, out_dtype="fp8")
+            result["fp8_output"] = {
+                "workload": WORKLOAD_TEXT["mix"] + ", BF16 cache, output stored as E4M3 codes "
+                            "(out_scale 2^-7)",
+                "us_per_step": round(ro["ms"] * 1e3, 2),
+                "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, ro["kernel_ms"])},
+                "step_time_vs_bf16_output": round(ro["ms"] / ms, 4),
             }
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(w, dev)

@@ -71,6 +71,10 @@ typedef enum {
 
 typedef enum { LBSR_KV_BF16 = 0, LBSR_KV_FP8_E4M3 = 1 } lbsr_kv_dtype;
 typedef enum { LBSR_SCHED_DYNAMIC = 0, LBSR_SCHED_STATIC = 1 } lbsr_sched;
+/* Attention output type ([B] "Code analysis 1": the output dtype is passed
+ * explicitly).  FP8: out holds OCP E4M3 codes, code = RNE(clamp(o /
+ * out_scale, -448, 448)), one byte per element; lse_out stays fp32. */
+typedef enum { LBSR_OUT_BF16 = 0, LBSR_OUT_FP8_E4M3 = 1 } lbsr_out_dtype;
 
 /* Sticky device error bits (int32 at lbsr_ws_layout.error_word). */
 #define LBSR_DEV_ERR_SEQ_LEN 1   /* seq_len outside [1, max_blocks_per_seq*64]: clamped */
@@ -135,6 +139,8 @@ typedef struct {
   float k_scale;            /* FP8 cache: value = code * k_scale; > 0; ignored for BF16 */
   float v_scale;            /* FP8 cache: value = code * v_scale; > 0; ignored for BF16 */
   float sm_scale;           /* softmax scale; 0 -> 1/sqrt(128) */
+  int32_t out_dtype;        /* lbsr_out_dtype of `out` (0 = BF16) */
+  float out_scale;          /* FP8 output: value = code * out_scale; > 0; ignored for BF16 */
 } lbsr_params;
 
 typedef struct {
@@ -254,8 +260,8 @@ lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq
  * chunk is one online-softmax pass over its tiles; a sequence with several
  * chunks is merged by log-sum-exp weights (chunks are summed in a fixed
  * order, so the result is deterministic).
- *   q_out [batch][Hq][128] BF16   out [batch][Hq][128] BF16
- *   lse_out nullable float[batch][Hq]
+ *   q_out [batch][Hq][128] BF16   out [batch][Hq][128] BF16, or E4M3 codes
+ *   (params->out_dtype)           lse_out nullable float[batch][Hq]
  * Rows at or past L_b of a sequence's last page are never used, whatever
  * they hold.  Deterministic: no atomics.
  */

@@ -26,6 +26,7 @@ MAX_XCD_WEIGHT = 65536
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 KV_BF16, KV_FP8_E4M3 = 0, 1
 SCHED_DYNAMIC, SCHED_STATIC = 0, 1
+OUT_BF16, OUT_FP8_E4M3 = 0, 1
 DEV_ERR_SEQ_LEN, DEV_ERR_PAGE, DEV_ERR_POSITION = 1, 2, 4
 
 # Every symbol include/lbsr.h declares.
@@ -62,7 +63,8 @@ class Shape(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float),
                 ("norm_before_rope", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float), ("sm_scale", ctypes.c_float)]
+                ("v_scale", ctypes.c_float), ("sm_scale", ctypes.c_float),
+                ("out_dtype", ctypes.c_int32), ("out_scale", ctypes.c_float)]
 
 
 class SchedCfg(ctypes.Structure):

@@ -132,6 +132,10 @@ lbsr_status check_params(const lbsr_params* p, int32_t kv_dtype) {
     return fail(LBSR_E_INVALID, "norm_before_rope must be 0 or 1");
   if (!(p->sm_scale >= 0) || !isfinite(p->sm_scale))
     return fail(LBSR_E_INVALID, "sm_scale %g must be finite and >= 0", (double)p->sm_scale);
+  if (p->out_dtype != LBSR_OUT_BF16 && p->out_dtype != LBSR_OUT_FP8_E4M3)
+    return fail(LBSR_E_INVALID, "out_dtype %d unknown", p->out_dtype);
+  if (p->out_dtype == LBSR_OUT_FP8_E4M3 && (!(p->out_scale > 0) || !isfinite(p->out_scale)))
+    return fail(LBSR_E_INVALID, "out_scale %g must be finite and > 0", (double)p->out_scale);
   if (kv_dtype == LBSR_KV_FP8_E4M3 &&
       (!(p->k_scale > 0) || !isfinite(p->k_scale) || !(p->v_scale > 0) || !isfinite(p->v_scale)))
     return fail(LBSR_E_INVALID, "k_scale %g / v_scale %g must be finite and > 0",
@@ -341,21 +345,27 @@ lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_
                       int64_t* trace, hipStream_t stream) {
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
-  return hip_status(lbsr::launch_split_attention(geo, fp8, l.num_workers, q_out, kc, vc, bt,
-                                                 plan_ptrs(ws, l), out, lse_out,
+  // outputs and partials carry o / out_scale (FP8 output), V's scale folded in
+  const bool out_fp8 = params->out_dtype == LBSR_OUT_FP8_E4M3;
+  const double vs = fp8 ? (double)params->v_scale : 1.0;
+  const float o_scale = (float)(out_fp8 ? vs / (double)params->out_scale : vs);
+  return hip_status(lbsr::launch_split_attention(geo, fp8, out_fp8, l.num_workers, q_out, kc, vc,
+                                                 bt, plan_ptrs(ws, l), out, lse_out,
                                                  score_scale_log2(params, shape->kv_dtype),
-                                                 fp8 ? params->v_scale : 1.0f, trace, stream),
+                                                 o_scale, trace, stream),
                     "split attention launch");
 }
 
-lbsr_status run_combine(const lbsr_shape* shape, int32_t batch, const lbsr_ws_layout& l, void* ws,
-                        void* out, float* lse_out, bool fold_token_status, hipStream_t stream) {
+lbsr_status run_combine(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                        const lbsr_ws_layout& l, void* ws, void* out, float* lse_out,
+                        bool fold_token_status, hipStream_t stream) {
   const lbsr::Geometry geo = geometry(shape, batch);
   // a sequence has at most one chunk per worker (dynamic) or split (static),
   // and at most one per tile: the merge stages that many rows' lse in LDS
   const int per_seq = l.static_splits ? l.static_splits : l.num_workers;
   const int bound = per_seq < shape->max_blocks_per_seq ? per_seq : shape->max_blocks_per_seq;
   return hip_status(lbsr::launch_combine(geo, plan_ptrs(ws, l), out, lse_out, bound,
+                                         params->out_dtype == LBSR_OUT_FP8_E4M3,
                                          fold_token_status, stream),
                     "merge launch");
 }
@@ -448,7 +458,7 @@ lbsr_status lbsr_attention(const lbsr_shape* shape, const lbsr_params* params, i
   const hipStream_t s = (hipStream_t)stream;
   LBSR_CHECK(run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
                        lse_out, nullptr, s));
-  return run_combine(shape, batch, l, workspace, out, lse_out, false, s);
+  return run_combine(shape, params, batch, l, workspace, out, lse_out, false, s);
 }
 
 static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
@@ -496,7 +506,7 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
     st = run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
                    lse_out, trace, s);
   mark(2);
-  if (st == LBSR_OK) st = run_combine(shape, batch, l, workspace, out, lse_out, true, s);
+  if (st == LBSR_OK) st = run_combine(shape, params, batch, l, workspace, out, lse_out, true, s);
   mark(3);
   if (kernel_ms) {
     if (st == LBSR_OK) st = hip_status(hipEventSynchronize(ev[3]), "hipEventSynchronize");

@@ -260,8 +260,8 @@ template <bool kFp8>
 __device__ __forceinline__ void split_worker(
     int worker, const Geometry& geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
-    const PlanPtrs& plan, uint16_t* __restrict__ out, float* __restrict__ lse_out,
-    float score_scale_log2, float out_scale) {
+    const PlanPtrs& plan, void* __restrict__ out, float* __restrict__ lse_out,
+    float score_scale_log2, float out_scale, int out_fp8) {
   constexpr int kElemBytes = kFp8 ? 1 : 2;
   const int c_begin = wave_uniform(plan.worker_chunk[worker]);
   const int c_end = wave_uniform(plan.worker_chunk[worker + 1]);
@@ -341,8 +341,17 @@ __device__ __forceinline__ void split_worker(
       const float lse2 = l > 0.f ? m + __builtin_amdgcn_logf(l) : -__builtin_inff();  // log2
       if (col < GT) {
         const size_t orow = ((size_t)b * T + tok) * Hq + (size_t)g * G + hl;  // out / lse_out row
-        if (single) {
-          uint16_t* o = out + orow * kHeadDim + 4 * kc;
+        if (single && out_fp8) {
+          // E4M3 codes of o / out_scale (folded into scale): 4 bytes per db
+          uint8_t* o = (uint8_t*)out + orow * kHeadDim + 4 * kc;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const f32x4 x = O[db] * scale;
+            *(uint32_t*)(o + 16 * db) = f32x4_to_e4m3x4(x[0], x[1], x[2], x[3]);
+          }
+          if (kc == 0 && lse_out) lse_out[orow] = lse2 * kLn2;
+        } else if (single) {
+          uint16_t* o = (uint16_t*)out + orow * kHeadDim + 4 * kc;
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             bf16x4 v4;
@@ -375,13 +384,13 @@ template <bool kFp8>
 __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
     Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table, PlanPtrs plan,
-    uint16_t* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
-    float out_scale, int64_t* __restrict__ trace) {
+    void* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
+    float out_scale, int out_fp8, int64_t* __restrict__ trace) {
   int64_t t_start = 0;
   if (trace != nullptr && threadIdx.x == 0) t_start = (int64_t)wall_clock64();
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
   split_worker<kFp8>(worker, geo, q_out, k_pool, v_pool, block_table, plan, out, lse_out,
-                     score_scale_log2, out_scale);
+                     score_scale_log2, out_scale, out_fp8);
   if (trace != nullptr) {
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -431,9 +440,9 @@ constexpr int kMergeLseUnroll = LBSR_MERGE_LSE_UNROLL;
 // keep the whole grid resident at once, which measured faster than deeper
 // per-thread unrolling at lower occupancy.
 __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry geo, PlanPtrs plan,
-                                                                    uint16_t* __restrict__ out,
+                                                                    void* __restrict__ out,
                                                                     float* __restrict__ lse_out,
-                                                                    int min_slices,
+                                                                    int min_slices, int out_fp8,
                                                                     int fold_token_status) {
   constexpr int kThreads = kMergeWaves * kWave;
   const int slice = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -546,14 +555,19 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
     const int bs = slice * (16 / nslices) + t / (2 * G);
     const int h3 = (t % (2 * G)) >> 1;
     const int d = bs * 8 + (t & 1) * 4;
-    bf16x4 rr;
+    if (out_fp8) {
+      *(uint32_t*)((uint8_t*)out + out_row(h3) * kHeadDim + d) =
+          f32x4_to_e4m3x4(sum[0], sum[1], sum[2], sum[3]);
+    } else {
+      bf16x4 rr;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) rr[x] = (__bf16)sum[x];
-    *(bf16x4*)(out + out_row(h3) * kHeadDim + d) = rr;
+      for (int x = 0; x < 4; ++x) rr[x] = (__bf16)sum[x];
+      *(bf16x4*)((uint16_t*)out + out_row(h3) * kHeadDim + d) = rr;
+    }
   }
 }
 
-hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers,
+hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, int num_workers,
                                   const void* q_out, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const PlanPtrs& plan, void* out,
                                   float* lse_out, float score_scale_log2, float out_scale,
@@ -562,17 +576,18 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers
   if (fp8) {
     split_attention_kernel<true><<<num_workers, waves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
-        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale, trace);
+        block_table, plan, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0, trace);
   } else {
     split_attention_kernel<false><<<num_workers, waves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
-        block_table, plan, (uint16_t*)out, lse_out, score_scale_log2, out_scale, trace);
+        block_table, plan, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0, trace);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
-                          int max_chunks_per_seq, bool fold_token_status, hipStream_t stream) {
+                          int max_chunks_per_seq, bool out_fp8, bool fold_token_status,
+                          hipStream_t stream) {
   // S slices: a power of two dividing 32 with 32G/S <= 64 float4 per row
   // slice, G = group * Tq columns per (chunk, KV group)
   const int cols = geo.group * geo.tokens;
@@ -581,8 +596,9 @@ hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, 
   const int max_slices = slices > LBSR_MERGE_MAX_SLICES ? slices : LBSR_MERGE_MAX_SLICES;
   dim3 grid(max_slices, geo.num_kv_heads, geo.batch);
   const size_t lds = (size_t)max_chunks_per_seq * cols * sizeof(float);
-  merge_kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, (uint16_t*)out, lse_out,
-                                                           slices, fold_token_status ? 1 : 0);
+  merge_kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, out, lse_out, slices,
+                                                           out_fp8 ? 1 : 0,
+                                                           fold_token_status ? 1 : 0);
   return hipGetLastError();
 }
 

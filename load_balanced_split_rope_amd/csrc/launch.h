@@ -17,16 +17,19 @@ hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const v
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, const SchedParams& sp,
                        const PlanPtrs& plan, hipStream_t stream);
 
-hipError_t launch_split_attention(const Geometry& geo, bool fp8, int num_workers,
+hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, int num_workers,
                                   const void* q_out, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const PlanPtrs& plan, void* out,
                                   float* lse_out, float score_scale_log2, float out_scale,
                                   int64_t* trace, hipStream_t stream);
 
+// out_fp8: `out` holds E4M3 codes of the merged values (which the split
+// kernel already divided by the output scale).
 // fold_token_status: also OR plan.token_status (written by the fused
 // plan + prologue launch of the same step) into the error word.
 hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, float* lse_out,
-                          int max_chunks_per_seq, bool fold_token_status, hipStream_t stream);
+                          int max_chunks_per_seq, bool out_fp8, bool fold_token_status,
+                          hipStream_t stream);
 
 hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 const PlanPtrs& plan, const Geometry& geo,

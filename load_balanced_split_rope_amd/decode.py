@@ -30,6 +30,8 @@ class DecodeConfig:
     v_scale: float = 1.0
     sm_scale: float = 0.0         # 0 -> 1/sqrt(128)
     tokens_per_seq: int = 1       # new tokens per sequence (multi-token decode)
+    out_dtype: str = "bf16"       # "bf16", or "fp8": E4M3 codes of out / out_scale
+    out_scale: float = 1.0
 
     def shape(self):
         return B.Shape(self.num_q_heads, self.num_kv_heads, B.HEAD_DIM, B.PAGE_SIZE,
@@ -44,8 +46,17 @@ class DecodeConfig:
         return (batch,) + rest if Tq == 1 else (batch, Tq) + rest
 
     def params(self):
+        if self.out_dtype not in ("bf16", "fp8"):
+            raise ValueError(f"out_dtype {self.out_dtype!r}: 'bf16' or 'fp8'")
         return B.Params(self.rope_theta, self.rms_eps, int(self.norm_before_rope),
-                        self.k_scale, self.v_scale, self.sm_scale)
+                        self.k_scale, self.v_scale, self.sm_scale,
+                        B.OUT_BF16 if self.out_dtype == "bf16" else B.OUT_FP8_E4M3,
+                        self.out_scale)
+
+    @property
+    def out_torch_dtype(self):
+        """dtype of `out`: bfloat16, or uint8 E4M3 codes."""
+        return torch.bfloat16 if self.out_dtype == "bf16" else torch.uint8
 
     @property
     def cache_dtype(self):
@@ -167,7 +178,7 @@ def attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, sched: Sc
     batch = q_out.shape[0]
     Hq, D = cfg.num_q_heads, B.HEAD_DIM
     _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
-    _need(out, "out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(out, "out", cfg.out_torch_dtype, shape=cfg.tokens_shape(batch, Hq, D))
     if lse_out is not None:
         _need(lse_out, "lse_out", torch.float32, shape=cfg.tokens_shape(batch, Hq))
     _check_table(cfg, block_table, batch)
@@ -188,7 +199,7 @@ def _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_tabl
     _need(k, "k", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
     _need(v, "v", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
     _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
-    _need(out, "out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(out, "out", cfg.out_torch_dtype, shape=cfg.tokens_shape(batch, Hq, D))
     _need(positions, "positions", torch.int32, shape=cfg.tokens_shape(batch))
     _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
     _need(q_norm_w, "q_norm_w", torch.bfloat16, shape=(D,))

@@ -41,7 +41,7 @@ from .schedule import (tiles_per_sequence, plan_dynamic, plan_static,
                        default_static_splits, Plan)
 from .attention import attend_full, attend_chunk, combine_lse
 from .step import (prologue, cache_slot, gather_kv, decode_attention,
-                   split_attention)
+                   split_attention, encode_output)
 from . import multitoken   # several new tokens per sequence (R20)
 
 __all__ = [
@@ -51,5 +51,5 @@ __all__ = [
     "tiles_per_sequence", "plan_dynamic", "plan_static",
     "default_static_splits", "Plan", "attend_full", "attend_chunk",
     "combine_lse", "prologue", "cache_slot", "gather_kv", "decode_attention",
-    "split_attention", "multitoken",
+    "split_attention", "encode_output", "multitoken",
 ]

@@ -18,6 +18,8 @@ Readings used here:
   q_out (BF16), the cache slot (BF16 or E4M3) and the final output (BF16).
   Everything else is fp64.  Tests compare GPU results with these fp64 values.
 * R17 -- rows at or past L_b inside the last page are never used.
+* R21 -- with an FP8 output the attention output is stored as E4M3 codes of
+  o / out_scale (clamp to +-448, then round to nearest even); lse stays fp32.
 """
 
 import numpy as np
@@ -77,6 +79,18 @@ def prologue(q, k, v, positions, wq, wk, block_table, *, theta, eps, kv_dtype,
     else:
         raise ValueError(kv_dtype)
     return out
+
+
+def encode_output(o, out_dtype="bf16", out_scale=1.0):
+    """The stored attention output (R10, R21): BF16 bits of o, or -- FP8 output,
+    page B "Code analysis 1" (the output dtype is passed explicitly) -- the E4M3
+    codes of o / out_scale, clamped to +-448 and rounded to nearest even."""
+    o = np.asarray(o, dtype=np.float64)
+    if out_dtype == "bf16":
+        return f64_to_bf16_bits(o)
+    if out_dtype == "fp8":
+        return f64_to_e4m3(o / out_scale)
+    raise ValueError(out_dtype)
 
 
 def decode_values(stored, kv_dtype, scale):

@@ -45,6 +45,34 @@ def check_output(got, ref, kv_dtype, what="output", rel_l2=True):
     return max_abs, rl2
 
 
+def e4m3_step(x):
+    """Spacing of OCP E4M3 values around |x| (2^-9 in the subnormal range)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.ldexp(1.0, (np.maximum(e, -6) - 3).astype(np.int64))
+
+
+def check_output_fp8(codes, ref, kv_dtype, out_scale, what="output"):
+    """FP8 output (R21): the decoded codes times out_scale must lie within the
+    R14 tolerance of the fp64 result plus half an E4M3 step of the output;
+    where |ref| / out_scale exceeds 448 the code must be the saturated one."""
+    from oracle import e4m3_to_f64
+    got = e4m3_to_f64(np.asarray(codes, dtype=np.uint8)) * out_scale
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: NaN codes"
+    x = ref / out_scale
+    sat = np.abs(x) > 448
+    assert np.all(np.abs(got[sat]) == 448 * out_scale), f"{what}: saturation"
+    base = BF16_ATOL + BF16_RTOL * np.abs(ref) if kv_dtype == "bf16" else np.full(ref.shape, FP8_ATOL)
+    tol = base + 0.5 * e4m3_step(np.minimum(np.abs(x), 448)) * out_scale
+    err = np.abs(got - ref)
+    bad = (err > tol) & ~sat
+    assert not bad.any(), f"{what}: {int(bad.sum())} codes out of tolerance, max err {err.max():.3e}"
+    return float(err[~sat].max()) if (~sat).any() else 0.0
+
+
 def poison_indices(inp, w, kind, spare_pages=True):
     """Pool indices (one pool) of every element the step must not read.
 

@@ -34,7 +34,7 @@ def run_step(w, g, sched, lse=True, cfg=None):
     cfg = cfg or config_for(w, g)
     ws = lb.alloc_workspace(cfg, w.batch, sched, device=dev)
     q_out = torch.empty_like(g["q"])
-    out = torch.empty_like(g["q"])
+    out = torch.empty(g["q"].shape, dtype=cfg.out_torch_dtype, device=dev)
     lse_t = (torch.empty(cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
              if lse else None)
     lb.decode_step(cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"], g["q_norm_w"],

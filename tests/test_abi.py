@@ -212,3 +212,26 @@ def test_workspace_grows_with_tokens(lib):
     assert two.partial_lse - two.partial_o >= 2 * cmax * 64 * 128 * 4
     assert two.total - two.partial_lse >= 2 * cmax * 64 * 4
     assert two.total > one.total
+
+
+def test_params_struct_matches_header():
+    """lbsr_params: double, float, int32, 3 floats, int32 out_dtype, float out_scale: 40 bytes."""
+    assert ctypes.sizeof(B.Params) == 40
+    assert B.Params.out_dtype.offset == 28 and B.Params.out_scale.offset == 32
+
+
+@pytest.mark.parametrize("out_dtype,out_scale,status", [
+    (B.OUT_BF16, 0.0, B.OK), (B.OUT_FP8_E4M3, 0.5, B.OK), (B.OUT_FP8_E4M3, 0.0, B.E_INVALID),
+    (B.OUT_FP8_E4M3, float("inf"), B.E_INVALID), (B.OUT_FP8_E4M3, -1.0, B.E_INVALID),
+    (7, 1.0, B.E_INVALID),
+])
+def test_out_dtype_validation(lib, out_dtype, out_scale, status):
+    s = cfg_mix().shape()
+    c = Schedule("dynamic", num_workers=256).cfg()
+    p = cfg_mix().params()
+    p.out_dtype, p.out_scale = out_dtype, out_scale
+    fake = ctypes.c_void_p(0x10000)
+    got = lib.lbsr_attention(ctypes.byref(s), ctypes.byref(p), 32, fake, fake, fake, fake,
+                             ctypes.byref(c), fake, 16, fake, fake, ctypes.c_void_p(0))
+    # a valid configuration fails only at the (too small) workspace, before any launch
+    assert got == (B.E_WORKSPACE if status == B.OK else status), lib.lbsr_last_error()

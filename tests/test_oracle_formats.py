@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import bf16_bits_to_f64, f64_to_bf16_bits, e4m3_to_f64, f64_to_e4m3
 
 
@@ -108,3 +109,20 @@ def test_e4m3_clamps_instead_of_nan():
     """Reading R9: out-of-range values saturate to +-448; NaN stays NaN."""
     out = f64_to_e4m3(np.array([480.0, 1e9, -1e9, np.inf, -np.inf, np.nan]))
     assert out.tolist() == [0x7E, 0x7E, 0xFE, 0x7E, 0xFE, 0x7F]
+
+
+def test_encode_output_by_hand():
+    """R21 on hand-worked values (OCP E4M3: bias 7, 3 mantissa bits, max 448,
+    subnormal step 2^-9), out_scale 2."""
+    o = np.array([1.0, -1.0, 1000.0, -1000.0, 2.0 ** -4, 2.0 ** -8, 2.0 ** -11, 0.0,
+                  2 * 1.0625, 2 * 1.1875, 2 * 3 * 2.0 ** -10])
+    codes = oracle.encode_output(o, "fp8", 2.0)
+    # 0.5 -> 0x30; 500 -> clamp 448 -> 0x7E; 2^-5 -> 0x10; 2^-9 -> 0x01 (smallest
+    # subnormal); 2^-12 -> rounds to 0; 1.0625 (tie between 1 and 1.125) -> even 1.0 = 0x38;
+    # 1.1875 (tie between 1.125 and 1.25) -> even 1.25 = 0x3A; 3*2^-10 = 1.5 subnormal
+    # steps (tie) -> even 2 steps = 0x02
+    assert codes.tolist() == [0x30, 0xB0, 0x7E, 0xFE, 0x10, 0x01, 0x00, 0x00, 0x38, 0x3A, 0x02]
+    bits = oracle.encode_output(np.array([1.0, -2.5]), "bf16")
+    assert bits.tolist() == [0x3F80, 0xC020]
+    with pytest.raises(ValueError):
+        oracle.encode_output(o, "fp16")
