@@ -284,6 +284,19 @@ lbsr_status validate_attention(const lbsr_shape* shape, const lbsr_params* param
   return LBSR_OK;
 }
 
+// theta^(-2i/128) for i < 64, with the host's libm; the last theta's table is
+// kept per thread, as a step normally reuses it.
+const lbsr::RopeFreqs& rope_freqs(double theta) {
+  thread_local double cached_theta = 0.0;
+  thread_local lbsr::RopeFreqs table;
+  if (theta != cached_theta) {
+    for (int i = 0; i < LBSR_HEAD_DIM / 2; ++i)
+      table.omega[i] = pow(theta, (-2.0 * (double)i) / (double)LBSR_HEAD_DIM);
+    cached_theta = theta;
+  }
+  return table;
+}
+
 lbsr_status run_prologue(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
                          const void* q, const void* k, const void* v, const int32_t* positions,
                          const void* wq, const void* wk, const int32_t* bt, void* kc, void* vc,
@@ -291,7 +304,8 @@ lbsr_status run_prologue(const lbsr_shape* shape, const lbsr_params* params, int
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
   return hip_status(lbsr::launch_prologue(geo, fp8, q, k, v, positions, wq, wk, bt, kc, vc, q_out,
-                                          error_word, params->rope_theta, (double)params->rms_eps,
+                                          error_word, rope_freqs(params->rope_theta),
+                                          (double)params->rms_eps,
                                           params->norm_before_rope, fp8 ? params->k_scale : 1.0,
                                           fp8 ? params->v_scale : 1.0, stream),
                     "prologue launch");
@@ -327,7 +341,7 @@ lbsr_status run_plan_prologue(const lbsr_shape* shape, const lbsr_params* params
   return hip_status(
       lbsr::launch_plan_prologue(seq_lens, sched_params(shape, cfg, l), plan_ptrs(ws, l), geo, fp8, q,
                                  k, v, positions,
-                                 wq, wk, bt, kc, vc, q_out, params->rope_theta,
+                                 wq, wk, bt, kc, vc, q_out, rope_freqs(params->rope_theta),
                                  (double)params->rms_eps, params->norm_before_rope,
                                  fp8 ? params->k_scale : 1.0, fp8 ? params->v_scale : 1.0, stream),
       "plan + prologue launch");

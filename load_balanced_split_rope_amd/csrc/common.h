@@ -27,6 +27,13 @@ __host__ __device__ inline int xcd_run_size(int x, int num_workers) {
   return (num_workers - x + kXcds - 1) / kXcds;
 }
 
+// RoPE frequencies theta^(-2i/128), i < 64, computed once on the host (they
+// depend only on theta) and passed by value; lane i of a prologue wave reads
+// omega[i].
+struct RopeFreqs {
+  double omega[kHeadDim / 2];
+};
+
 // The schedule's parameters, passed by value.
 struct SchedParams {
   int32_t min_len;       // shorter lengths are clamped up and flagged (a sequence holds its new tokens)

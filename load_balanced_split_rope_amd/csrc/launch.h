@@ -10,7 +10,7 @@ namespace lbsr {
 hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const void* k,
                            const void* v, const int32_t* positions, const void* wq,
                            const void* wk, const int32_t* block_table, void* k_cache,
-                           void* v_cache, void* q_out, int32_t* error_word, double theta,
+                           void* v_cache, void* q_out, int32_t* error_word, const RopeFreqs& freqs,
                            double eps, int norm_first, double k_scale, double v_scale,
                            hipStream_t stream);
 
@@ -36,7 +36,7 @@ hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 bool fp8, const void* q, const void* k, const void* v,
                                 const int32_t* positions, const void* wq, const void* wk,
                                 const int32_t* block_table, void* k_cache, void* v_cache,
-                                void* q_out, double theta, double eps, int norm_first,
+                                void* q_out, const RopeFreqs& freqs, double eps, int norm_first,
                                 double k_scale, double v_scale, hipStream_t stream);
 
 }  // namespace lbsr

@@ -12,7 +12,9 @@
 // The work is tiny (a few MB per step) and latency bound, so it is computed
 // in fp64 (full rate on CDNA4) with contraction off, and every stored value is
 // rounded once from fp64: the stored bits then equal the exact result's
-// rounding except within ~1e-15 relative of a rounding midpoint.
+// rounding except within ~1e-15 relative of a rounding midpoint.  The
+// frequencies come precomputed (RopeFreqs): an fp64 pow per lane was the
+// largest single step of the chain.
 //
 // One wave per row; lane l owns the rotation pair (l, l + 64).
 #pragma once
@@ -97,7 +99,7 @@ __device__ inline void prologue_row(
     const int32_t* __restrict__ positions, const uint16_t* __restrict__ wq,
     const uint16_t* __restrict__ wk, const int32_t* __restrict__ block_table,
     void* __restrict__ k_cache, void* __restrict__ v_cache, uint16_t* __restrict__ q_out,
-    int32_t* __restrict__ error_word, int32_t* __restrict__ token_status, double theta,
+    int32_t* __restrict__ error_word, int32_t* __restrict__ token_status, const RopeFreqs& freqs,
     double eps, int norm_first, double k_scale, double v_scale) {
 #pragma clang fp contract(off)
   const int Hq = geo.num_q_heads, Hkv = geo.num_kv_heads;
@@ -127,7 +129,7 @@ __device__ inline void prologue_row(
 
   if (kind != 2) {
     const double w0 = bf16_to_f64(w[lane]), w1 = bf16_to_f64(w[lane + 64]);
-    const double omega = pow(theta, (-2.0 * (double)lane) / (double)kHeadDim);
+    const double omega = freqs.omega[lane];
     const double a = (double)pos * omega;
     double sn, cs;
     sincos(a, &sn, &cs);

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prologue_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ positions,
     const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
     const int32_t* __restrict__ block_table, void* __restrict__ k_cache,
-    void* __restrict__ v_cache, uint16_t* __restrict__ q_out, double theta, double eps,
+    void* __restrict__ v_cache, uint16_t* __restrict__ q_out, RopeFreqs freqs, double eps,
     int norm_first, double k_scale, double v_scale) {
   extern __shared__ int s_cu[];
   if (blockIdx.x == 0) {
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prologue_kernel(
   // touch it: each token's status is stored (overwritten every step) and the
   // merge kernel, which runs after both, folds it into the error word.
   prologue_row<kFp8>(tok, tok / geo.tokens, r - tok * rows, geo, q, k, v, positions, wq, wk,
-                     block_table, k_cache, v_cache, q_out, nullptr, plan.token_status, theta,
+                     block_table, k_cache, v_cache, q_out, nullptr, plan.token_status, freqs,
                      eps, norm_first, k_scale, v_scale);
 }
 
@@ -42,7 +42,7 @@ hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 bool fp8, const void* q, const void* k, const void* v,
                                 const int32_t* positions, const void* wq, const void* wk,
                                 const int32_t* block_table, void* k_cache, void* v_cache,
-                                void* q_out, double theta, double eps, int norm_first,
+                                void* q_out, const RopeFreqs& freqs, double eps, int norm_first,
                                 double k_scale, double v_scale, hipStream_t stream) {
   const int rows = geo.num_q_heads + 2 * geo.num_kv_heads;
   const int blocks =
@@ -55,12 +55,12 @@ hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
     plan_prologue_kernel<true><<<blocks, kPlanThreads, lds, stream>>>(
         seq_lens, sp, plan, geo, qq, kk, vv, positions,
         (const uint16_t*)wq, (const uint16_t*)wk, block_table, k_cache, v_cache,
-        (uint16_t*)q_out, theta, eps, norm_first, k_scale, v_scale);
+        (uint16_t*)q_out, freqs, eps, norm_first, k_scale, v_scale);
   else
     plan_prologue_kernel<false><<<blocks, kPlanThreads, lds, stream>>>(
         seq_lens, sp, plan, geo, qq, kk, vv, positions,
         (const uint16_t*)wq, (const uint16_t*)wk, block_table, k_cache, v_cache,
-        (uint16_t*)q_out, theta, eps, norm_first, k_scale, v_scale);
+        (uint16_t*)q_out, freqs, eps, norm_first, k_scale, v_scale);
   return hipGetLastError();
 }
 
