@@ -126,7 +126,8 @@ class Case:
 
     def calibrate(self, P, reps=8):
         """Per-XCD weights from traced steps: a round with equal shares, then a
-        round under the first estimate; the two rounds' rates are averaged."""
+        round under the first estimate; the two rounds' rates are averaged.
+        (Further rounds of busy-time correction measured no better.)"""
         rates, wts = [], None
         for _ in range(2):
             sched = lb.Schedule("dynamic", num_workers=P, xcd_weights=wts)
@@ -302,6 +303,11 @@ def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16"):
     return r
 
 
+def case_static_ms(case, P, steps):
+    """Step time of the static split-KV baseline at its default S."""
+    return case.timed_steps(lb.Schedule("static", num_workers=P), steps, 5)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +427,28 @@ def main():
                 "step_time_vs_one_token": round(rm["ms"] / ms, 4),
                 "xcd_weights": rm.get("xcd_weights"),
             }
+            # controls: a uniform batch, where the static split at its default S
+            # equals the dynamic plan (expected ratio ~1), and the log-uniform
+            # mixed batch with an FP8 cache
+            controls = {}
+            for name in ("uniform", "loguniform"):
+                wc = wl.named(name)
+                steps_c = args.steps if name == "uniform" else max(10, args.steps // 4)
+                rc = measure(wc, dev, P, steps_c, args.warmup, False, False)
+                cc = Case(wc, dev)
+                st = case_static_ms(cc, P, steps_c)
+                del cc
+                torch.cuda.empty_cache()
+                cbc = compulsory_bytes(wc)["total"]
+                controls[name] = {
+                    "workload": WORKLOAD_TEXT[name], "us_per_step": round(rc["ms"] * 1e3, 2),
+                    "value_GBs": round(cbc / (rc["ms"] * 1e-3) / 1e9, 1),
+                    "hbm_frac_step": round(cbc / (rc["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "static_default_us_per_step": round(st * 1e3, 2),
+                    "dynamic_speedup_vs_static_default": round(st / rc["ms"], 3),
+                    "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, rc["kernel_ms"])},
+                }
+            result["controls"] = controls
             ro = measure(w, dev, P, args.steps, args.warmup, False, weighted, out_dtype="fp8")
             result["fp8_output"] = {
                 "workload": WORKLOAD_TEXT["mix"] + ", BF16 cache, output stored as E4M3 codes "
