@@ -167,6 +167,7 @@ WORKLOAD_TEXT = {
     "uniform": "uniform: 32 x 4096 tokens",
     "loguniform": "loguniform: 64 sequences, lengths log-uniform in [512, 262144], FP8 cache",
     "mix_mtp2": "mix_mtp2: 1 x 131072 + 31 x 4096 tokens, 2 new tokens per sequence",
+    "mix_mtp4": "mix_mtp4: 1 x 131072 + 31 x 4096 tokens, 4 new tokens per sequence",
 }
 WALL_CLOCK_MHZ = 100.0   # the constant clock the trace stamps (100 MHz on MI300-class GPUs)
 
@@ -314,7 +315,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mix",
-                    choices=["mix", "mix_fp8", "uniform", "loguniform", "mix_mtp2"],
+                    choices=["mix", "mix_fp8", "uniform", "loguniform", "mix_mtp2", "mix_mtp4"],
                     help="headline workload (the metric is quoted on mix)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (a known-size kernel "
@@ -426,6 +427,15 @@ def main():
                 "split_attention_frac": round(spm / HBM_PEAK_GBS, 4),
                 "step_time_vs_one_token": round(rm["ms"] / ms, 4),
                 "xcd_weights": rm.get("xcd_weights"),
+            }
+            w4 = wl.named("mix_mtp4")
+            r4 = measure(w4, dev, P, args.steps, args.warmup, False, weighted)
+            result["mtp4"] = {
+                "workload": WORKLOAD_TEXT["mix_mtp4"] + " (32 (token, head) columns per KV head: "
+                            "two 16-column blocks on neighbouring waves)",
+                "us_per_step": round(r4["ms"] * 1e3, 2),
+                "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, r4["kernel_ms"])},
+                "step_time_vs_one_token": round(r4["ms"] / ms, 4),
             }
             # controls: a uniform batch, where the static split at its default S
             # equals the dynamic plan (expected ratio ~1), and the log-uniform

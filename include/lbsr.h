@@ -113,8 +113,12 @@ typedef enum { LBSR_OUT_BF16 = 0, LBSR_OUT_FP8_E4M3 = 1 } lbsr_out_dtype;
  * positions [batch][Tq], lse_out [batch][Tq][Hq] -- and seq_lens[b] counts all
  * Tq of them.  New token j of sequence b sits at position L_b - Tq + j and
  * attends rows [0, L_b - Tq + j]: the cached prefix and new tokens 0..j.
- * The Tq * G queries of one KV head share each KV read.  Tq = 1 is the
- * ordinary step and the layouts reduce to the ones written below.
+ * The Tq * G queries of one KV head share each KV read: up to 16 of them in
+ * one wave; more (up to 64) run as blocks of 16 on neighbouring waves that
+ * read the same tiles together.  The merge stages (chunks of a sequence) x
+ * (G * Tq) weights in 64 KiB of LDS: a larger product (e.g. 1024 workers
+ * with G * Tq = 32) is LBSR_E_UNSUPPORTED.  Tq = 1 is the ordinary step and
+ * the layouts reduce to the ones written below.
  */
 
 typedef struct {
@@ -124,7 +128,7 @@ typedef struct {
   int32_t page_size;          /* must be 64 */
   int32_t kv_dtype;           /* lbsr_kv_dtype */
   int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
-  int32_t tokens_per_seq;     /* Tq: new tokens per sequence, >= 1 with G * Tq <= 16
+  int32_t tokens_per_seq;     /* Tq: new tokens per sequence, >= 1 with G * Tq <= 64
                                  (multi-token decode, see below); 1 = one-token step */
   int32_t reserved;           /* must be 0 */
   int64_t num_pages;          /* pages in each pool, >= 1 */

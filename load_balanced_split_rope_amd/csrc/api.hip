@@ -94,9 +94,9 @@ lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
   if (s->num_q_heads > 4096) return fail(LBSR_E_UNSUPPORTED, "Hq %d > 4096", s->num_q_heads);
   if (s->tokens_per_seq < 1)
     return fail(LBSR_E_INVALID, "tokens_per_seq %d < 1", s->tokens_per_seq);
-  if ((int64_t)s->tokens_per_seq * (s->num_q_heads / s->num_kv_heads) > lbsr::kMaxGroup)
-    return fail(LBSR_E_UNSUPPORTED, "tokens_per_seq %d x group %d > 16", s->tokens_per_seq,
-                s->num_q_heads / s->num_kv_heads);
+  if ((int64_t)s->tokens_per_seq * (s->num_q_heads / s->num_kv_heads) > lbsr::kMaxColumns)
+    return fail(LBSR_E_UNSUPPORTED, "tokens_per_seq %d x group %d > %d", s->tokens_per_seq,
+                s->num_q_heads / s->num_kv_heads, lbsr::kMaxColumns);
   if (s->reserved != 0) return fail(LBSR_E_INVALID, "shape.reserved must be 0");
   if (s->kv_dtype != LBSR_KV_BF16 && s->kv_dtype != LBSR_KV_FP8_E4M3)
     return fail(LBSR_E_INVALID, "kv_dtype %d unknown", s->kv_dtype);
@@ -186,6 +186,16 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
     cmax = W;
   }
   if (W > (1 << 22)) return fail(LBSR_E_UNSUPPORTED, "%lld workers is too many", (long long)W);
+  {
+    // the merge stages (chunks of one sequence) x (columns of a KV head) weights in LDS
+    const int64_t per_seq = cfg->sched == LBSR_SCHED_DYNAMIC ? P : S;
+    const int64_t rows = per_seq < shape->max_blocks_per_seq ? per_seq : shape->max_blocks_per_seq;
+    const int64_t cols = (int64_t)shape->tokens_per_seq * (shape->num_q_heads / shape->num_kv_heads);
+    if (rows * cols * 4 > lbsr::kMergeLdsBytes)
+      return fail(LBSR_E_UNSUPPORTED,
+                  "%lld chunks per sequence x %lld columns exceed the merge's %d-byte LDS stage",
+                  (long long)rows, (long long)cols, lbsr::kMergeLdsBytes);
+  }
   const int64_t Hq = shape->num_q_heads;
   const int64_t Tq = shape->tokens_per_seq;
   size_t off = 0;

@@ -16,7 +16,8 @@
 //     new token j, so the 8 heads of the pages' model fill 8 of the 16
 //     columns in a one-token step and all 16 with two new tokens per
 //     sequence (multi-token decode) at no extra KV traffic; unused columns
-//     are zero.  4 token blocks x 4 channel steps.
+//     are zero.  More than 16 columns (up to 64) are split into blocks of
+//     16, each run by its own wave.  4 token blocks x 4 channel steps.
 //   * O^T[128][16] += V^T[128][64] . P^T[64][16]: 8 channel blocks x 2 token
 //     steps.  The score accumulator's lane layout is reused as the P^T operand
 //     without moving data: the V page layout orders tokens to match it.
@@ -281,16 +282,22 @@ __device__ __forceinline__ void split_worker(
   if (c_begin >= c_end) return;
 
   const int lane = threadIdx.x & 63;
-  const int col = lane & 15;  // matrix column = (new token, q head inside the group)
+  const int col = lane & 15;  // matrix column inside the wave's block of 16
   const int kc = lane >> 4;   // which 8-element slice of the contraction this lane feeds
   const int nwaves = blockDim.x >> 6;
   const int Hq = geo.num_q_heads, G = geo.group, T = geo.tokens;
-  const int GT = G * T;                      // columns in use
-  const int tok = col < GT ? col / G : 0;    // this column's new token
-  const int hl = col - tok * G;              // and its head inside the group
-  const int lag = T - 1 - tok;               // it attends rows < L - lag
+  const int GT = G * T;              // columns of one KV head: (new token, q head) pairs
+  const int ncb = (GT + 15) >> 4;    // blocks of 16 columns per KV head
 
-  for (int g = threadIdx.x >> 6; g < geo.num_kv_heads; g += nwaves) {
+  // A wave runs one (KV head, column block) at a time.  With several blocks
+  // per head, the waves of one head are neighbours and read the same tiles
+  // at about the same time (in lockstep), so the repeats come from L2.
+  for (int vg = threadIdx.x >> 6; vg < geo.num_kv_heads * ncb; vg += nwaves) {
+    const int g = vg / ncb;
+    const int gc = (vg - g * ncb) * 16 + col;   // this lane's column among the head's GT
+    const int tok = gc < GT ? gc / G : 0;       // its new token
+    const int hl = gc - tok * G;                // and its head inside the group
+    const int lag = T - 1 - tok;                // it attends rows < L - lag
     for (int c = c_begin; c < c_end; ++c) {
       const int32_t* ch = plan.chunks + 4 * (size_t)c;
       const int b = wave_uniform(ch[0]);
@@ -303,7 +310,7 @@ __device__ __forceinline__ void split_worker(
       // Q^T operand: column col = q head g*G + hl of new token tok (zero past
       // the G*Tq columns in use), channels 32*s + 8*kc .. +8 for step s.
       bf16x8 qB[4];
-      if (col < GT) {
+      if (gc < GT) {
         const u32x4* qp =
             (const u32x4*)(q_out + (((size_t)b * T + tok) * Hq + (size_t)g * G + hl) * kHeadDim) +
             kc;
@@ -353,7 +360,7 @@ __device__ __forceinline__ void split_worker(
       const float l = sum_xor32(sum_xor16(lsum));
       const float scale = l > 0.f ? out_scale / l : 0.f;
       const float lse2 = l > 0.f ? m + __builtin_amdgcn_logf(l) : -__builtin_inff();  // log2
-      if (col < GT) {
+      if (gc < GT) {
         const size_t orow = ((size_t)b * T + tok) * Hq + (size_t)g * G + hl;  // out / lse_out row
         if (single && out_fp8) {
           // E4M3 codes of o / out_scale (folded into scale): 4 bytes per db
@@ -380,11 +387,11 @@ __device__ __forceinline__ void split_worker(
           // contiguous for the merge; chunk c's rows are Hq*Tq long
           const size_t HqT = (size_t)Hq * T;
           float* po = plan.partial_o + ((size_t)c * HqT + (size_t)g * GT) * kHeadDim +
-                      col * 8 + 4 * (kc & 1);
+                      gc * 8 + 4 * (kc & 1);
 #pragma unroll
           for (int db = 0; db < 8; ++db)
             *(f32x4*)(po + (2 * db + (kc >> 1)) * 8 * GT) = O[db] * scale;
-          if (kc == 0) plan.partial_lse[(size_t)c * HqT + (size_t)g * GT + col] = lse2;
+          if (kc == 0) plan.partial_lse[(size_t)c * HqT + (size_t)g * GT + gc] = lse2;
         }
       }
     }
@@ -496,7 +503,9 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
   const bool active = r_sub_raw < rows_per_inst;
   const int r_sub = active ? r_sub_raw : 0;
   const int e = active ? lane - r_sub_raw * per_row : 0;   // float4 inside the piece
-  const int hh = (e % (2 * G)) >> 1;                       // head of that float4
+  // a row is [16 slices of 8 channels][G columns][2 float4]; float4 f of the
+  // row (f = slice * per_row + e) holds column (f % 2G) / 2
+  const int hh = ((slice * per_row + e) % (2 * G)) >> 1;
   const f32x4* po = (const f32x4*)plan.partial_o + head0 * 32 + slice * per_row + e;
   const int rows_per_round = kMergeWaves * rows_per_inst * kMergeUnroll;
   auto row_of = [&](int base, int u) { return base + (u * kMergeWaves + wave) * rows_per_inst + r_sub; };
@@ -565,10 +574,12 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < kMergeWaves; ++w)
       for (int r = 0; r < rows_per_inst; ++r) sum += s_acc[w * kWave + r * per_row + t];
-    // float4 t of the piece: 8-channel slice slice*(16/S) + t/(2G), head (t%2G)/2
-    const int bs = slice * (16 / nslices) + t / (2 * G);
-    const int h3 = (t % (2 * G)) >> 1;
-    const int d = bs * 8 + (t & 1) * 4;
+    // float4 f = slice * per_row + t of the row: 8-channel slice f / 2G,
+    // column (f % 2G) / 2, channels 4 * (f % 2) ..
+    const int f = slice * per_row + t;
+    const int bs = f / (2 * G);
+    const int h3 = (f % (2 * G)) >> 1;
+    const int d = bs * 8 + (f & 1) * 4;
     if (out_fp8) {
       *(uint32_t*)((uint8_t*)out + out_row(h3) * kHeadDim + d) =
           f32x4_to_e4m3x4(sum[0], sum[1], sum[2], sum[3]);
@@ -586,9 +597,11 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, i
                                   const int32_t* block_table, const PlanPtrs& plan, void* out,
                                   float* lse_out, float score_scale_log2, float out_scale,
                                   int64_t* trace, hipStream_t stream) {
-  const int waves = geo.num_kv_heads < kMaxAttnWaves ? geo.num_kv_heads : kMaxAttnWaves;
-  // lockstep only when every wave gets the same number of KV heads
-  const bool sync = geo.num_kv_heads % waves == 0;
+  // one wave per (KV head, 16-column block), at most 8
+  const int virt = geo.num_kv_heads * ((geo.group * geo.tokens + 15) / 16);
+  const int waves = virt < kMaxAttnWaves ? virt : kMaxAttnWaves;
+  // lockstep only when every wave gets the same number of them
+  const bool sync = virt % waves == 0;
   auto launch = [&](auto kernel) {
     kernel<<<num_workers, waves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
@@ -608,7 +621,7 @@ hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, 
                           int max_chunks_per_seq, bool out_fp8, bool fold_token_status,
                           hipStream_t stream) {
   // S slices: a power of two dividing 32 with 32G/S <= 64 float4 per row
-  // slice, G = group * Tq columns per (chunk, KV group)
+  // slice, G = group * Tq columns per (chunk, KV group), at most 64
   const int cols = geo.group * geo.tokens;
   int slices = LBSR_MERGE_MIN_SLICES;
   while (slices < 32 && 32 * cols / slices > kWave) slices *= 2;

@@ -15,6 +15,7 @@ head dim 128; 64-token pages):
 * ``loguniform``  batch 64, lengths log-uniform in [512, 262144], FP8 E4M3
 * ``mix_mtp2``    the BF16 mix with 2 new tokens per sequence (multi-token
                   decode, as when one drafted token is verified)
+* ``mix_mtp4``    the same with 4 new tokens per sequence (three drafted)
 
 Recipe (per workload, seed s): ``numpy.random.SeedSequence(s)`` spawns child
 streams, in order: 0 lengths, 1 q, 2 k, 3 v, 4 q-norm weight, 5 k-norm weight,
@@ -87,11 +88,13 @@ def named(name):
                         k_scale=2.0 ** -5, v_scale=2.0 ** -4, seed=5)
     if name == "mix_mtp2":
         return Workload("mix_mtp2", [131072] + [4096] * 31, seed=6, tokens=2)
+    if name == "mix_mtp4":
+        return Workload("mix_mtp4", [131072] + [4096] * 31, seed=7, tokens=4)
     raise KeyError(name)
 
 
 NAMES = ("tiny", "uniform", "mix", "mix_fp8", "loguniform")
-MULTI_TOKEN_NAMES = ("mix_mtp2",)
+MULTI_TOKEN_NAMES = ("mix_mtp2", "mix_mtp4")
 
 
 def _bf16(x):

@@ -181,17 +181,21 @@ def test_shape_struct_matches_header():
     assert B.Shape.tokens_per_seq.offset == 24 and B.Shape.num_pages.offset == 32
 
 
-@pytest.mark.parametrize("Hq,Hkv,tokens,reserved,status", [
-    (64, 8, 1, 0, B.OK), (64, 8, 2, 0, B.OK), (16, 4, 4, 0, B.OK), (8, 8, 16, 0, B.OK),
-    (64, 8, 0, 0, B.E_INVALID), (64, 8, -1, 0, B.E_INVALID),
-    (64, 8, 3, 0, B.E_UNSUPPORTED),          # 8 heads x 3 tokens > 16 columns
-    (8, 8, 17, 0, B.E_UNSUPPORTED),
-    (64, 8, 1, 5, B.E_INVALID),
+@pytest.mark.parametrize("Hq,Hkv,tokens,reserved,workers,status", [
+    (64, 8, 1, 0, 256, B.OK), (64, 8, 2, 0, 256, B.OK), (16, 4, 4, 0, 256, B.OK),
+    (8, 8, 16, 0, 256, B.OK), (64, 8, 3, 0, 256, B.OK), (64, 8, 8, 0, 256, B.OK),
+    (8, 8, 64, 0, 256, B.OK),
+    (64, 8, 0, 0, 256, B.E_INVALID), (64, 8, -1, 0, 256, B.E_INVALID),
+    (64, 8, 9, 0, 256, B.E_UNSUPPORTED),          # 8 heads x 9 tokens > 64 columns
+    (8, 8, 65, 0, 256, B.E_UNSUPPORTED),
+    (64, 8, 4, 0, 1024, B.E_UNSUPPORTED),         # 1024 chunks x 32 columns > the merge's LDS
+    (64, 8, 2, 0, 1024, B.OK),                    # 1024 x 16 x 4 B = 64 KiB: fits
+    (64, 8, 1, 5, 256, B.E_INVALID),
 ])
-def test_tokens_per_seq_validation(lib, Hq, Hkv, tokens, reserved, status):
+def test_tokens_per_seq_validation(lib, Hq, Hkv, tokens, reserved, workers, status):
     s = DecodeConfig(Hq, Hkv, "bf16", 2048, 4300, tokens_per_seq=tokens).shape()
     s.reserved = reserved
-    c = Schedule("dynamic", num_workers=256).cfg()
+    c = Schedule("dynamic", num_workers=workers).cfg()
     out = B.WsLayout()
     got = lib.lbsr_workspace_layout(ctypes.byref(s), 32, ctypes.byref(c), ctypes.byref(out))
     assert got == status, lib.lbsr_last_error()

@@ -99,6 +99,11 @@ MULTI = [
     dict(seq_lens=[16, 64 * 9 + 1], num_q_heads=8, num_kv_heads=8, tokens=16),   # group 1
     dict(seq_lens=[300, 65], num_q_heads=32, num_kv_heads=4, tokens=2, norm_before_rope=True,
          kv_dtype="fp8"),
+    # more than 16 columns per KV head: blocks of 16 on neighbouring waves
+    dict(seq_lens=[5, 66, 1000, 131], num_q_heads=64, num_kv_heads=8, tokens=4),        # 32
+    dict(seq_lens=[3, 700, 64 * 3 + 2], num_q_heads=8, num_kv_heads=1, tokens=3),       # 24
+    dict(seq_lens=[8, 520, 2000], num_q_heads=16, num_kv_heads=2, tokens=8, kv_dtype="fp8"),  # 64
+    dict(seq_lens=[40, 300], num_q_heads=12, num_kv_heads=4, tokens=11),               # 33
 ]
 MULTI_SCHEDS = [lb.Schedule("dynamic", num_workers=1), lb.Schedule("dynamic", num_workers=7),
                 lb.Schedule("dynamic", num_workers=256), lb.Schedule("static", num_workers=256),
