@@ -293,6 +293,41 @@ lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
                              size_t ws_bytes, void *out, float *lse_out, void *stream);
 
 /*
+ * Prefill / chunked-prefill attention ([B] "Why is this good?": the backend
+ * is reported on prefill and mixed batches too).  shape->tokens_per_seq = Tq
+ * new tokens per sequence, any count up to 2^18 (the decode path's G * Tq <=
+ * 64 does not apply); new token t of sequence b (position L_b - Tq + t, its k
+ * and v already in the cache) attends rows [0, L_b - Tq + t]:
+ *   out[b][t][h]     = sum_j softmax_j(sm_scale * <q_out[b][t][h], K_j>) V_j
+ *   lse_out[b][t][h] = ln sum_j exp(sm_scale * <q_out[b][t][h], K_j>)
+ * One pass per (sequence, KV head, block of 128/G new tokens) over its causal
+ * range, each K/V tile read once per block: no schedule, no workspace.
+ *   q_out [batch][Tq][Hq][128] BF16        seq_lens [batch] int32 (device)
+ *   out   [batch][Tq][Hq][128] BF16, or E4M3 codes (params->out_dtype)
+ *   lse_out nullable float[batch][Tq][Hq]  error_word nullable int32*
+ * A length outside [Tq, max_blocks*64] is clamped (LBSR_DEV_ERR_SEQ_LEN); a
+ * page outside [0, num_pages) reads page 0 (LBSR_DEV_ERR_PAGE).
+ */
+lbsr_status lbsr_prefill_attention(const lbsr_shape *shape, const lbsr_params *params,
+                                   int32_t batch, const void *q_out, const void *k_cache,
+                                   const void *v_cache, const int32_t *block_table,
+                                   const int32_t *seq_lens, void *out, float *lse_out,
+                                   int32_t *error_word, void *stream);
+
+/*
+ * A prefill step: lbsr_rope_norm_kv_write on the Tq new tokens of every
+ * sequence (positions[b][t] = seq_lens[b] - Tq + t), then
+ * lbsr_prefill_attention, on one stream.  Arguments as for those two calls.
+ */
+lbsr_status lbsr_prefill_step(const lbsr_shape *shape, const lbsr_params *params,
+                              int32_t batch, const void *q, const void *k, const void *v,
+                              const int32_t *positions, const int32_t *seq_lens,
+                              const void *q_norm_w, const void *k_norm_w,
+                              const int32_t *block_table, void *k_cache, void *v_cache,
+                              void *q_out, void *out, float *lse_out, int32_t *error_word,
+                              void *stream);
+
+/*
  * Benchmark helper: lbsr_decode_step with a HIP event recorded on `stream`
  * around each of its three launches (schedule + prologue, split attention,
  * merge, in that order); waits for the stream and writes the three durations

@@ -33,7 +33,8 @@ DEV_ERR_SEQ_LEN, DEV_ERR_PAGE, DEV_ERR_POSITION = 1, 2, 4
 EXPORTS = (
     "lbsr_abi_version", "lbsr_status_string", "lbsr_last_error", "lbsr_device_workers",
     "lbsr_workspace_layout", "lbsr_workspace_size", "lbsr_rope_norm_kv_write", "lbsr_plan",
-    "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed",
+    "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed", "lbsr_prefill_attention",
+    "lbsr_prefill_step",
 )
 
 
@@ -110,6 +111,10 @@ def _declare(lib):
         "lbsr_decode_step": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                              + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t, _P,
                                             _P, _P]),
+        "lbsr_prefill_attention": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
+                                   + [_P] * 9),
+        "lbsr_prefill_step": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
+                              + [_P] * 15),
         "lbsr_decode_step_timed": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                                    + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t,
                                                   _P, _P, _P, ctypes.POINTER(ctypes.c_float), _P]),

@@ -94,9 +94,9 @@ lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
   if (s->num_q_heads > 4096) return fail(LBSR_E_UNSUPPORTED, "Hq %d > 4096", s->num_q_heads);
   if (s->tokens_per_seq < 1)
     return fail(LBSR_E_INVALID, "tokens_per_seq %d < 1", s->tokens_per_seq);
-  if ((int64_t)s->tokens_per_seq * (s->num_q_heads / s->num_kv_heads) > lbsr::kMaxColumns)
-    return fail(LBSR_E_UNSUPPORTED, "tokens_per_seq %d x group %d > %d", s->tokens_per_seq,
-                s->num_q_heads / s->num_kv_heads, lbsr::kMaxColumns);
+  if (s->tokens_per_seq > lbsr::kMaxTokensPerSeq)
+    return fail(LBSR_E_UNSUPPORTED, "tokens_per_seq %d > %d", s->tokens_per_seq,
+                lbsr::kMaxTokensPerSeq);
   if (s->reserved != 0) return fail(LBSR_E_INVALID, "shape.reserved must be 0");
   if (s->kv_dtype != LBSR_KV_BF16 && s->kv_dtype != LBSR_KV_FP8_E4M3)
     return fail(LBSR_E_INVALID, "kv_dtype %d unknown", s->kv_dtype);
@@ -115,6 +115,10 @@ lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
   if (!page_major && !head_major)
     return fail(LBSR_E_INVALID, "page_stride/head_stride make tiles overlap");
   if (batch < 1) return fail(LBSR_E_INVALID, "batch %d < 1", batch);
+  // the prologue runs one wave per (new token, row): the count must fit an int
+  if ((int64_t)batch * s->tokens_per_seq * (s->num_q_heads + 2 * s->num_kv_heads) > INT32_MAX / 2)
+    return fail(LBSR_E_UNSUPPORTED, "batch %d x tokens_per_seq %d is too many rows", batch,
+                s->tokens_per_seq);
   if (batch > lbsr::kMaxBatch)
     return fail(LBSR_E_UNSUPPORTED, "batch %d > %d", batch, lbsr::kMaxBatch);
   if ((int64_t)batch * s->max_blocks_per_seq > INT32_MAX)
@@ -145,9 +149,19 @@ lbsr_status check_params(const lbsr_params* p, int32_t kv_dtype) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The decode attention path (split + merge) holds one KV head's (new token,
+// q head) columns in at most 4 matrix-core column blocks.
+lbsr_status check_columns(const lbsr_shape* s) {
+  if ((int64_t)s->tokens_per_seq * (s->num_q_heads / s->num_kv_heads) > lbsr::kMaxColumns)
+    return fail(LBSR_E_UNSUPPORTED, "tokens_per_seq %d x group %d > %d (use the prefill path)",
+                s->tokens_per_seq, s->num_q_heads / s->num_kv_heads, lbsr::kMaxColumns);
+  return LBSR_OK;
+}
+
 lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sched_cfg* cfg,
                            lbsr_ws_layout* out) {
   LBSR_CHECK(check_shape(shape, batch));
+  LBSR_CHECK(check_columns(shape));
   if (!cfg) return fail(LBSR_E_INVALID, "cfg is NULL");
   if (!out) return fail(LBSR_E_INVALID, "out is NULL");
   if (cfg->sched != LBSR_SCHED_DYNAMIC && cfg->sched != LBSR_SCHED_STATIC)
@@ -394,6 +408,42 @@ lbsr_status run_combine(const lbsr_shape* shape, const lbsr_params* params, int3
                     "merge launch");
 }
 
+lbsr_status run_prefill(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                        const void* q_out, const void* kc, const void* vc, const int32_t* bt,
+                        const int32_t* seq_lens, void* out, float* lse_out, int32_t* error_word,
+                        hipStream_t stream) {
+  const lbsr::Geometry geo = geometry(shape, batch);
+  const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
+  const bool out_fp8 = params->out_dtype == LBSR_OUT_FP8_E4M3;
+  const double vs = fp8 ? (double)params->v_scale : 1.0;
+  const float o_scale = (float)(out_fp8 ? vs / (double)params->out_scale : vs);
+  return hip_status(lbsr::launch_prefill(geo, fp8, out_fp8, q_out, kc, vc, bt, seq_lens, out,
+                                         lse_out, score_scale_log2(params, shape->kv_dtype),
+                                         o_scale, error_word, stream),
+                    "prefill launch");
+}
+
+lbsr_status validate_prefill(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                             const void* q_out, const void* kc, const void* vc, const int32_t* bt,
+                             const int32_t* seq_lens, void* out, const float* lse_out,
+                             const int32_t* error_word) {
+  LBSR_CHECK(check_shape(shape, batch));
+  LBSR_CHECK(check_params(params, shape->kv_dtype));
+  LBSR_CHECK(check_ptr(q_out, 16, "q_out"));
+  LBSR_CHECK(check_ptr(kc, 16, "k_cache"));
+  LBSR_CHECK(check_ptr(vc, 16, "v_cache"));
+  LBSR_CHECK(check_ptr(bt, 4, "block_table"));
+  LBSR_CHECK(check_ptr(seq_lens, 4, "seq_lens"));
+  LBSR_CHECK(check_ptr(out, 16, "out"));
+  if (lse_out && !aligned(lse_out, 4)) return fail(LBSR_E_INVALID, "lse_out misaligned");
+  if (error_word && !aligned(error_word, 4)) return fail(LBSR_E_INVALID, "error_word misaligned");
+  // one workgroup per (block of new tokens, sequence, KV head)
+  const int64_t per = 128 / (shape->num_q_heads / shape->num_kv_heads);
+  const int64_t grid = (shape->tokens_per_seq + per - 1) / per * batch * shape->num_kv_heads;
+  if (grid > INT32_MAX) return fail(LBSR_E_UNSUPPORTED, "prefill grid of %lld workgroups", (long long)grid);
+  return LBSR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -539,6 +589,41 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
     for (int i = 0; i < 4; ++i) (void)hipEventDestroy(ev[i]);
   }
   return st;
+}
+
+lbsr_status lbsr_prefill_attention(const lbsr_shape* shape, const lbsr_params* params,
+                                   int32_t batch, const void* q_out, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, void* out, float* lse_out,
+                                   int32_t* error_word, void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(validate_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table,
+                              seq_lens, out, lse_out, error_word));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  return run_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table, seq_lens, out,
+                     lse_out, error_word, (hipStream_t)stream);
+}
+
+lbsr_status lbsr_prefill_step(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
+                              const void* q, const void* k, const void* v,
+                              const int32_t* positions, const int32_t* seq_lens,
+                              const void* q_norm_w, const void* k_norm_w,
+                              const int32_t* block_table, void* k_cache, void* v_cache,
+                              void* q_out, void* out, float* lse_out, int32_t* error_word,
+                              void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(validate_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
+                               block_table, k_cache, v_cache, q_out, error_word));
+  LBSR_CHECK(validate_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table,
+                              seq_lens, out, lse_out, error_word));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  const hipStream_t s = (hipStream_t)stream;
+  LBSR_CHECK(run_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
+                          block_table, k_cache, v_cache, q_out, error_word, s));
+  return run_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table, seq_lens, out,
+                     lse_out, error_word, s);
 }
 
 lbsr_status lbsr_decode_step(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,

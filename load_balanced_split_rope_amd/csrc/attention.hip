@@ -32,27 +32,9 @@
 
 #include "common.h"
 #include "launch.h"
+#include "tile_math.h"
 
 namespace lbsr {
-
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-// 8 E4M3 codes (two dwords) -> 8 BF16 values, exactly.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool kFp8>
 struct TileRegs {
@@ -71,41 +53,6 @@ __device__ __forceinline__ void load_frags(u32x4 (&dst)[TileRegs<kFp8>::kFrags],
   for (int f = 0; f < TileRegs<kFp8>::kFrags; ++f)
     dst[f] = __builtin_nontemporal_load(tile + f * kWave + lane);
 }
-
-// Page id of tile t, validated without branching: a bad id reads page 0 and
-// sets `bad` (reported once per chunk).
-__device__ __forceinline__ int fetch_page(const int32_t* __restrict__ row, int t, int64_t num_pages,
-                                          bool& bad) {
-  const int p = wave_uniform(row[t]);
-  const bool ok = p >= 0 && p < num_pages;
-  bad |= !ok;
-  return ok ? p : 0;
-}
-
-// Pairwise max / sum with lane l ^ 16 and lane l ^ 32 (VALU lane swaps, no LDS).
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Online-softmax state of one (chunk, KV head) pass.
-struct SoftmaxState {
-  f32x4 O[8];   // O^T: lane holds channels 16*db + 4*kc + e of column col
-  float m;      // running max (log2 domain), uniform over the 4 lanes of a column
-  float lsum;   // this lane's share of the running sum
-};
 
 // One 64-token tile: scores, online softmax update, P.V.  `rem` = rows of the
 // tile before the sequence end (1..64); the lane's column attends rows below
@@ -150,74 +97,20 @@ __device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
     S[tb] = acc;
   }
 
-  // ---- online softmax (log2 domain) ----
-  float p[16];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[4 * tb + e] = S[tb][e] * score_scale_log2;
-  if (rem - tail < kPage) {   // some column's last row falls in this tile
-    const int lim = rem - lag;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (16 * tb + 4 * kc + e >= lim) p[4 * tb + e] = -__builtin_inff();
-  }
-  float mx = p[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, p[i]);
-  mx = max_xor32(max_xor16(mx));
-  const float m_new = fmaxf(st.m, mx);
-  // With several new tokens a column can have no row yet (its limit lies
-  // before this chunk's rows so far): its max stays -inf, and 0 serves as
-  // the exponent base so that alpha and p come out 0 instead of NaN.
-  const float m_base = m_new == -__builtin_inff() ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_base);
-  float psum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    p[i] = fast_exp2(p[i] - m_base);
-    psum += p[i];
-  }
-  st.lsum = st.lsum * alpha + psum;
-  st.m = m_new;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.O[i] *= alpha;
-  // P^T operand for token step s: elements e<4 from token block 2s, e>=4 from 2s+1
+  // ---- online softmax (log2 domain); some column's last row may fall in this tile ----
   bf16x8 pB[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)p[8 * s + e];
+  softmax_tile(S, st, rem - tail < kPage, rem - lag, kc, score_scale_log2, pB);
 
   // ---- rows past the sequence end hold anything (even NaN): zero their V ----
   if (rem < kPage) {
+    uint32_t keep[2][4];
+    v_keep_masks<kFp8>(rem, kc, keep);
     if constexpr (kFp8) {
-      // dword j of a lane holds tokens 16*j + 4*kc + (0..3), one per byte
-      uint32_t keep[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t mk = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * j + 4 * kc + i < rem) mk |= 0xFFu << (8 * i);
-        keep[j] = mk;
-      }
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) R.v[f][j] &= keep[j];
+        for (int j = 0; j < 4; ++j) R.v[f][j] &= keep[0][j];
     } else {
-      // fragment 2*db + s, dword j holds tokens 16*(2s + j/2) + 4*kc + 2*(j%2) + (0,1)
-      uint32_t keep[2][4];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t0k = 16 * (2 * s + (j >> 1)) + 4 * kc + 2 * (j & 1);
-          keep[s][j] = (t0k < rem ? 0xFFFFu : 0u) | (t0k + 1 < rem ? 0xFFFF0000u : 0u);
-        }
 #pragma unroll
       for (int db = 0; db < 8; ++db)
 #pragma unroll

@@ -12,6 +12,7 @@ constexpr int kTileElems = kHeadDim * kPage;
 constexpr int kWave = 64;
 constexpr int kMaxGroup = 16;      // q heads per KV head that one matrix-core column block holds
 constexpr int kMaxColumns = 64;    // (new token, q head) pairs per KV head: 4 column blocks
+constexpr int kMaxTokensPerSeq = 1 << 18;  // new tokens per sequence (prefill)
 constexpr int kMergeLdsBytes = 65536;  // the merge stages chunks x columns weights in LDS
 constexpr int kMaxBatch = 16384;   // the plan keeps per-sequence prefix sums in LDS
 constexpr int kPlanThreads = 1024;

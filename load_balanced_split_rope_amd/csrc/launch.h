@@ -31,6 +31,12 @@ hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, 
                           int max_chunks_per_seq, bool out_fp8, bool fold_token_status,
                           hipStream_t stream);
 
+hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const void* q_out,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, void* out, float* lse_out,
+                          float score_scale_log2, float out_scale, int32_t* error_word,
+                          hipStream_t stream);
+
 hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 const PlanPtrs& plan, const Geometry& geo,
                                 bool fp8, const void* q, const void* k, const void* v,

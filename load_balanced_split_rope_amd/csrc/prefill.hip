@@ -1,0 +1,230 @@
+// Prefill and chunked-prefill attention: many new tokens per sequence.
+//
+// [B] "Why is this good?" reports the backend on prefill and mixed batches as
+// well as decode.  The step's new tokens (Tq per sequence, token j at position
+// L - Tq + j, its k and v already written by the prologue) attend causally:
+// token j sees rows [0, L - Tq + j].  With a prefix in the cache this is
+// chunked prefill; with L = Tq it is a plain prefill.
+//
+// Mapping on CDNA4:
+//   * workgroup = (sequence b, KV head g, block of 128 (token, head) columns,
+//     i.e. 128/G consecutive new tokens with all G q heads of the group);
+//     8 waves of 16 columns, the same matrix-core shapes as the decode split
+//     kernel (S^T = K.Q^T, O^T += V^T.P^T on v_mfma_f32_16x16x32_bf16).
+//   * the block's causal range [0, L - Tq + last token] is walked tile by
+//     tile; each K/V tile is read from HBM once per workgroup, straight into
+//     LDS in its fragment order (the page layout already is the operand
+//     order), double-buffered: every thread loads its share of tile t+1
+//     into registers while the waves compute on tile t from LDS, then writes
+//     it to the other buffer before the workgroup barrier.
+//   * one online-softmax pass per column over the whole range, so the result
+//     goes straight to the output: no partials, no merge.
+//   * workgroups are numbered longest-first (the blocks of the last tokens
+//     see the most rows), so the dispatcher starts the long ones first.
+
+#include "launch.h"
+#include "tile_math.h"
+
+namespace lbsr {
+
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillColumns = kPrefillWaves * 16;   // 128 (token, head) columns per workgroup
+
+template <bool kFp8>
+__global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
+    Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, void* __restrict__ out, float* __restrict__ lse_out,
+    float score_scale_log2, float out_scale, int out_fp8, int32_t* __restrict__ error_word,
+    int num_blocks_q) {
+  constexpr int NF = kFp8 ? 8 : 16;                  // 1 KiB fragments per K (or V) tile
+  constexpr int kStage = 2 * NF * kWave;             // u32x4 per stage: K then V
+  constexpr int kPerThread = kStage / (kPrefillWaves * kWave);   // 4 (BF16) or 2 (FP8)
+  constexpr int kElemBytes = kFp8 ? 1 : 2;
+  __shared__ u32x4 s_kv[2][kStage];                  // 64 KiB (BF16) / 32 KiB (FP8)
+
+  const int T = geo.tokens, G = geo.group, Hq = geo.num_q_heads;
+  const int per_block = geo.batch * geo.num_kv_heads;
+  const int qb = num_blocks_q - 1 - (int)(blockIdx.x / per_block);   // last blocks first
+  const int bg = (int)(blockIdx.x % per_block);
+  const int b = bg / geo.num_kv_heads, g = bg - b * geo.num_kv_heads;
+  const int tokens_per_block = kPrefillColumns / G;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kc = lane >> 4;
+
+  // length: at least the new tokens, at most the block table's reach
+  const int max_len = geo.max_blocks * kPage;
+  const int L_in = seq_lens[b];
+  const int L = L_in < T ? T : (L_in > max_len ? max_len : L_in);
+  const int tok0 = qb * tokens_per_block;
+  const int tok_end = tok0 + tokens_per_block < T ? tok0 + tokens_per_block : T;
+  const int limit_last = L - T + tok_end;           // rows the block's last token attends
+  const int limit_first = L - T + tok0 + 1;         // and its first
+  const int ntiles = (limit_last + kPage - 1) / kPage;
+
+  // this lane's column: token tok0 + j, head hl of group g
+  const int gc = wave * 16 + col;
+  const int j = gc / G, hl = gc - j * G;
+  const int jt = tok0 + j;
+  const bool valid = gc < tokens_per_block * G && jt < T;
+  const int limit = L - T + jt + 1;                 // this column attends rows < limit
+
+  bf16x8 qB[4];
+  if (valid) {
+    const u32x4* qp =
+        (const u32x4*)(q_out + (((size_t)b * T + jt) * Hq + (size_t)g * G + hl) * kHeadDim) + kc;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(qp[4 * s]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+
+  const int32_t* bt_row = block_table + (size_t)b * geo.max_blocks;
+  bool bad_page = false;
+  auto load_tile = [&](int t, u32x4 (&dst)[kPerThread]) {
+    const int p = bt_row[t];
+    const bool ok = p >= 0 && p < geo.num_pages;
+    bad_page |= !ok;
+    const size_t base = ((size_t)(ok ? p : 0) * geo.page_stride + (size_t)g * geo.head_stride) *
+                        kElemBytes;
+    const u32x4* kt = (const u32x4*)(k_pool + base);
+    const u32x4* vt = (const u32x4*)(v_pool + base);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int q = tid + i * kPrefillWaves * kWave;          // slot in the stage
+      const u32x4* src = q < NF * kWave ? kt + q : vt + (q - NF * kWave);
+      dst[i] = __builtin_nontemporal_load(src);
+    }
+  };
+  auto store_tile = [&](int stage, const u32x4 (&src)[kPerThread]) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) s_kv[stage][tid + i * kPrefillWaves * kWave] = src[i];
+  };
+
+  SoftmaxState st;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -__builtin_inff();
+  st.lsum = 0.f;
+
+  u32x4 pre[kPerThread];
+  load_tile(0, pre);
+  store_tile(0, pre);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, pre);
+    const u32x4* kf = s_kv[stage];
+    const u32x4* vf = s_kv[stage] + NF * kWave;
+
+    // ---- scores ----
+    f32x4 S[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 a;
+        if constexpr (kFp8) {
+          const u32x4 w = kf[(2 * tb + (s >> 1)) * kWave + lane];
+          a = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+        } else {
+          a = as_bf16x8(kf[(4 * tb + s) * kWave + lane]);
+        }
+        acc = mfma_bf16(a, qB[s], acc);
+      }
+      S[tb] = acc;
+    }
+
+    // ---- online softmax: columns' limits fall in this tile or earlier ----
+    bf16x8 pB[2];
+    const int row0 = t * kPage;
+    softmax_tile(S, st, limit_first - row0 < kPage, limit - row0, kc, score_scale_log2, pB);
+
+    // ---- P.V, with rows at or past the sequence end zeroed in the last tile ----
+    const int rem = L - row0;
+    uint32_t keep[2][4];
+    const bool tail = rem < kPage;
+    if (tail) v_keep_masks<kFp8>(rem, kc, keep);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 a;
+        if constexpr (kFp8) {
+          u32x4 w = vf[db * kWave + lane];
+          if (tail) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) w[x] &= keep[0][x];
+          }
+          a = s ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+        } else {
+          u32x4 w = vf[(2 * db + s) * kWave + lane];
+          if (tail) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) w[x] &= keep[s][x];
+          }
+          a = as_bf16x8(w);
+        }
+        st.O[db] = mfma_bf16(a, pB[s], st.O[db]);
+      }
+    }
+    if (t + 1 < ntiles) store_tile(stage ^ 1, pre);
+    __syncthreads();
+  }
+  if (bad_page && error_word) atomicOr(error_word, (int32_t)kErrPage);
+
+  // ---- output ----
+  const float l = sum_xor32(sum_xor16(st.lsum));
+  const float scale = l > 0.f ? out_scale / l : 0.f;
+  if (valid) {
+    const size_t orow = ((size_t)b * T + jt) * Hq + (size_t)g * G + hl;
+    if (out_fp8) {
+      uint8_t* o = (uint8_t*)out + orow * kHeadDim + 4 * kc;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f32x4 x = st.O[db] * scale;
+        *(uint32_t*)(o + 16 * db) = f32x4_to_e4m3x4(x[0], x[1], x[2], x[3]);
+      }
+    } else {
+      uint16_t* o = (uint16_t*)out + orow * kHeadDim + 4 * kc;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(st.O[db][e] * scale);
+        *(bf16x4*)(o + 16 * db) = v4;
+      }
+    }
+    if (kc == 0 && lse_out)
+      lse_out[orow] = (l > 0.f ? st.m + __builtin_amdgcn_logf(l) : -__builtin_inff()) * kLn2;
+  }
+  if (tid == 0 && L != L_in && error_word && qb == 0 && g == 0) atomicOr(error_word, (int32_t)kErrSeqLen);
+}
+
+int prefill_blocks_q(const Geometry& geo) {
+  const int per = kPrefillColumns / geo.group;
+  return (geo.tokens + per - 1) / per;
+}
+
+hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const void* q_out,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, void* out, float* lse_out,
+                          float score_scale_log2, float out_scale, int32_t* error_word,
+                          hipStream_t stream) {
+  const int nqb = prefill_blocks_q(geo);
+  const size_t grid = (size_t)nqb * geo.batch * geo.num_kv_heads;
+  auto launch = [&](auto kernel) {
+    kernel<<<(unsigned)grid, kPrefillWaves * kWave, 0, stream>>>(
+        geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
+        block_table, seq_lens, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0,
+        error_word, nqb);
+  };
+  if (fp8) launch(prefill_kernel<true>);
+  else launch(prefill_kernel<false>);
+  return hipGetLastError();
+}
+
+}  // namespace lbsr

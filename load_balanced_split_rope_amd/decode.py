@@ -245,6 +245,57 @@ def decode_step_timed(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w,
     return list(ms)
 
 
+def prefill_attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, seq_lens, out,
+                      lse_out=None, error_word=None, stream=None):
+    """lbsr_prefill_attention: every new token (cfg.tokens_per_seq per sequence)
+    attends its causal prefix; no schedule or workspace."""
+    batch = q_out.shape[0]
+    Hq, D = cfg.num_q_heads, B.HEAD_DIM
+    _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(out, "out", cfg.out_torch_dtype, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, shape=cfg.tokens_shape(batch, Hq))
+    if error_word is not None:
+        _need(error_word, "error_word", torch.int32, numel=1)
+    _check_table(cfg, block_table, batch)
+    _check_pools(cfg, k_cache, v_cache)
+    s, p = cfg.shape(), cfg.params()
+    B._check(B.lib().lbsr_prefill_attention(
+        ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q_out), B._ptr(k_cache), B._ptr(v_cache),
+        B._ptr(block_table), B._ptr(seq_lens), B._ptr(out), B._ptr(lse_out), B._ptr(error_word),
+        B._stream(stream)))
+
+
+def prefill_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
+                 block_table, k_cache, v_cache, q_out, out, lse_out=None, error_word=None,
+                 stream=None):
+    """lbsr_prefill_step: the prologue on every new token, then prefill attention."""
+    batch = q.shape[0]
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, B.HEAD_DIM
+    _need(q, "q", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(k, "k", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=cfg.tokens_shape(batch, Hkv, D))
+    _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(out, "out", cfg.out_torch_dtype, shape=cfg.tokens_shape(batch, Hq, D))
+    _need(positions, "positions", torch.int32, shape=cfg.tokens_shape(batch))
+    _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+    _need(q_norm_w, "q_norm_w", torch.bfloat16, shape=(D,))
+    _need(k_norm_w, "k_norm_w", torch.bfloat16, shape=(D,))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, shape=cfg.tokens_shape(batch, Hq))
+    if error_word is not None:
+        _need(error_word, "error_word", torch.int32, numel=1)
+    _check_table(cfg, block_table, batch)
+    _check_pools(cfg, k_cache, v_cache)
+    s, p = cfg.shape(), cfg.params()
+    B._check(B.lib().lbsr_prefill_step(
+        ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
+        B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
+        B._ptr(block_table), B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out), B._ptr(out),
+        B._ptr(lse_out), B._ptr(error_word), B._stream(stream)))
+
+
 def read_plan(cfg: DecodeConfig, batch: int, sched: Schedule, workspace):
     """Copy the plan arrays out of a workspace (synchronises; for tests and tools)."""
     lay = workspace_layout(cfg, batch, sched)

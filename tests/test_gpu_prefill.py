@@ -1,0 +1,152 @@
+"""Prefill and chunked prefill (lbsr_prefill_step) against the fp64 oracle:
+every new token attends its causal prefix (R20's reading, with any number of
+new tokens).  q_out is bit-exact; outputs and lse to the R14 tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import multitoken as mt, attend_full, bf16_bits_to_f64
+from oracle.step import _sequence_kv
+import load_balanced_split_rope_amd as lb
+from load_balanced_split_rope_amd import workloads as wl
+from checks import (check_output, check_output_fp8, poison_cache, host_pools, host_step_inputs,
+                    oracle_cfg, to_f64, bits_u16)
+from gpu_util import device, to_device, config_for, run_step
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(w, g, cfg=None):
+    dev = g["q"].device
+    cfg = cfg or config_for(w, g)
+    q_out = torch.empty_like(g["q"])
+    out = torch.empty(g["q"].shape, dtype=cfg.out_torch_dtype, device=dev)
+    lse = torch.empty(cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    lb.prefill_step(cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"], g["q_norm_w"],
+                    g["k_norm_w"], g["block_table"], g["k_cache"], g["v_cache"], q_out, out,
+                    lse, err)
+    torch.cuda.synchronize()
+    return {"q_out": q_out, "out": out, "lse": lse, "error": int(err.item()), "cfg": cfg}
+
+
+def oracle_prefill(w, inp):
+    h = host_step_inputs(inp)
+    B, Tq, Hq = w.batch, w.tokens, w.num_q_heads
+    q = h["q"].reshape(B, Tq, Hq, 128)
+    k = h["k"].reshape(B, Tq, w.num_kv_heads, 128)
+    v = h["v"].reshape(B, Tq, w.num_kv_heads, 128)
+    pos = h["positions"].reshape(B, Tq)
+    pro = mt.prologue_tokens(q, k, v, pos, h["wq"], h["wk"], h["block_table"],
+                             theta=w.rope_theta, eps=w.rms_eps, kv_dtype=w.kv_dtype,
+                             k_scale=np.float32(w.k_scale).item(),
+                             v_scale=np.float32(w.v_scale).item(),
+                             norm_before_rope=w.norm_before_rope)
+    cfg = oracle_cfg(inp, w)
+    cfg["k_scale"], cfg["v_scale"] = np.float32(w.k_scale).item(), np.float32(w.v_scale).item()
+    q_out = pro["q_out"].reshape(B, Tq, Hq, 128)
+    ref = mt.decode_attention_tokens(q_out, host_pools(inp, w), pro, h["seq_lens"],
+                                     h["block_table"], cfg)
+    o = np.array([[[ref[(b, j, hh)][0] for hh in range(Hq)] for j in range(Tq)] for b in range(B)])
+    lse = np.array([[[ref[(b, j, hh)][1] for hh in range(Hq)] for j in range(Tq)]
+                    for b in range(B)])
+    return pro, o, lse
+
+
+CASES = [
+    dict(seq_lens=[100, 300], num_q_heads=64, num_kv_heads=8, tokens=100),        # prefill + chunk
+    dict(seq_lens=[37, 500, 1000], num_q_heads=64, num_kv_heads=8, tokens=37),    # partial block
+    dict(seq_lens=[300, 2000], num_q_heads=8, num_kv_heads=8, tokens=300),         # group 1
+    dict(seq_lens=[65, 129, 4096], num_q_heads=16, num_kv_heads=4, tokens=65, kv_dtype="fp8"),
+    dict(seq_lens=[50, 700], num_q_heads=32, num_kv_heads=2, tokens=50),           # group 16
+    dict(seq_lens=[90, 91], num_q_heads=12, num_kv_heads=4, tokens=90, norm_before_rope=True),
+    dict(seq_lens=[1, 64, 65], num_q_heads=8, num_kv_heads=1, tokens=1),           # one token
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_prefill_matches_oracle(case):
+    dev = device()
+    w = wl.custom(seed=800 + case, **CASES[case])
+    inp = wl.make_inputs(w)
+    poison_cache(inp, w)
+    print(f"prefill case {case}: lens {w.seq_lens} tokens {w.tokens} "
+          f"{w.num_q_heads}q/{w.num_kv_heads}kv {w.kv_dtype}", flush=True)
+    res = run_prefill(w, to_device(inp, dev))
+    assert res["error"] == 0
+    pro, ro, rl = oracle_prefill(w, inp)
+    assert np.array_equal(bits_u16(res["q_out"]).reshape(pro["q_out"].shape), pro["q_out"])
+    check_output(to_f64(res["out"]).reshape(ro.shape), ro, w.kv_dtype, "prefill output")
+    lse = to_f64(res["lse"]).reshape(rl.shape)
+    assert np.all(np.abs(lse - rl) <= 1e-4 + 1e-5 * np.abs(rl)), float(np.max(np.abs(lse - rl)))
+
+
+def test_prefill_agrees_with_decode_path():
+    """With few new tokens both paths apply; they agree to fp32 reassociation
+    (the decode path splits the KV range into chunks and merges them)."""
+    dev = device()
+    w = wl.custom([70, 4100, 700], num_q_heads=64, num_kv_heads=8, tokens=8, seed=820)
+    inp = wl.make_inputs(w)
+    rp = run_prefill(w, to_device(inp, dev))
+    rd = run_step(w, to_device(inp, dev), lb.Schedule("dynamic", num_workers=256))
+    assert torch.equal(rp["q_out"], rd["q_out"])
+    d = (rp["out"].float() - rd["out"].float()).abs().max().item()
+    assert d <= 2 ** -6, d
+    assert (rp["lse"] - rd["lse"]).abs().max().item() < 1e-4
+
+
+def test_prefill_fp8_output():
+    dev = device()
+    w = wl.custom([200, 333], num_q_heads=64, num_kv_heads=8, tokens=200, seed=830)
+    inp = wl.make_inputs(w)
+    g = to_device(inp, dev)
+    cfg = config_for(w, g)
+    cfg.out_dtype, cfg.out_scale = "fp8", 2.0 ** -6 * 1.21
+    res = run_prefill(w, g, cfg)
+    _, ro, _ = oracle_prefill(w, inp)
+    check_output_fp8(res["out"].cpu().numpy(), ro, "bf16", cfg.out_scale)
+
+
+def test_prefill_flags_short_length():
+    """A length below the new-token count is clamped up and flagged, not faulted."""
+    dev = device()
+    w = wl.custom([40, 90], num_q_heads=8, num_kv_heads=1, tokens=40, seed=840)
+    g = to_device(wl.make_inputs(w), dev)
+    g["seq_lens"][0] = 3
+    res = run_prefill(w, g)
+    assert res["error"] & lb._binding.DEV_ERR_SEQ_LEN
+
+
+@pytest.mark.slow
+def test_prefill_full_size_sampled():
+    """4 sequences of 4096 new tokens (two with a 2048-token prefix), sampled."""
+    dev = device()
+    w = wl.custom([4096, 6144, 4096, 6144], num_q_heads=64, num_kv_heads=8, tokens=4096,
+                  seed=850)
+    g = wl.make_inputs(w, device=dev)
+    res = run_prefill(w, g)
+    assert res["error"] == 0
+    h = host_step_inputs(g)
+    B, Tq, Hq = w.batch, w.tokens, w.num_q_heads
+    pick = [0, 1, 2047, 4095]
+    k = h["k"].reshape(B, Tq, w.num_kv_heads, 128)
+    v = h["v"].reshape(B, Tq, w.num_kv_heads, 128)
+    pos = h["positions"].reshape(B, Tq)
+    # prologue on every token (all k/v rows are needed), attention on picked tokens
+    pro = mt.prologue_tokens(h["q"].reshape(B, Tq, Hq, 128), k, v, pos, h["wq"], h["wk"],
+                             h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
+                             kv_dtype="bf16")
+    cfg = oracle_cfg(g, w)
+    q_out = pro["q_out"].reshape(B, Tq, Hq, 128)
+    out, lse = to_f64(res["out"]), to_f64(res["lse"])
+    pools = host_pools(g, w)
+    for b in (0, 3):
+        for j in pick:
+            for hh in (0, 9, 63):
+                K, V = _sequence_kv(pools, pro, b, hh // 8, h["seq_lens"], h["block_table"], cfg)
+                lim = mt.causal_limit(w.seq_lens[b], Tq, j)
+                o_ref, l_ref = attend_full(bf16_bits_to_f64(q_out[b, j, [hh]]), K[:lim], V[:lim],
+                                           cfg["sm_scale"])
+                check_output(out[b, j, hh], o_ref[0], "bf16", f"seq {b} token {j} head {hh}")
+                assert abs(lse[b, j, hh] - l_ref[0]) <= 1e-4 + 1e-5 * abs(l_ref[0])
