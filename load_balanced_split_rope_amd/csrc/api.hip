@@ -438,7 +438,7 @@ lbsr_status validate_prefill(const lbsr_shape* shape, const lbsr_params* params,
   if (lse_out && !aligned(lse_out, 4)) return fail(LBSR_E_INVALID, "lse_out misaligned");
   if (error_word && !aligned(error_word, 4)) return fail(LBSR_E_INVALID, "error_word misaligned");
   // one workgroup per (block of new tokens, sequence, KV head)
-  const int64_t per = 128 / (shape->num_q_heads / shape->num_kv_heads);
+  const int64_t per = lbsr::kPrefillColumns / (shape->num_q_heads / shape->num_kv_heads);
   const int64_t grid = (shape->tokens_per_seq + per - 1) / per * batch * shape->num_kv_heads;
   if (grid > INT32_MAX) return fail(LBSR_E_UNSUPPORTED, "prefill grid of %lld workgroups", (long long)grid);
   return LBSR_OK;

@@ -13,6 +13,18 @@ constexpr int kWave = 64;
 constexpr int kMaxGroup = 16;      // q heads per KV head that one matrix-core column block holds
 constexpr int kMaxColumns = 64;    // (new token, q head) pairs per KV head: 4 column blocks
 constexpr int kMaxTokensPerSeq = 1 << 18;  // new tokens per sequence (prefill)
+
+// Prefill workgroups: 8 waves, each with kPrefillBlocks blocks of 16 (token,
+// head) columns; every K/V fragment a wave reads from LDS feeds all its blocks.
+#ifndef LBSR_PREFILL_WAVES
+#define LBSR_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaves = LBSR_PREFILL_WAVES;
+#ifndef LBSR_PREFILL_BLOCKS
+#define LBSR_PREFILL_BLOCKS 2
+#endif
+constexpr int kPrefillBlocks = LBSR_PREFILL_BLOCKS;
+constexpr int kPrefillColumns = kPrefillWaves * 16 * kPrefillBlocks;   // per workgroup
 constexpr int kMergeLdsBytes = 65536;  // the merge stages chunks x columns weights in LDS
 constexpr int kMaxBatch = 16384;   // the plan keeps per-sequence prefix sums in LDS
 constexpr int kPlanThreads = 1024;

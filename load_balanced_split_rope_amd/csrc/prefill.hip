@@ -7,10 +7,12 @@
 // chunked prefill; with L = Tq it is a plain prefill.
 //
 // Mapping on CDNA4:
-//   * workgroup = (sequence b, KV head g, block of 128 (token, head) columns,
-//     i.e. 128/G consecutive new tokens with all G q heads of the group);
-//     8 waves of 16 columns, the same matrix-core shapes as the decode split
-//     kernel (S^T = K.Q^T, O^T += V^T.P^T on v_mfma_f32_16x16x32_bf16).
+//   * workgroup = (sequence b, KV head g, block of 256 (token, head) columns,
+//     i.e. 256/G consecutive new tokens with all G q heads of the group);
+//     8 waves of two 16-column blocks each, the same matrix-core shapes as
+//     the decode split kernel (S^T = K.Q^T, O^T += V^T.P^T on
+//     v_mfma_f32_16x16x32_bf16); every fragment a wave reads from LDS feeds
+//     both of its blocks, halving LDS traffic per flop.
 //   * the block's causal range [0, L - Tq + last token] is walked tile by
 //     tile; each K/V tile is read from HBM once per workgroup, straight into
 //     LDS in its fragment order (the page layout already is the operand
@@ -26,9 +28,6 @@
 #include "tile_math.h"
 
 namespace lbsr {
-
-constexpr int kPrefillWaves = 8;
-constexpr int kPrefillColumns = kPrefillWaves * 16;   // 128 (token, head) columns per workgroup
 
 template <bool kFp8>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
@@ -63,22 +62,27 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
   const int limit_first = L - T + tok0 + 1;         // and its first
   const int ntiles = (limit_last + kPage - 1) / kPage;
 
-  // this lane's column: token tok0 + j, head hl of group g
-  const int gc = wave * 16 + col;
-  const int j = gc / G, hl = gc - j * G;
-  const int jt = tok0 + j;
-  const bool valid = gc < tokens_per_block * G && jt < T;
-  const int limit = L - T + jt + 1;                 // this column attends rows < limit
-
-  bf16x8 qB[4];
-  if (valid) {
-    const u32x4* qp =
-        (const u32x4*)(q_out + (((size_t)b * T + jt) * Hq + (size_t)g * G + hl) * kHeadDim) + kc;
+  // this lane's column in each of the wave's blocks: token tok0 + j, head hl
+  int jt[kPrefillBlocks], hl[kPrefillBlocks], limit[kPrefillBlocks];
+  bool valid[kPrefillBlocks];
+  bf16x8 qB[kPrefillBlocks][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(qp[4 * s]);
-  } else {
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+    const int gc = (wave * kPrefillBlocks + cb) * 16 + col;
+    const int j = gc / G;
+    hl[cb] = gc - j * G;
+    jt[cb] = tok0 + j;
+    valid[cb] = gc < tokens_per_block * G && jt[cb] < T;
+    limit[cb] = L - T + jt[cb] + 1;                 // the column attends rows < limit
+    if (valid[cb]) {
+      const u32x4* qp = (const u32x4*)(q_out + (((size_t)b * T + jt[cb]) * Hq + (size_t)g * G +
+                                                hl[cb]) * kHeadDim) + kc;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+      for (int s = 0; s < 4; ++s) qB[cb][s] = as_bf16x8(qp[4 * s]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qB[cb][s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
   }
 
   const int32_t* bt_row = block_table + (size_t)b * geo.max_blocks;
@@ -103,11 +107,14 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     for (int i = 0; i < kPerThread; ++i) s_kv[stage][tid + i * kPrefillWaves * kWave] = src[i];
   };
 
-  SoftmaxState st;
+  SoftmaxState st[kPrefillBlocks];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -__builtin_inff();
-  st.lsum = 0.f;
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st[cb].O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st[cb].m = -__builtin_inff();
+    st[cb].lsum = 0.f;
+  }
 
   u32x4 pre[kPerThread];
   load_tile(0, pre);
@@ -119,11 +126,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     const u32x4* kf = s_kv[stage];
     const u32x4* vf = s_kv[stage] + NF * kWave;
 
-    // ---- scores ----
-    f32x4 S[4];
+    // ---- scores: every K fragment read from LDS serves all column blocks ----
+    f32x4 S[kPrefillBlocks][4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < kPrefillBlocks; ++cb) S[cb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8 a;
@@ -133,15 +141,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
         } else {
           a = as_bf16x8(kf[(4 * tb + s) * kWave + lane]);
         }
-        acc = mfma_bf16(a, qB[s], acc);
+#pragma unroll
+        for (int cb = 0; cb < kPrefillBlocks; ++cb) S[cb][tb] = mfma_bf16(a, qB[cb][s], S[cb][tb]);
       }
-      S[tb] = acc;
     }
 
     // ---- online softmax: columns' limits fall in this tile or earlier ----
-    bf16x8 pB[2];
+    bf16x8 pB[kPrefillBlocks][2];
     const int row0 = t * kPage;
-    softmax_tile(S, st, limit_first - row0 < kPage, limit - row0, kc, score_scale_log2, pB);
+#pragma unroll
+    for (int cb = 0; cb < kPrefillBlocks; ++cb)
+      softmax_tile(S[cb], st[cb], limit_first - row0 < kPage, limit[cb] - row0, kc,
+                   score_scale_log2, pB[cb]);
 
     // ---- P.V, with rows at or past the sequence end zeroed in the last tile ----
     const int rem = L - row0;
@@ -168,7 +179,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
           }
           a = as_bf16x8(w);
         }
-        st.O[db] = mfma_bf16(a, pB[s], st.O[db]);
+#pragma unroll
+        for (int cb = 0; cb < kPrefillBlocks; ++cb)
+          st[cb].O[db] = mfma_bf16(a, pB[cb][s], st[cb].O[db]);
       }
     }
     if (t + 1 < ntiles) store_tile(stage ^ 1, pre);
@@ -177,15 +190,17 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
   if (bad_page && error_word) atomicOr(error_word, (int32_t)kErrPage);
 
   // ---- output ----
-  const float l = sum_xor32(sum_xor16(st.lsum));
-  const float scale = l > 0.f ? out_scale / l : 0.f;
-  if (valid) {
-    const size_t orow = ((size_t)b * T + jt) * Hq + (size_t)g * G + hl;
+#pragma unroll
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+    const float l = sum_xor32(sum_xor16(st[cb].lsum));
+    const float scale = l > 0.f ? out_scale / l : 0.f;
+    if (!valid[cb]) continue;
+    const size_t orow = ((size_t)b * T + jt[cb]) * Hq + (size_t)g * G + hl[cb];
     if (out_fp8) {
       uint8_t* o = (uint8_t*)out + orow * kHeadDim + 4 * kc;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const f32x4 x = st.O[db] * scale;
+        const f32x4 x = st[cb].O[db] * scale;
         *(uint32_t*)(o + 16 * db) = f32x4_to_e4m3x4(x[0], x[1], x[2], x[3]);
       }
     } else {
@@ -194,12 +209,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
       for (int db = 0; db < 8; ++db) {
         bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(st.O[db][e] * scale);
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(st[cb].O[db][e] * scale);
         *(bf16x4*)(o + 16 * db) = v4;
       }
     }
     if (kc == 0 && lse_out)
-      lse_out[orow] = (l > 0.f ? st.m + __builtin_amdgcn_logf(l) : -__builtin_inff()) * kLn2;
+      lse_out[orow] = (l > 0.f ? st[cb].m + __builtin_amdgcn_logf(l) : -__builtin_inff()) * kLn2;
   }
   if (tid == 0 && L != L_in && error_word && qb == 0 && g == 0) atomicOr(error_word, (int32_t)kErrSeqLen);
 }

@@ -68,47 +68,58 @@ struct SoftmaxState {
 };
 
 // Online-softmax update with one tile's scores S (the lane's 16 scores of its
-// column, see above): scale into the log2 domain, mask rows >= lim when
-// `mask`, update the running max and sum, rescale O, and return P^T as the
-// two BF16 operands of the P.V step (elements e < 4 from token block 2s,
-// e >= 4 from 2s + 1).  A column with no unmasked row yet keeps m = -inf; 0
-// then serves as the exponent base so that alpha and p are 0, not NaN.
+// column, see above), in the log2 domain: x = fl(c*s), p = 2^(x - m).  The
+// scaled score is materialised once and used for both the max and the
+// exponent, so the row that sets the max gets p = 1 exactly (a one-row
+// softmax returns V bit for bit).  Rows >= lim are masked when `mask`.
+// Returns P^T as the two BF16 operands of the P.V step (elements e < 4 from
+// token block 2s, e >= 4 from 2s + 1).
+//
+// Deferred rescaling: the running max m is raised (and O and the sum
+// rescaled) only when some column of the wave would otherwise see
+// p > 2^8 -- so on most tiles the 32 multiplies per lane of the O rescale
+// are skipped, while p stays within BF16's range and fp32 sums stay far from
+// overflow.  The result is the same online softmax with a different (but
+// consistent) reference max.  A column with no unmasked row yet keeps
+// m = -inf; 0 then serves as the exponent base, so p and alpha are 0.
 __device__ __forceinline__ void softmax_tile(const f32x4 (&S)[4], SoftmaxState& st, bool mask,
-                                             int lim, int kc, float score_scale_log2,
-                                             bf16x8 (&pB)[2]) {
-  float p[16];
+                                             int lim, int kc, float c, bf16x8 (&pB)[2]) {
+  float x[16];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[4 * tb + e] = S[tb][e] * score_scale_log2;
+    for (int e = 0; e < 4; ++e) x[4 * tb + e] = S[tb][e] * c;
   if (mask) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (16 * tb + 4 * kc + e >= lim) p[4 * tb + e] = -__builtin_inff();
+        if (16 * tb + 4 * kc + e >= lim) x[4 * tb + e] = -__builtin_inff();
   }
-  float mx = p[0];
+  float mx = x[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, p[i]);
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
   mx = max_xor32(max_xor16(mx));
-  const float m_new = fmaxf(st.m, mx);
-  const float m_base = m_new == -__builtin_inff() ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_base);
+  if (__any(mx > st.m + 8.f)) {                          // wave-uniform
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - (m_new == -__builtin_inff() ? 0.f : m_new));
+    st.lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.O[i] *= alpha;
+    st.m = m_new;
+  }
+  const float base = st.m == -__builtin_inff() ? 0.f : st.m;
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    p[i] = fast_exp2(p[i] - m_base);
-    psum += p[i];
+    x[i] = fast_exp2(x[i] - base);
+    psum += x[i];
   }
-  st.lsum = st.lsum * alpha + psum;
-  st.m = m_new;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.O[i] *= alpha;
+  st.lsum += psum;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)p[8 * s + e];
+    for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)x[8 * s + e];
 }
 
 // Byte masks that zero the V rows at or past `rem` (rows past a sequence's
