@@ -12,7 +12,9 @@ Prints one JSON line.  value = compulsory bytes per step / step time (GB/s).
 Also reported: the same for the FP8 cache, the static equal split-KV
 baseline (default S = floor(256/B) and the best S of a sweep), per-kernel
 times from HIP events on the launch stream, the split-attention kernel's
-roofline, and the fp64 CPU oracle timed on the host.
+roofline, multi-token decode, FP8 output, a uniform and a log-uniform batch,
+prefill and chunked prefill against the matrix-core peak, and the fp64 CPU
+oracle timed on the host.
 """
 
 import argparse
@@ -33,6 +35,7 @@ from load_balanced_split_rope_amd import workloads as wl        # noqa: E402
 
 METRIC = ("decode-attn µs/step + achieved HBM GB/s (% peak), 1x128K+31x4K mix, BF16/FP8")
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0        # dense BF16 matrix-core peak of MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_attention_traffic.json")
 
 
@@ -168,6 +171,9 @@ WORKLOAD_TEXT = {
     "loguniform": "loguniform: 64 sequences, lengths log-uniform in [512, 262144], FP8 cache",
     "mix_mtp2": "mix_mtp2: 1 x 131072 + 31 x 4096 tokens, 2 new tokens per sequence",
     "mix_mtp4": "mix_mtp4: 1 x 131072 + 31 x 4096 tokens, 4 new tokens per sequence",
+    "prefill": "prefill: 4 prompts x 8192 new tokens, causal, BF16 cache",
+    "prefill_fp8": "prefill_fp8: 4 prompts x 8192 new tokens, causal, FP8 E4M3 cache",
+    "chunked_prefill": "chunked_prefill: 32 x (4096-token prefix + 512 new tokens), BF16 cache",
 }
 WALL_CLOCK_MHZ = 100.0   # the constant clock the trace stamps (100 MHz on MI300-class GPUs)
 
@@ -193,7 +199,7 @@ def load_balance(tr):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("attention.hip", "common.h"):
+    for f in ("attention.hip", "tile_math.h", "common.h"):
         with open(os.path.join(ROOT, "load_balanced_split_rope_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -211,6 +217,70 @@ def measured_traffic(workload, kv_dtype):
         return None
     entry = rec.get("workloads", {}).get(f"{workload}/{kv_dtype}")
     return None if entry is None else entry.get("bytes_per_launch")
+
+
+def prefill_flops(w):
+    """Causal attention flops of a prefill step: new token j of sequence b
+    attends L_b - Tq + j + 1 rows; 4 flops per (row, q head, channel) for
+    Q.K^T and P.V."""
+    Tq, tot = w.tokens, 0
+    for L in w.seq_lens:
+        tot += Tq * (L - Tq + 1) + Tq * (Tq - 1) // 2
+    return 4 * 128 * w.num_q_heads * tot
+
+
+def prefill_leg(dev, reps=10, warmup=3):
+    """lbsr_prefill_step (prologue + attention) and lbsr_prefill_attention alone,
+    each timed with HIP events on the launch stream; the attention kernel is
+    matrix-core bound, so its roofline is flops against the BF16 MFMA peak."""
+    legs = {}
+    for name in wl.PREFILL_NAMES:
+        w = wl.named(name)
+        g = wl.make_inputs(w, device=dev)
+        cfg = lb.DecodeConfig(w.num_q_heads, w.num_kv_heads, w.kv_dtype, g["max_blocks"],
+                              g["num_pages"], page_stride=g["page_stride"],
+                              head_stride=g["head_stride"], rope_theta=w.rope_theta,
+                              rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale,
+                              tokens_per_seq=w.tokens)
+        q_out = torch.empty_like(g["q"])
+        out = torch.empty_like(g["q"])
+        lse = torch.empty(cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32,
+                          device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        step_args = (cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"], g["q_norm_w"],
+                     g["k_norm_w"], g["block_table"], g["k_cache"], g["v_cache"], q_out, out, lse,
+                     err)
+        attn_args = (cfg, q_out, g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], out,
+                     lse, err)
+
+        def event_ms(fn, args):
+            for _ in range(warmup):
+                fn(*args)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        step_ms = event_ms(lb.prefill_step, step_args)
+        attn_ms = event_ms(lb.prefill_attention, attn_args)
+        if int(err.item()) != 0:
+            raise RuntimeError(f"prefill leg {name}: device error word {int(err.item()):#x}")
+        f = prefill_flops(w)
+        tflops = f / (attn_ms * 1e-3) / 1e12
+        legs[name] = {
+            "workload": WORKLOAD_TEXT[name], "us_per_step": round(step_ms * 1e3, 1),
+            "attention_us": round(attn_ms * 1e3, 1), "flops": f,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": f"prefill_kernel<{w.kv_dtype}>"},
+        }
+        del g, q_out, out, lse, step_args, attn_args
+        torch.cuda.empty_cache()
+    return legs
 
 
 def cpu_baseline(w, dev, min_seconds=10.0):
@@ -321,6 +391,8 @@ def main():
                     help="only run a plain 1 GiB device copy 5 times (a known-size kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill leg (prefill, prefill_fp8, chunked_prefill), as JSON")
     ap.add_argument("--no-xcd-weights", action="store_true",
                     help="equal worker shares only (skip the per-XCD rate calibration)")
     ap.add_argument("--quick", action="store_true",
@@ -339,6 +411,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": 5}))
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_leg(dev)}), flush=True)
         return
     P = lb.device_workers(0)
     full = not args.quick
@@ -467,6 +542,7 @@ def main():
                 "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, ro["kernel_ms"])},
                 "step_time_vs_bf16_output": round(ro["ms"] / ms, 4),
             }
+            result["prefill"] = prefill_leg(dev)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(w, dev)
     print(json.dumps(result), flush=True)

@@ -115,7 +115,7 @@ lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
   if (!page_major && !head_major)
     return fail(LBSR_E_INVALID, "page_stride/head_stride make tiles overlap");
   if (batch < 1) return fail(LBSR_E_INVALID, "batch %d < 1", batch);
-  // the prologue runs one wave per (new token, row): the count must fit an int
+  // the prologue runs at most one wave per (new token, row): the count must fit an int
   if ((int64_t)batch * s->tokens_per_seq * (s->num_q_heads + 2 * s->num_kv_heads) > INT32_MAX / 2)
     return fail(LBSR_E_UNSUPPORTED, "batch %d x tokens_per_seq %d is too many rows", batch,
                 s->tokens_per_seq);

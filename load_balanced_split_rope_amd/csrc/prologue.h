@@ -16,7 +16,8 @@
 // frequencies come precomputed (RopeFreqs): an fp64 pow per lane was the
 // largest single step of the chain.
 //
-// One wave per row; lane l owns the rotation pair (l, l + 64).
+// A wave runs consecutive rows of one token; lane l owns the rotation pair
+// (l, l + 64).
 #pragma once
 
 #include "common.h"
@@ -26,6 +27,15 @@ namespace lbsr {
 // fp64 -> BF16 bits with a single round-to-nearest-even, from the bit pattern.
 __device__ inline uint16_t f64_to_bf16_rne(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
+  const uint32_t biased = (uint32_t)(mag >> 52);
+  if (biased >= 1023 - 126 && biased <= 1023 + 127) {
+    // BF16-normal range: round the magnitude's bit pattern at its 45th bit
+    // (half minus one, plus the kept LSB: ties to even).  A carry moves into
+    // the exponent field, and past the largest finite value gives infinity.
+    const uint64_t r = mag + ((1ull << 44) - 1) + ((mag >> 45) & 1);
+    return (uint16_t)((uint32_t)(u >> 48 & 0x8000) | (uint32_t)((r >> 45) - (896u << 7)));
+  }
   const uint32_t sign = (uint32_t)(u >> 63) << 15;
   const int exp = (int)((u >> 52) & 0x7FF);
   const uint64_t mant = u & 0xFFFFFFFFFFFFFull;
@@ -86,112 +96,138 @@ __device__ inline double wave_sum_f64(double x) {
   return x;
 }
 
-// Row `row` of new token `tok` (tok = b * Tq + j for new token j of sequence
-// b = seq): rows [0, Hq) are q heads, [Hq, Hq+Hkv) k heads, then v heads.
-// Called by a whole wave.  A k/v row whose position or page is out of range
-// skips its cache write and reports LBSR_DEV_ERR_* bits: OR-ed into
-// `error_word` if given, and/or stored (0 when fine) to `token_status[tok]`
-// if given -- every k/v row of a token stores the same value.
-template <bool kFp8>
-__device__ inline void prologue_row(
-    int tok, int seq, int row, const Geometry& geo, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ positions, const uint16_t* __restrict__ wq,
-    const uint16_t* __restrict__ wk, const int32_t* __restrict__ block_table,
-    void* __restrict__ k_cache, void* __restrict__ v_cache, uint16_t* __restrict__ q_out,
-    int32_t* __restrict__ error_word, int32_t* __restrict__ token_status, const RopeFreqs& freqs,
-    double eps, int norm_first, double k_scale, double v_scale) {
+// Rows [row_begin, row_end) of new token `tok` (tok = b * Tq + j for new
+// token j of sequence b = seq); rows [0, Hq) are q heads, [Hq, Hq+Hkv) k
+// heads, then v heads.  Called by a whole wave.  The rotation angle depends
+// only on the position and the channel pair, so its sine and cosine are
+// computed once for the run, as are the norm weights and the cache slot.
+// A k/v row whose position or page is out of range skips its cache write and
+// reports LBSR_DEV_ERR_* bits: OR-ed into `error_word` if given, and/or
+// stored (0 when fine) to `token_status[tok]` if given -- every run holding
+// k/v rows of a token stores the same value.  kOneRow: every run is a single
+// row (row_end = row_begin + 1), the decode-sized case, compiled without the
+// loop.
+template <bool kFp8, bool kOneRow>
+__device__ inline void prologue_rows(
+    int tok, int seq, int row_begin, int row_end, const Geometry& geo,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ positions,
+    const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
+    const int32_t* __restrict__ block_table, void* __restrict__ k_cache,
+    void* __restrict__ v_cache, uint16_t* __restrict__ q_out, int32_t* __restrict__ error_word,
+    int32_t* __restrict__ token_status, const RopeFreqs& freqs, double eps, int norm_first,
+    double k_scale, double v_scale) {
 #pragma clang fp contract(off)
   const int Hq = geo.num_q_heads, Hkv = geo.num_kv_heads;
   const int lane = threadIdx.x & 63;
   const int pos = positions[tok];
+  if (kOneRow) row_end = row_begin + 1;
 
-  const uint16_t* src;
-  const uint16_t* w = nullptr;
-  int kind;  // 0 = q, 1 = k, 2 = v
-  int g = 0;
-  if (row < Hq) {
-    kind = 0;
-    src = q + ((size_t)tok * Hq + row) * kHeadDim;
-    w = wq;
-  } else if (row < Hq + Hkv) {
-    kind = 1;
-    g = row - Hq;
-    src = k + ((size_t)tok * Hkv + g) * kHeadDim;
-    w = wk;
-  } else {
-    kind = 2;
-    g = row - Hq - Hkv;
-    src = v + ((size_t)tok * Hkv + g) * kHeadDim;
+  // the row's source: q heads, then k heads, then v heads of this token
+  auto source = [&](int row) -> const uint16_t* {
+    if (row < Hq) return q + ((size_t)tok * Hq + row) * kHeadDim;
+    if (row < Hq + Hkv) return k + ((size_t)tok * Hkv + (row - Hq)) * kHeadDim;
+    return v + ((size_t)tok * Hkv + (row - Hq - Hkv)) * kHeadDim;
+  };
+  const uint16_t* src = source(row_begin);
+  uint16_t next0 = src[lane], next1 = src[lane + 64];
+
+  double sn = 0.0, cs = 1.0;
+  double wq0 = 0.0, wq1 = 0.0, wk0 = 0.0, wk1 = 0.0;
+  if (row_begin < Hq) {
+    wq0 = bf16_to_f64(wq[lane]);
+    wq1 = bf16_to_f64(wq[lane + 64]);
   }
-  const uint16_t raw0 = src[lane], raw1 = src[lane + 64];
-  double y0 = bf16_to_f64(raw0), y1 = bf16_to_f64(raw1);
-
-  if (kind != 2) {
-    const double w0 = bf16_to_f64(w[lane]), w1 = bf16_to_f64(w[lane + 64]);
-    const double omega = freqs.omega[lane];
-    const double a = (double)pos * omega;
-    double sn, cs;
-    sincos(a, &sn, &cs);
-    for (int step = 0; step < 2; ++step) {
-      const bool do_norm = (step == 0) == (norm_first != 0);
-      if (do_norm) {
-        const double ms = wave_sum_f64(y0 * y0 + y1 * y1) / (double)kHeadDim;
-        const double r = sqrt(ms + eps);
-        y0 = y0 / r * w0;
-        y1 = y1 / r * w1;
-      } else {
-        const double r0 = y0 * cs - y1 * sn;
-        const double r1 = y1 * cs + y0 * sn;
-        y0 = r0;
-        y1 = r1;
-      }
-    }
+  if (row_begin < Hq + Hkv && row_end > Hq) {
+    wk0 = bf16_to_f64(wk[lane]);
+    wk1 = bf16_to_f64(wk[lane + 64]);
   }
+  if (row_begin < Hq + Hkv) sincos((double)pos * freqs.omega[lane], &sn, &cs);
 
-  if (kind == 0) {
-    uint16_t* dst = q_out + ((size_t)tok * Hq + row) * kHeadDim;
-    dst[lane] = f64_to_bf16_rne(y0);
-    dst[lane + 64] = f64_to_bf16_rne(y1);
-    return;
-  }
-
-  // cache write of the new token's row
+  // the cache slot of the token's k/v rows
   int32_t flags = 0;
   int page = -1;
-  if (pos < 0 || pos >= geo.max_blocks * kPage) {
-    flags = kErrPosition;
-  } else {
-    page = block_table[(size_t)seq * geo.max_blocks + (pos >> 6)];
-    if (page < 0 || page >= geo.num_pages) flags = kErrPage;
-  }
-  if (lane == 0) {
-    if (token_status) token_status[tok] = flags;
-    if (error_word && flags) atomicOr(error_word, flags);
-  }
-  if (flags) return;
-  const int r = pos & (kPage - 1);
-  const size_t base = (size_t)page * geo.page_stride + (size_t)g * geo.head_stride;
-  if (!kFp8) {
-    uint16_t* dst = (uint16_t*)(kind == 1 ? k_cache : v_cache) + base;
-    if (kind == 1) {
-      dst[k_offset_bf16(r, lane)] = f64_to_bf16_rne(y0);
-      dst[k_offset_bf16(r, lane + 64)] = f64_to_bf16_rne(y1);
+  if (row_end > Hq) {
+    if (pos < 0 || pos >= geo.max_blocks * kPage) {
+      flags = kErrPosition;
     } else {
-      dst[v_offset_bf16(r, lane)] = raw0;  // v is BF16 already: stored as is
-      dst[v_offset_bf16(r, lane + 64)] = raw1;
+      page = block_table[(size_t)seq * geo.max_blocks + (pos >> 6)];
+      if (page < 0 || page >= geo.num_pages) flags = kErrPage;
     }
-  } else {
-    uint8_t* dst = (uint8_t*)(kind == 1 ? k_cache : v_cache) + base;
-    if (kind == 1) {
-      dst[k_offset_fp8(r, lane)] = f64_to_e4m3_sat(y0 / k_scale);
-      dst[k_offset_fp8(r, lane + 64)] = f64_to_e4m3_sat(y1 / k_scale);
+    if (lane == 0) {
+      if (token_status) token_status[tok] = flags;
+      if (error_word && flags) atomicOr(error_word, flags);
+    }
+  }
+  const int slot_row = pos & (kPage - 1);
+
+  for (int row = row_begin; row < row_end; ++row) {
+    const uint16_t raw0 = next0, raw1 = next1;
+    if (!kOneRow && row + 1 < row_end) {     // the next row's loads, ahead of this row's math
+      const uint16_t* nsrc = source(row + 1);
+      next0 = nsrc[lane];
+      next1 = nsrc[lane + 64];
+    }
+    const int kind = row < Hq ? 0 : (row < Hq + Hkv ? 1 : 2);   // q, k, v
+    double y0 = bf16_to_f64(raw0), y1 = bf16_to_f64(raw1);
+    if (kind != 2) {
+      const double w0 = kind == 0 ? wq0 : wk0, w1 = kind == 0 ? wq1 : wk1;
+      for (int step = 0; step < 2; ++step) {
+        const bool do_norm = (step == 0) == (norm_first != 0);
+        if (do_norm) {
+          const double ms = wave_sum_f64(y0 * y0 + y1 * y1) / (double)kHeadDim;
+          const double inv = 1.0 / sqrt(ms + eps);
+          y0 = y0 * inv * w0;
+          y1 = y1 * inv * w1;
+        } else {
+          const double r0 = y0 * cs - y1 * sn;
+          const double r1 = y1 * cs + y0 * sn;
+          y0 = r0;
+          y1 = r1;
+        }
+      }
+    }
+    if (kind == 0) {
+      uint16_t* dst = q_out + ((size_t)tok * Hq + row) * kHeadDim;
+      dst[lane] = f64_to_bf16_rne(y0);
+      dst[lane + 64] = f64_to_bf16_rne(y1);
+      continue;
+    }
+    if (flags) continue;
+    const int g = kind == 1 ? row - Hq : row - Hq - Hkv;
+    const size_t base = (size_t)page * geo.page_stride + (size_t)g * geo.head_stride;
+    if (!kFp8) {
+      uint16_t* dst = (uint16_t*)(kind == 1 ? k_cache : v_cache) + base;
+      if (kind == 1) {
+        dst[k_offset_bf16(slot_row, lane)] = f64_to_bf16_rne(y0);
+        dst[k_offset_bf16(slot_row, lane + 64)] = f64_to_bf16_rne(y1);
+      } else {
+        dst[v_offset_bf16(slot_row, lane)] = raw0;  // v is BF16 already: stored as is
+        dst[v_offset_bf16(slot_row, lane + 64)] = raw1;
+      }
     } else {
-      dst[v_offset_fp8(r, lane)] = f64_to_e4m3_sat(y0 / v_scale);
-      dst[v_offset_fp8(r, lane + 64)] = f64_to_e4m3_sat(y1 / v_scale);
+      uint8_t* dst = (uint8_t*)(kind == 1 ? k_cache : v_cache) + base;
+      if (kind == 1) {
+        dst[k_offset_fp8(slot_row, lane)] = f64_to_e4m3_sat(y0 / k_scale);
+        dst[k_offset_fp8(slot_row, lane + 64)] = f64_to_e4m3_sat(y1 / k_scale);
+      } else {
+        dst[v_offset_fp8(slot_row, lane)] = f64_to_e4m3_sat(y0 / v_scale);
+        dst[v_offset_fp8(slot_row, lane + 64)] = f64_to_e4m3_sat(y1 / v_scale);
+      }
     }
   }
 }
 
+// How many runs each token's rows are cut into: enough waves to fill the GPU
+// a few times over (one row per wave when the tokens are few, as in decode),
+// a whole token per wave when they are many, as in prefill.
+inline int prologue_runs_per_token(int tokens, int rows) {
+  constexpr int kTargetWaves = 32768;
+  const int runs = (kTargetWaves + tokens - 1) / (tokens > 0 ? tokens : 1);
+  return runs < 1 ? 1 : (runs > rows ? rows : runs);
+}
+
+// Run `i` of `runs` covers rows [i * rows / runs, (i + 1) * rows / runs).
+__device__ inline int prologue_run_begin(int i, int runs, int rows) { return i * rows / runs; }
 
 }  // namespace lbsr

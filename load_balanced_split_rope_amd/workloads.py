@@ -16,6 +16,10 @@ head dim 128; 64-token pages):
 * ``mix_mtp2``    the BF16 mix with 2 new tokens per sequence (multi-token
                   decode, as when one drafted token is verified)
 * ``mix_mtp4``    the same with 4 new tokens per sequence (three drafted)
+* ``prefill``     prefill of 4 prompts of 8192 tokens (every token is new), BF16
+* ``prefill_fp8`` the same with an FP8 E4M3 cache
+* ``chunked_prefill``  32 sequences of 4608 tokens whose last 512 are new
+                  (a 512-token prefill chunk after a 4096-token prefix)
 
 Recipe (per workload, seed s): ``numpy.random.SeedSequence(s)`` spawns child
 streams, in order: 0 lengths, 1 q, 2 k, 3 v, 4 q-norm weight, 5 k-norm weight,
@@ -73,7 +77,7 @@ def loguniform_lengths(seed, batch=64, lo=512, hi=262144):
 
 
 def named(name):
-    """The five named workloads."""
+    """The named workloads listed above."""
     if name == "tiny":
         return Workload("tiny", [1, 63, 64, 200], num_q_heads=8, num_kv_heads=1, seed=1)
     if name == "uniform":
@@ -90,11 +94,19 @@ def named(name):
         return Workload("mix_mtp2", [131072] + [4096] * 31, seed=6, tokens=2)
     if name == "mix_mtp4":
         return Workload("mix_mtp4", [131072] + [4096] * 31, seed=7, tokens=4)
+    if name == "prefill":
+        return Workload("prefill", [8192] * 4, seed=8, tokens=8192)
+    if name == "prefill_fp8":
+        return Workload("prefill_fp8", [8192] * 4, kv_dtype="fp8", k_scale=2.0 ** -5,
+                        v_scale=2.0 ** -4, seed=9, tokens=8192)
+    if name == "chunked_prefill":
+        return Workload("chunked_prefill", [4608] * 32, seed=10, tokens=512)
     raise KeyError(name)
 
 
 NAMES = ("tiny", "uniform", "mix", "mix_fp8", "loguniform")
 MULTI_TOKEN_NAMES = ("mix_mtp2", "mix_mtp4")
+PREFILL_NAMES = ("prefill", "prefill_fp8", "chunked_prefill")
 
 
 def _bf16(x):

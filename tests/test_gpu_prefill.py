@@ -119,34 +119,44 @@ def test_prefill_flags_short_length():
 
 
 @pytest.mark.slow
-def test_prefill_full_size_sampled():
-    """4 sequences of 4096 new tokens (two with a 2048-token prefix), sampled."""
+@pytest.mark.parametrize("name", wl.PREFILL_NAMES)
+def test_prefill_full_size_sampled(name):
+    """The benchmark's prefill workloads at full size: q_out of every token
+    bit-exact on sampled sequences, outputs and lse of sampled (token, head)
+    pairs against the oracle."""
     dev = device()
-    w = wl.custom([4096, 6144, 4096, 6144], num_q_heads=64, num_kv_heads=8, tokens=4096,
-                  seed=850)
+    w = wl.named(name)
     g = wl.make_inputs(w, device=dev)
+    pools = host_pools(g, w)              # the caches before the step writes them
+    print(f"prefill full size {name}", flush=True)
     res = run_prefill(w, g)
     assert res["error"] == 0
     h = host_step_inputs(g)
-    B, Tq, Hq = w.batch, w.tokens, w.num_q_heads
-    pick = [0, 1, 2047, 4095]
-    k = h["k"].reshape(B, Tq, w.num_kv_heads, 128)
-    v = h["v"].reshape(B, Tq, w.num_kv_heads, 128)
-    pos = h["positions"].reshape(B, Tq)
-    # prologue on every token (all k/v rows are needed), attention on picked tokens
-    pro = mt.prologue_tokens(h["q"].reshape(B, Tq, Hq, 128), k, v, pos, h["wq"], h["wk"],
-                             h["block_table"], theta=w.rope_theta, eps=w.rms_eps,
-                             kv_dtype="bf16")
+    B, Tq, Hq, Hkv = w.batch, w.tokens, w.num_q_heads, w.num_kv_heads
+    seqs = [0, B - 1]
+    pick = [0, 1, Tq // 2 - 1, Tq - 1]
+    pos = h["positions"].reshape(B, Tq)[seqs]
+    # prologue on every token of the sampled sequences (all their k/v rows are read)
+    pro = mt.prologue_tokens(h["q"].reshape(B, Tq, Hq, 128)[seqs],
+                             h["k"].reshape(B, Tq, Hkv, 128)[seqs],
+                             h["v"].reshape(B, Tq, Hkv, 128)[seqs], pos, h["wq"], h["wk"],
+                             h["block_table"][seqs], theta=w.rope_theta, eps=w.rms_eps,
+                             kv_dtype=w.kv_dtype, k_scale=np.float32(w.k_scale).item(),
+                             v_scale=np.float32(w.v_scale).item())
+    q_out = pro["q_out"].reshape(len(seqs), Tq, Hq, 128)
+    got_q = bits_u16(res["q_out"]).reshape(B, Tq, Hq, 128)
+    assert np.array_equal(got_q[seqs], q_out)
     cfg = oracle_cfg(g, w)
-    q_out = pro["q_out"].reshape(B, Tq, Hq, 128)
+    cfg["k_scale"], cfg["v_scale"] = np.float32(w.k_scale).item(), np.float32(w.v_scale).item()
     out, lse = to_f64(res["out"]), to_f64(res["lse"])
-    pools = host_pools(g, w)
-    for b in (0, 3):
-        for j in pick:
-            for hh in (0, 9, 63):
-                K, V = _sequence_kv(pools, pro, b, hh // 8, h["seq_lens"], h["block_table"], cfg)
+    lens = h["seq_lens"][seqs]
+    for i, b in enumerate(seqs):
+        for hh in (0, 9, 63):
+            K, V = _sequence_kv(pools, pro, i, hh // (Hq // Hkv), lens, h["block_table"][seqs],
+                                cfg)
+            for j in pick:
                 lim = mt.causal_limit(w.seq_lens[b], Tq, j)
-                o_ref, l_ref = attend_full(bf16_bits_to_f64(q_out[b, j, [hh]]), K[:lim], V[:lim],
+                o_ref, l_ref = attend_full(bf16_bits_to_f64(q_out[i, j, [hh]]), K[:lim], V[:lim],
                                            cfg["sm_scale"])
-                check_output(out[b, j, hh], o_ref[0], "bf16", f"seq {b} token {j} head {hh}")
+                check_output(out[b, j, hh], o_ref[0], w.kv_dtype, f"seq {b} token {j} head {hh}")
                 assert abs(lse[b, j, hh] - l_ref[0]) <= 1e-4 + 1e-5 * abs(l_ref[0])
