@@ -174,6 +174,8 @@ WORKLOAD_TEXT = {
     "prefill": "prefill: 4 prompts x 8192 new tokens, causal, BF16 cache",
     "prefill_fp8": "prefill_fp8: 4 prompts x 8192 new tokens, causal, FP8 E4M3 cache",
     "chunked_prefill": "chunked_prefill: 32 x (4096-token prefix + 512 new tokens), BF16 cache",
+    "ragged_prefill": "ragged_prefill: 8 prompts, 512 to 8192 new tokens each (25,788 packed) "
+                      "after prefixes of 0 to 20,000 tokens, BF16 cache",
 }
 WALL_CLOCK_MHZ = 100.0   # the constant clock the trace stamps (100 MHz on MI300-class GPUs)
 
@@ -221,11 +223,12 @@ def measured_traffic(workload, kv_dtype):
 
 def prefill_flops(w):
     """Causal attention flops of a prefill step: new token j of sequence b
-    attends L_b - Tq + j + 1 rows; 4 flops per (row, q head, channel) for
-    Q.K^T and P.V."""
-    Tq, tot = w.tokens, 0
-    for L in w.seq_lens:
-        tot += Tq * (L - Tq + 1) + Tq * (Tq - 1) // 2
+    (n_b new tokens) attends L_b - n_b + j + 1 rows; 4 flops per (row, q head,
+    channel) for Q.K^T and P.V."""
+    counts = w.new_tokens if w.varlen else [w.tokens] * w.batch
+    tot = 0
+    for L, n in zip(w.seq_lens, counts):
+        tot += n * (L - n + 1) + n * (n - 1) // 2
     return 4 * 128 * w.num_q_heads * tot
 
 
@@ -241,17 +244,25 @@ def prefill_leg(dev, reps=10, warmup=3):
                               g["num_pages"], page_stride=g["page_stride"],
                               head_stride=g["head_stride"], rope_theta=w.rope_theta,
                               rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale,
-                              tokens_per_seq=w.tokens)
+                              tokens_per_seq=w.max_new_tokens)
         q_out = torch.empty_like(g["q"])
         out = torch.empty_like(g["q"])
-        lse = torch.empty(cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32,
-                          device=dev)
+        lse = torch.empty(g["q"].shape[:-1], dtype=torch.float32, device=dev)
         err = torch.zeros(1, dtype=torch.int32, device=dev)
-        step_args = (cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"], g["q_norm_w"],
-                     g["k_norm_w"], g["block_table"], g["k_cache"], g["v_cache"], q_out, out, lse,
-                     err)
-        attn_args = (cfg, q_out, g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"], out,
-                     lse, err)
+        common = (g["seq_lens"], g["q_norm_w"], g["k_norm_w"], g["block_table"], g["k_cache"],
+                  g["v_cache"], q_out, out, lse, err)
+        if w.varlen:
+            ws = lb.alloc_prefill_workspace(cfg, w.batch, g["q"].shape[0], device=dev)
+            step_fn, attn_fn = lb.prefill_step_varlen, lb.prefill_attention_varlen
+            step_args = ((cfg, g["q_start"], g["q"], g["k"], g["v"], g["positions"]) + common[:7]
+                         + (ws,) + common[7:])
+            attn_args = (cfg, g["q_start"], q_out, g["k_cache"], g["v_cache"], g["block_table"],
+                         g["seq_lens"], ws, out, lse, err)
+        else:
+            step_fn, attn_fn = lb.prefill_step, lb.prefill_attention
+            step_args = (cfg, g["q"], g["k"], g["v"], g["positions"]) + common
+            attn_args = (cfg, q_out, g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"],
+                         out, lse, err)
 
         def event_ms(fn, args):
             for _ in range(warmup):
@@ -264,8 +275,8 @@ def prefill_leg(dev, reps=10, warmup=3):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
-        step_ms = event_ms(lb.prefill_step, step_args)
-        attn_ms = event_ms(lb.prefill_attention, attn_args)
+        step_ms = event_ms(step_fn, step_args)
+        attn_ms = event_ms(attn_fn, attn_args)
         if int(err.item()) != 0:
             raise RuntimeError(f"prefill leg {name}: device error word {int(err.item()):#x}")
         f = prefill_flops(w)
@@ -392,7 +403,8 @@ def main():
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="only the prefill leg (prefill, prefill_fp8, chunked_prefill), as JSON")
+                    help="only the prefill leg (prefill, prefill_fp8, chunked_prefill, "
+                         "ragged_prefill), as JSON")
     ap.add_argument("--no-xcd-weights", action="store_true",
                     help="equal worker shares only (skip the per-XCD rate calibration)")
     ap.add_argument("--quick", action="store_true",

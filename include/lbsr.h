@@ -80,6 +80,9 @@ typedef enum { LBSR_OUT_BF16 = 0, LBSR_OUT_FP8_E4M3 = 1 } lbsr_out_dtype;
 #define LBSR_DEV_ERR_SEQ_LEN 1   /* seq_len outside [1, max_blocks_per_seq*64]: clamped */
 #define LBSR_DEV_ERR_PAGE 2      /* block-table entry outside [0, num_pages): page 0 used */
 #define LBSR_DEV_ERR_POSITION 4  /* position outside [0, max_blocks_per_seq*64): write skipped */
+#define LBSR_DEV_ERR_QUERY_START 8 /* varlen prefill: q_start range of a sequence malformed
+                                      (negative, decreasing, past total_tokens or longer
+                                      than shape->tokens_per_seq): sequence skipped */
 
 /*
  * Cache page layout ([A] "Why does dynamic scheduling matter in attention?"
@@ -300,7 +303,7 @@ lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
  * and v already in the cache) attends rows [0, L_b - Tq + t]:
  *   out[b][t][h]     = sum_j softmax_j(sm_scale * <q_out[b][t][h], K_j>) V_j
  *   lse_out[b][t][h] = ln sum_j exp(sm_scale * <q_out[b][t][h], K_j>)
- * One pass per (sequence, KV head, block of 128/G new tokens) over its causal
+ * One pass per (sequence, KV head, block of 256/G new tokens) over its causal
  * range, each K/V tile read once per block: no schedule, no workspace.
  *   q_out [batch][Tq][Hq][128] BF16        seq_lens [batch] int32 (device)
  *   out   [batch][Tq][Hq][128] BF16, or E4M3 codes (params->out_dtype)
@@ -326,6 +329,63 @@ lbsr_status lbsr_prefill_step(const lbsr_shape *shape, const lbsr_params *params
                               const int32_t *block_table, void *k_cache, void *v_cache,
                               void *q_out, void *out, float *lse_out, int32_t *error_word,
                               void *stream);
+
+/*
+ * Ragged ("varlen") prefill: sequence b has its own count n_b >= 0 of new
+ * tokens, as in a chunked-prefill batch of prompts of different lengths
+ * ([B] "Why is this good?": prefill and mixed batches).  The new tokens of
+ * all sequences are packed along one token axis of total_tokens rows:
+ *   q_start  [batch + 1] int32 (device): sequence b's new tokens are rows
+ *            [q_start[b], q_start[b+1]) of q_out / out / lse_out; q_start[0]
+ *            = 0, non-decreasing, q_start[batch] = total_tokens;
+ *   q_out, out [total_tokens][Hq][128]; lse_out nullable [total_tokens][Hq].
+ * shape->tokens_per_seq is an upper bound on every n_b.  New token t of
+ * sequence b (position L_b - n_b + t) attends rows [0, L_b - n_b + t], as in
+ * lbsr_prefill_attention with Tq = n_b.
+ * workspace: device memory of lbsr_prefill_varlen_workspace_size bytes,
+ * 256-byte aligned, caller-owned, overwritten by every call (so calls that
+ * share one must be ordered).  A first launch writes there the list of
+ * (sequence, block of 256/G new tokens) work items sorted by the rows they
+ * attend, longest first; the attention launch runs one workgroup per (item,
+ * KV head) in that order.  (Workgroups reach compute units in a fixed
+ * rotation by index: a grid ordered by sequence, or holding empty blocks,
+ * binds CUs to the same few sequences and idles the rest.)  A sequence whose q_start range is
+ * malformed (negative, decreasing, past total_tokens, or n_b above the bound)
+ * is skipped and flags LBSR_DEV_ERR_QUERY_START; its out rows are not
+ * written.  total_tokens = 0 launches nothing.  A mixed batch runs its
+ * decoding sequences through lbsr_decode_step (length-balanced split KV) and
+ * its prompts through this call, on one stream; one-token sequences are also
+ * accepted here, without the split.
+ */
+lbsr_status lbsr_prefill_attention_varlen(const lbsr_shape *shape, const lbsr_params *params,
+                                          int32_t batch, int32_t total_tokens,
+                                          const int32_t *q_start, const void *q_out,
+                                          const void *k_cache, const void *v_cache,
+                                          const int32_t *block_table, const int32_t *seq_lens,
+                                          void *workspace, size_t ws_bytes, void *out,
+                                          float *lse_out, int32_t *error_word, void *stream);
+
+/* Bytes of a ragged prefill's workspace: 256 + 8 * (ceil(total_tokens * G /
+ * 256) + batch).  Host only. */
+lbsr_status lbsr_prefill_varlen_workspace_size(const lbsr_shape *shape, int32_t batch,
+                                               int32_t total_tokens, size_t *bytes);
+
+/*
+ * A ragged prefill step: the prologue on all total_tokens packed new tokens
+ * (q [total_tokens][Hq][128], k/v [total_tokens][Hkv][128], positions
+ * [total_tokens] with positions[q_start[b] + t] = seq_lens[b] - n_b + t; a
+ * token's sequence, for its block-table row, is found from q_start), then
+ * lbsr_prefill_attention_varlen, on one stream.
+ */
+lbsr_status lbsr_prefill_step_varlen(const lbsr_shape *shape, const lbsr_params *params,
+                                     int32_t batch, int32_t total_tokens,
+                                     const int32_t *q_start, const void *q, const void *k,
+                                     const void *v, const int32_t *positions,
+                                     const int32_t *seq_lens, const void *q_norm_w,
+                                     const void *k_norm_w, const int32_t *block_table,
+                                     void *k_cache, void *v_cache, void *q_out,
+                                     void *workspace, size_t ws_bytes, void *out,
+                                     float *lse_out, int32_t *error_word, void *stream);
 
 /*
  * Benchmark helper: lbsr_decode_step with a HIP event recorded on `stream`

@@ -27,14 +27,15 @@ OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 KV_BF16, KV_FP8_E4M3 = 0, 1
 SCHED_DYNAMIC, SCHED_STATIC = 0, 1
 OUT_BF16, OUT_FP8_E4M3 = 0, 1
-DEV_ERR_SEQ_LEN, DEV_ERR_PAGE, DEV_ERR_POSITION = 1, 2, 4
+DEV_ERR_SEQ_LEN, DEV_ERR_PAGE, DEV_ERR_POSITION, DEV_ERR_QUERY_START = 1, 2, 4, 8
 
 # Every symbol include/lbsr.h declares.
 EXPORTS = (
     "lbsr_abi_version", "lbsr_status_string", "lbsr_last_error", "lbsr_device_workers",
     "lbsr_workspace_layout", "lbsr_workspace_size", "lbsr_rope_norm_kv_write", "lbsr_plan",
     "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed", "lbsr_prefill_attention",
-    "lbsr_prefill_step",
+    "lbsr_prefill_step", "lbsr_prefill_attention_varlen", "lbsr_prefill_step_varlen",
+    "lbsr_prefill_varlen_workspace_size",
 )
 
 
@@ -115,6 +116,13 @@ def _declare(lib):
                                    + [_P] * 9),
         "lbsr_prefill_step": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                               + [_P] * 15),
+        "lbsr_prefill_attention_varlen": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params),
+                                               _I32, _I32] + [_P] * 7 + [ctypes.c_size_t]
+                                              + [_P] * 4),
+        "lbsr_prefill_step_varlen": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32,
+                                          _I32] + [_P] * 13 + [ctypes.c_size_t] + [_P] * 4),
+        "lbsr_prefill_varlen_workspace_size": (st, [ctypes.POINTER(Shape), _I32, _I32,
+                                                    ctypes.POINTER(ctypes.c_size_t)]),
         "lbsr_decode_step_timed": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                                    + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t,
                                                   _P, _P, _P, ctypes.POINTER(ctypes.c_float), _P]),

@@ -104,6 +104,11 @@ lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
     return fail(LBSR_E_INVALID, "max_blocks_per_seq %d < 1", s->max_blocks_per_seq);
   if ((int64_t)s->max_blocks_per_seq * LBSR_PAGE_SIZE > INT32_MAX)
     return fail(LBSR_E_INVALID, "max_blocks_per_seq %d too large", s->max_blocks_per_seq);
+  // every sequence holds its new tokens, so they fit the block table's reach
+  // (kernels clamp lengths up to the token count and walk that many rows)
+  if ((int64_t)s->tokens_per_seq > (int64_t)s->max_blocks_per_seq * LBSR_PAGE_SIZE)
+    return fail(LBSR_E_INVALID, "tokens_per_seq %d > max_blocks_per_seq %d x %d rows",
+                s->tokens_per_seq, s->max_blocks_per_seq, LBSR_PAGE_SIZE);
   if (s->num_pages < 1 || s->num_pages > INT32_MAX)
     return fail(LBSR_E_INVALID, "num_pages %lld out of [1, 2^31)", (long long)s->num_pages);
   if (s->page_stride < LBSR_TILE_ELEMS || s->page_stride % LBSR_TILE_ELEMS ||
@@ -324,14 +329,17 @@ const lbsr::RopeFreqs& rope_freqs(double theta) {
 lbsr_status run_prologue(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
                          const void* q, const void* k, const void* v, const int32_t* positions,
                          const void* wq, const void* wk, const int32_t* bt, void* kc, void* vc,
-                         void* q_out, int32_t* error_word, hipStream_t stream) {
+                         void* q_out, int32_t* error_word, hipStream_t stream,
+                         int32_t total_tokens = -1, const int32_t* q_start = nullptr) {
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
+  const int num_tokens = q_start ? total_tokens : batch * shape->tokens_per_seq;
   return hip_status(lbsr::launch_prologue(geo, fp8, q, k, v, positions, wq, wk, bt, kc, vc, q_out,
                                           error_word, rope_freqs(params->rope_theta),
                                           (double)params->rms_eps,
                                           params->norm_before_rope, fp8 ? params->k_scale : 1.0,
-                                          fp8 ? params->v_scale : 1.0, stream),
+                                          fp8 ? params->v_scale : 1.0, num_tokens, q_start,
+                                          stream),
                     "prologue launch");
 }
 
@@ -411,7 +419,8 @@ lbsr_status run_combine(const lbsr_shape* shape, const lbsr_params* params, int3
 lbsr_status run_prefill(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
                         const void* q_out, const void* kc, const void* vc, const int32_t* bt,
                         const int32_t* seq_lens, void* out, float* lse_out, int32_t* error_word,
-                        hipStream_t stream) {
+                        hipStream_t stream, int32_t total_tokens = -1,
+                        const int32_t* q_start = nullptr, void* work = nullptr) {
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
   const bool out_fp8 = params->out_dtype == LBSR_OUT_FP8_E4M3;
@@ -419,7 +428,8 @@ lbsr_status run_prefill(const lbsr_shape* shape, const lbsr_params* params, int3
   const float o_scale = (float)(out_fp8 ? vs / (double)params->out_scale : vs);
   return hip_status(lbsr::launch_prefill(geo, fp8, out_fp8, q_out, kc, vc, bt, seq_lens, out,
                                          lse_out, score_scale_log2(params, shape->kv_dtype),
-                                         o_scale, error_word, stream),
+                                         o_scale, error_word, q_start, total_tokens,
+                                         (int32_t*)work, stream),
                     "prefill launch");
 }
 
@@ -441,6 +451,29 @@ lbsr_status validate_prefill(const lbsr_shape* shape, const lbsr_params* params,
   const int64_t per = lbsr::kPrefillColumns / (shape->num_q_heads / shape->num_kv_heads);
   const int64_t grid = (shape->tokens_per_seq + per - 1) / per * batch * shape->num_kv_heads;
   if (grid > INT32_MAX) return fail(LBSR_E_UNSUPPORTED, "prefill grid of %lld workgroups", (long long)grid);
+  return LBSR_OK;
+}
+
+// Bytes of a ragged prefill's workspace: header + one int2 per work item.
+size_t varlen_workspace_bytes(const lbsr_shape* shape, int32_t batch, int32_t total_tokens) {
+  const int64_t tpb = lbsr::kPrefillColumns / (shape->num_q_heads / shape->num_kv_heads);
+  const int64_t items = (total_tokens + tpb - 1) / tpb + batch;
+  return (size_t)lbsr::kPrefillListOffset + 8 * (size_t)items;
+}
+
+// The ragged batch's extra arguments: the packed token count, q_start and the
+// workspace of the work list.
+lbsr_status validate_varlen(const lbsr_shape* shape, int32_t batch, int32_t total_tokens,
+                            const int32_t* q_start, void* ws, size_t ws_bytes) {
+  if (total_tokens < 0) return fail(LBSR_E_INVALID, "total_tokens %d < 0", total_tokens);
+  const int64_t rows = shape->num_q_heads + 2 * shape->num_kv_heads;
+  if ((int64_t)total_tokens * rows > INT32_MAX / 2)
+    return fail(LBSR_E_UNSUPPORTED, "total_tokens %d is too many rows", total_tokens);
+  LBSR_CHECK(check_ptr(q_start, 4, "q_start"));
+  LBSR_CHECK(check_ptr(ws, 256, "workspace"));
+  const size_t need = varlen_workspace_bytes(shape, batch, total_tokens);
+  if (ws_bytes < need)
+    return fail(LBSR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return LBSR_OK;
 }
 
@@ -624,6 +657,61 @@ lbsr_status lbsr_prefill_step(const lbsr_shape* shape, const lbsr_params* params
                           block_table, k_cache, v_cache, q_out, error_word, s));
   return run_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table, seq_lens, out,
                      lse_out, error_word, s);
+}
+
+lbsr_status lbsr_prefill_attention_varlen(const lbsr_shape* shape, const lbsr_params* params,
+                                          int32_t batch, int32_t total_tokens,
+                                          const int32_t* q_start, const void* q_out,
+                                          const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          void* workspace, size_t ws_bytes, void* out,
+                                          float* lse_out, int32_t* error_word, void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(validate_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table,
+                              seq_lens, out, lse_out, error_word));
+  LBSR_CHECK(validate_varlen(shape, batch, total_tokens, q_start, workspace, ws_bytes));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  if (total_tokens == 0) return LBSR_OK;
+  return run_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table, seq_lens, out,
+                     lse_out, error_word, (hipStream_t)stream, total_tokens, q_start,
+                     workspace);
+}
+
+lbsr_status lbsr_prefill_varlen_workspace_size(const lbsr_shape* shape, int32_t batch,
+                                               int32_t total_tokens, size_t* bytes) {
+  g_last_error[0] = 0;
+  if (!bytes) return fail(LBSR_E_INVALID, "bytes is null");
+  LBSR_CHECK(check_shape(shape, batch));
+  if (total_tokens < 0) return fail(LBSR_E_INVALID, "total_tokens %d < 0", total_tokens);
+  *bytes = varlen_workspace_bytes(shape, batch, total_tokens);
+  return LBSR_OK;
+}
+
+lbsr_status lbsr_prefill_step_varlen(const lbsr_shape* shape, const lbsr_params* params,
+                                     int32_t batch, int32_t total_tokens,
+                                     const int32_t* q_start, const void* q, const void* k,
+                                     const void* v, const int32_t* positions,
+                                     const int32_t* seq_lens, const void* q_norm_w,
+                                     const void* k_norm_w, const int32_t* block_table,
+                                     void* k_cache, void* v_cache, void* q_out,
+                                     void* workspace, size_t ws_bytes, void* out,
+                                     float* lse_out, int32_t* error_word, void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(validate_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
+                               block_table, k_cache, v_cache, q_out, error_word));
+  LBSR_CHECK(validate_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table,
+                              seq_lens, out, lse_out, error_word));
+  LBSR_CHECK(validate_varlen(shape, batch, total_tokens, q_start, workspace, ws_bytes));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  if (total_tokens == 0) return LBSR_OK;
+  const hipStream_t s = (hipStream_t)stream;
+  LBSR_CHECK(run_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
+                          block_table, k_cache, v_cache, q_out, error_word, s, total_tokens,
+                          q_start));
+  return run_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table, seq_lens, out,
+                     lse_out, error_word, s, total_tokens, q_start, workspace);
 }
 
 lbsr_status lbsr_decode_step(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,

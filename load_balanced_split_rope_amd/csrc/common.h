@@ -25,6 +25,8 @@ constexpr int kPrefillWaves = LBSR_PREFILL_WAVES;
 #endif
 constexpr int kPrefillBlocks = LBSR_PREFILL_BLOCKS;
 constexpr int kPrefillColumns = kPrefillWaves * 16 * kPrefillBlocks;   // per workgroup
+constexpr int kPrefillBuckets = 4096;  // tile-count buckets of the ragged prefill's work list
+constexpr int kPrefillListOffset = 256;  // work list after a 256-byte header in its workspace
 constexpr int kMergeLdsBytes = 65536;  // the merge stages chunks x columns weights in LDS
 constexpr int kMaxBatch = 16384;   // the plan keeps per-sequence prefix sums in LDS
 constexpr int kPlanThreads = 1024;
@@ -33,7 +35,7 @@ constexpr int kMaxAttnWaves = 8;   // waves (KV heads in flight) per attention w
 constexpr int kXcds = 8;           // an MI355X has 8 XCDs; workgroup i is dispatched to XCD i % 8
 constexpr int kMaxXcdWeight = 65536;
 
-enum : int32_t { kErrSeqLen = 1, kErrPage = 2, kErrPosition = 4 };
+enum : int32_t { kErrSeqLen = 1, kErrPage = 2, kErrPosition = 4, kErrQueryStart = 8 };
 
 // Number of the P attention workgroups that land on XCD x (those i < P with
 // i % 8 == x).  Workers are handed out so that XCD x runs a contiguous range

@@ -7,12 +7,14 @@
 
 namespace lbsr {
 
+// num_tokens: batch * Tq, or the packed count of a ragged batch (q_start
+// non-null: token -> sequence by binary search).
 hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const void* k,
                            const void* v, const int32_t* positions, const void* wq,
                            const void* wk, const int32_t* block_table, void* k_cache,
                            void* v_cache, void* q_out, int32_t* error_word, const RopeFreqs& freqs,
                            double eps, int norm_first, double k_scale, double v_scale,
-                           hipStream_t stream);
+                           int num_tokens, const int32_t* q_start, hipStream_t stream);
 
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, const SchedParams& sp,
                        const PlanPtrs& plan, hipStream_t stream);
@@ -31,11 +33,19 @@ hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, 
                           int max_chunks_per_seq, bool out_fp8, bool fold_token_status,
                           hipStream_t stream);
 
+// q_start non-null: ragged batch, sequence b's new tokens at packed rows
+// [q_start[b], q_start[b+1]) of total_tokens; geo.tokens bounds every count.
+// A plan launch first writes the longest-first work list into `work`
+// (kPrefillListOffset + 8 * prefill_max_items bytes).
 hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const void* q_out,
                           const void* k_cache, const void* v_cache, const int32_t* block_table,
                           const int32_t* seq_lens, void* out, float* lse_out,
                           float score_scale_log2, float out_scale, int32_t* error_word,
+                          const int32_t* q_start, int total_tokens, int32_t* work,
                           hipStream_t stream);
+
+// Work-list entries a ragged prefill may need: one per block of new tokens.
+int prefill_max_items(const Geometry& geo, int total_tokens);
 
 hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 const PlanPtrs& plan, const Geometry& geo,

@@ -4,7 +4,9 @@
 // well as decode.  The step's new tokens (Tq per sequence, token j at position
 // L - Tq + j, its k and v already written by the prologue) attend causally:
 // token j sees rows [0, L - Tq + j].  With a prefix in the cache this is
-// chunked prefill; with L = Tq it is a plain prefill.
+// chunked prefill; with L = Tq it is a plain prefill.  Ragged batches give
+// each sequence its own Tq through q_start (the packed rows of sequence b are
+// [q_start[b], q_start[b+1])); geo.tokens is then the bound on any Tq.
 //
 // Mapping on CDNA4:
 //   * workgroup = (sequence b, KV head g, block of 256 (token, head) columns,
@@ -23,8 +25,14 @@
 //     goes straight to the output: no partials, no merge.
 //   * workgroups are numbered longest-first (the blocks of the last tokens
 //     see the most rows), so the dispatcher starts the long ones first.
+//     Workgroups reach CUs in a fixed rotation by index, not greedily: a
+//     grid that interleaves blocks of unequal length (or empty ones) leaves
+//     CUs idle, each bound to the same few sequences.  A ragged batch is
+//     therefore dispatched from a work list that a one-workgroup plan sorts
+//     by tile count, longest first, with no empty entries (prefill_plan_kernel).
 
 #include "launch.h"
+#include "plan.h"
 #include "tile_math.h"
 
 namespace lbsr {
@@ -35,22 +43,48 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, void* __restrict__ out, float* __restrict__ lse_out,
     float score_scale_log2, float out_scale, int out_fp8, int32_t* __restrict__ error_word,
-    int num_blocks_q) {
+    int num_blocks_q, const int32_t* __restrict__ q_start, int total_tokens,
+    const int32_t* __restrict__ work) {
   constexpr int NF = kFp8 ? 8 : 16;                  // 1 KiB fragments per K (or V) tile
   constexpr int kStage = 2 * NF * kWave;             // u32x4 per stage: K then V
   constexpr int kPerThread = kStage / (kPrefillWaves * kWave);   // 4 (BF16) or 2 (FP8)
   constexpr int kElemBytes = kFp8 ? 1 : 2;
   __shared__ u32x4 s_kv[2][kStage];                  // 64 KiB (BF16) / 32 KiB (FP8)
 
-  const int T = geo.tokens, G = geo.group, Hq = geo.num_q_heads;
-  const int per_block = geo.batch * geo.num_kv_heads;
-  const int qb = num_blocks_q - 1 - (int)(blockIdx.x / per_block);   // last blocks first
-  const int bg = (int)(blockIdx.x % per_block);
-  const int b = bg / geo.num_kv_heads, g = bg - b * geo.num_kv_heads;
+  const int G = geo.group, Hq = geo.num_q_heads;
+  int qb, b, g;
+  if (work) {                    // ragged batch: item blockIdx / Hkv of the sorted list
+    const int item = (int)(blockIdx.x / geo.num_kv_heads);
+    g = (int)(blockIdx.x % geo.num_kv_heads);
+    if (item >= work[0]) return;                     // past the list: the whole workgroup leaves
+    const int2 it = ((const int2*)((const char*)work + kPrefillListOffset))[item];
+    b = it.x;
+    qb = it.y;
+  } else {
+    const int per_block = geo.batch * geo.num_kv_heads;
+    qb = num_blocks_q - 1 - (int)(blockIdx.x / per_block);   // last blocks first
+    const int bg = (int)(blockIdx.x % per_block);
+    b = bg / geo.num_kv_heads;
+    g = bg - b * geo.num_kv_heads;
+  }
   const int tokens_per_block = kPrefillColumns / G;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, kc = lane >> 4;
+
+  // this sequence's new tokens: T of them, at packed rows first_row + [0, T)
+  int T = geo.tokens;
+  size_t first_row = (size_t)b * T;
+  if (q_start) {
+    const int s0 = q_start[b], s1 = q_start[b + 1];
+    if (s0 < 0 || s1 < s0 || s1 > total_tokens || s1 - s0 > geo.tokens) {
+      if (tid == 0 && qb == 0 && g == 0 && error_word) atomicOr(error_word, (int32_t)kErrQueryStart);
+      return;                                        // the whole workgroup leaves
+    }
+    T = s1 - s0;
+    first_row = (size_t)s0;
+  }
+  if (qb * tokens_per_block >= T) return;            // a block past this sequence's tokens
 
   // length: at least the new tokens, at most the block table's reach
   const int max_len = geo.max_blocks * kPage;
@@ -75,7 +109,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     valid[cb] = gc < tokens_per_block * G && jt[cb] < T;
     limit[cb] = L - T + jt[cb] + 1;                 // the column attends rows < limit
     if (valid[cb]) {
-      const u32x4* qp = (const u32x4*)(q_out + (((size_t)b * T + jt[cb]) * Hq + (size_t)g * G +
+      const u32x4* qp = (const u32x4*)(q_out + ((first_row + jt[cb]) * Hq + (size_t)g * G +
                                                 hl[cb]) * kHeadDim) + kc;
 #pragma unroll
       for (int s = 0; s < 4; ++s) qB[cb][s] = as_bf16x8(qp[4 * s]);
@@ -195,7 +229,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     const float l = sum_xor32(sum_xor16(st[cb].lsum));
     const float scale = l > 0.f ? out_scale / l : 0.f;
     if (!valid[cb]) continue;
-    const size_t orow = ((size_t)b * T + jt[cb]) * Hq + (size_t)g * G + hl[cb];
+    const size_t orow = (first_row + jt[cb]) * Hq + (size_t)g * G + hl[cb];
     if (out_fp8) {
       uint8_t* o = (uint8_t*)out + orow * kHeadDim + 4 * kc;
 #pragma unroll
@@ -216,7 +250,81 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     if (kc == 0 && lse_out)
       lse_out[orow] = (l > 0.f ? st[cb].m + __builtin_amdgcn_logf(l) : -__builtin_inff()) * kLn2;
   }
-  if (tid == 0 && L != L_in && error_word && qb == 0 && g == 0) atomicOr(error_word, (int32_t)kErrSeqLen);
+  if (tid == 0 && L != L_in && error_word && qb == 0 && g == 0)
+    atomicOr(error_word, (int32_t)kErrSeqLen);
+}
+
+// The ragged batch's work list: every (sequence, block of new tokens) with at
+// least one token, sorted by its tile count (the rows its last token attends,
+// in 64-row tiles), longest first -- a counting sort over tile-count buckets
+// (tiles >> shift), in one 1024-thread workgroup.  Layout of `work`: [0] item
+// count, then from byte kPrefillListOffset int2 (sequence, block) pairs, at
+// most max_items of them.  Order within a bucket is arrival order; it decides
+// only which workgroup runs an item, not any result.
+__device__ inline bool ragged_range(const int32_t* q_start, const int32_t* seq_lens, int b,
+                                    int total_tokens, int bound, int max_len, int& T, int& L) {
+  const int s0 = q_start[b], s1 = q_start[b + 1];
+  if (s0 < 0 || s1 < s0 || s1 > total_tokens || s1 - s0 > bound) return false;
+  T = s1 - s0;
+  const int L_in = seq_lens[b];
+  L = L_in < T ? T : (L_in > max_len ? max_len : L_in);
+  return true;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+    Geometry geo, const int32_t* __restrict__ q_start, const int32_t* __restrict__ seq_lens,
+    int total_tokens, int32_t* __restrict__ work, int max_items, int shift,
+    int32_t* __restrict__ error_word) {
+  __shared__ int s_bucket[kPrefillBuckets];
+  __shared__ int s_wave[kPlanThreads / kWave + 1];
+  const int tid = threadIdx.x;
+  const int tpb = kPrefillColumns / geo.group;
+  const int max_len = geo.max_blocks * kPage;
+  auto bucket_of = [&](int T, int L, int qb) {
+    const int tok_end = (qb + 1) * tpb < T ? (qb + 1) * tpb : T;
+    const int tiles = (L - T + tok_end + kPage - 1) / kPage;
+    const int k = tiles >> shift;
+    return kPrefillBuckets - 1 - (k < kPrefillBuckets ? k : kPrefillBuckets - 1);  // longest first
+  };
+  for (int i = tid; i < kPrefillBuckets; i += kPlanThreads) s_bucket[i] = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int b = tid; b < geo.batch; b += kPlanThreads) {
+    int T, L;
+    if (!ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L)) {
+      bad = true;
+      continue;
+    }
+    for (int qb = 0; qb * tpb < T; ++qb) atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
+  }
+  __syncthreads();
+  // exclusive offsets over the buckets: thread t owns buckets [4t, 4t + 4)
+  constexpr int kPer = kPrefillBuckets / kPlanThreads;
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) local += s_bucket[kPer * tid + i];
+  int total = 0;
+  int off = block_inclusive_scan(local, s_wave, total) - local;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = s_bucket[kPer * tid + i];
+    s_bucket[kPer * tid + i] = off;
+    off += c;
+  }
+  __syncthreads();
+  int2* list = (int2*)((char*)work + kPrefillListOffset);
+  for (int b = tid; b < geo.batch; b += kPlanThreads) {
+    int T, L;
+    if (!ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L)) continue;
+    for (int qb = 0; qb * tpb < T; ++qb) {
+      const int pos = atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
+      if (pos < max_items) list[pos] = make_int2(b, qb);
+    }
+  }
+  // overlapping ranges (a malformed q_start) can give more items than the list holds
+  if (tid == 0) work[0] = total < max_items ? total : max_items;
+  if (error_word && (bad || (tid == 0 && total > max_items)))
+    atomicOr(error_word, (int32_t)kErrQueryStart);
 }
 
 int prefill_blocks_q(const Geometry& geo) {
@@ -224,18 +332,32 @@ int prefill_blocks_q(const Geometry& geo) {
   return (geo.tokens + per - 1) / per;
 }
 
+int prefill_max_items(const Geometry& geo, int total_tokens) {
+  const int tpb = kPrefillColumns / geo.group;
+  return (total_tokens + tpb - 1) / tpb + geo.batch;
+}
+
 hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const void* q_out,
                           const void* k_cache, const void* v_cache, const int32_t* block_table,
                           const int32_t* seq_lens, void* out, float* lse_out,
                           float score_scale_log2, float out_scale, int32_t* error_word,
+                          const int32_t* q_start, int total_tokens, int32_t* work,
                           hipStream_t stream) {
   const int nqb = prefill_blocks_q(geo);
-  const size_t grid = (size_t)nqb * geo.batch * geo.num_kv_heads;
+  size_t grid = (size_t)nqb * geo.batch * geo.num_kv_heads;
+  if (q_start) {
+    const int max_items = prefill_max_items(geo, total_tokens);
+    int shift = 0;
+    while ((geo.max_blocks >> shift) >= kPrefillBuckets) ++shift;
+    prefill_plan_kernel<<<1, kPlanThreads, 0, stream>>>(geo, q_start, seq_lens, total_tokens,
+                                                         work, max_items, shift, error_word);
+    grid = (size_t)max_items * geo.num_kv_heads;
+  }
   auto launch = [&](auto kernel) {
     kernel<<<(unsigned)grid, kPrefillWaves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
         block_table, seq_lens, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0,
-        error_word, nqb);
+        error_word, nqb, q_start, total_tokens, q_start ? work : nullptr);
   };
   if (fp8) launch(prefill_kernel<true>);
   else launch(prefill_kernel<false>);

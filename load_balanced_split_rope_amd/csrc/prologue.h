@@ -218,6 +218,18 @@ __device__ inline void prologue_rows(
   }
 }
 
+// Sequence of packed new token `tok` in a ragged batch: the last b with
+// q_start[b] <= tok.  Any q_start contents give an index in [0, batch).
+__device__ inline int seq_of_token(const int32_t* __restrict__ q_start, int batch, int tok) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (q_start[mid] <= tok) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // How many runs each token's rows are cut into: enough waves to fill the GPU
 // a few times over (one row per wave when the tokens are few, as in decode),
 // a whole token per wave when they are many, as in prefill.

@@ -296,6 +296,86 @@ def prefill_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_no
         B._ptr(lse_out), B._ptr(error_word), B._stream(stream)))
 
 
+def prefill_varlen_workspace_size(cfg: DecodeConfig, batch: int, total_tokens: int) -> int:
+    """Bytes of a ragged prefill's workspace (its longest-first work list)."""
+    n = ctypes.c_size_t()
+    s = cfg.shape()
+    B._check(B.lib().lbsr_prefill_varlen_workspace_size(ctypes.byref(s), batch, total_tokens,
+                                                        ctypes.byref(n)))
+    return n.value
+
+
+def alloc_prefill_workspace(cfg: DecodeConfig, batch: int, total_tokens: int, device="cuda"):
+    n = prefill_varlen_workspace_size(cfg, batch, total_tokens)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _check_varlen(cfg, q_start, batch, total, workspace):
+    _need(q_start, "q_start", torch.int32, shape=(batch + 1,))
+    if total < 0:
+        raise ValueError(f"total_tokens {total} < 0")
+    _need(workspace, "workspace", torch.uint8)
+
+
+def prefill_attention_varlen(cfg: DecodeConfig, q_start, q_out, k_cache, v_cache, block_table,
+                             seq_lens, workspace, out, lse_out=None, error_word=None,
+                             stream=None):
+    """lbsr_prefill_attention_varlen: a ragged batch.  Sequence b's new tokens
+    are packed rows [q_start[b], q_start[b+1]) of q_out/out [N, Hq, D];
+    cfg.tokens_per_seq bounds every sequence's count; workspace from
+    alloc_prefill_workspace."""
+    batch, total = seq_lens.shape[0], q_out.shape[0]
+    Hq, D = cfg.num_q_heads, B.HEAD_DIM
+    _check_varlen(cfg, q_start, batch, total, workspace)
+    _need(q_out, "q_out", torch.bfloat16, shape=(total, Hq, D))
+    _need(out, "out", cfg.out_torch_dtype, shape=(total, Hq, D))
+    _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, shape=(total, Hq))
+    if error_word is not None:
+        _need(error_word, "error_word", torch.int32, numel=1)
+    _check_table(cfg, block_table, batch)
+    _check_pools(cfg, k_cache, v_cache)
+    s, p = cfg.shape(), cfg.params()
+    B._check(B.lib().lbsr_prefill_attention_varlen(
+        ctypes.byref(s), ctypes.byref(p), batch, total, B._ptr(q_start), B._ptr(q_out),
+        B._ptr(k_cache), B._ptr(v_cache), B._ptr(block_table), B._ptr(seq_lens),
+        B._ptr(workspace), workspace.numel(), B._ptr(out), B._ptr(lse_out), B._ptr(error_word),
+        B._stream(stream)))
+
+
+def prefill_step_varlen(cfg: DecodeConfig, q_start, q, k, v, positions, seq_lens, q_norm_w,
+                        k_norm_w, block_table, k_cache, v_cache, q_out, workspace, out,
+                        lse_out=None, error_word=None, stream=None):
+    """lbsr_prefill_step_varlen: the prologue on every packed new token, then
+    ragged prefill attention."""
+    batch, total = seq_lens.shape[0], q.shape[0]
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, B.HEAD_DIM
+    _check_varlen(cfg, q_start, batch, total, workspace)
+    _need(q, "q", torch.bfloat16, shape=(total, Hq, D))
+    _need(k, "k", torch.bfloat16, shape=(total, Hkv, D))
+    _need(v, "v", torch.bfloat16, shape=(total, Hkv, D))
+    _need(q_out, "q_out", torch.bfloat16, shape=(total, Hq, D))
+    _need(out, "out", cfg.out_torch_dtype, shape=(total, Hq, D))
+    _need(positions, "positions", torch.int32, shape=(total,))
+    _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
+    _need(q_norm_w, "q_norm_w", torch.bfloat16, shape=(D,))
+    _need(k_norm_w, "k_norm_w", torch.bfloat16, shape=(D,))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, shape=(total, Hq))
+    if error_word is not None:
+        _need(error_word, "error_word", torch.int32, numel=1)
+    _check_table(cfg, block_table, batch)
+    _check_pools(cfg, k_cache, v_cache)
+    s, p = cfg.shape(), cfg.params()
+    B._check(B.lib().lbsr_prefill_step_varlen(
+        ctypes.byref(s), ctypes.byref(p), batch, total, B._ptr(q_start), B._ptr(q), B._ptr(k),
+        B._ptr(v), B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
+        B._ptr(block_table), B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out),
+        B._ptr(workspace), workspace.numel(), B._ptr(out), B._ptr(lse_out), B._ptr(error_word),
+        B._stream(stream)))
+
+
 def read_plan(cfg: DecodeConfig, batch: int, sched: Schedule, workspace):
     """Copy the plan arrays out of a workspace (synchronises; for tests and tools)."""
     lay = workspace_layout(cfg, batch, sched)

@@ -20,6 +20,9 @@ head dim 128; 64-token pages):
 * ``prefill_fp8`` the same with an FP8 E4M3 cache
 * ``chunked_prefill``  32 sequences of 4608 tokens whose last 512 are new
                   (a 512-token prefill chunk after a 4096-token prefix)
+* ``ragged_prefill``  8 prompts with their own chunk lengths (8192, 4096,
+                  2048, 1024, 512, 3072, 6144, 700 new tokens) after prefixes
+                  of 0, 4096, 0, 8192, 0, 1024, 0, 20000 tokens (packed)
 
 Recipe (per workload, seed s): ``numpy.random.SeedSequence(s)`` spawns child
 streams, in order: 0 lengths, 1 q, 2 k, 3 v, 4 q-norm weight, 5 k-norm weight,
@@ -30,7 +33,9 @@ T + max(16, ceil(T/16)) pages; sequence b gets pages perm[cu[b]:cu[b+1]] of a
 random permutation; unused block-table entries are -1; positions[b] = L_b - 1.
 With Tq > 1 new tokens per sequence, q, k and v gain a token axis after the
 batch axis (drawn as [B, Tq, H, D], so Tq = 1 draws the same values) and
-positions[b, j] = L_b - Tq + j.
+positions[b, j] = L_b - Tq + j.  A ragged batch (new_tokens = [n_b]) packs
+its N = sum n_b new tokens along one axis: q, k, v drawn as [N, H, D],
+positions[q_start[b] + j] = L_b - n_b + j, q_start the prefix sums of n_b.
 On a GPU the cache contents (up to 5.7 GB) are drawn on the device with a
 torch generator seeded from children 7 and 8, in fixed 2**26-element blocks.
 """
@@ -59,6 +64,7 @@ class Workload:
     norm_before_rope: bool = False
     seed: int = 0
     tokens: int = 1            # new tokens per sequence (multi-token decode)
+    new_tokens: list = None    # per-sequence new-token counts of a ragged (varlen) batch
     extra: dict = field(default_factory=dict)
 
     @property
@@ -68,6 +74,15 @@ class Workload:
     @property
     def tiles(self):
         return [-(-int(L) // PAGE) for L in self.seq_lens]
+
+    @property
+    def varlen(self):
+        return self.new_tokens is not None
+
+    @property
+    def max_new_tokens(self):
+        """The bound on any sequence's new tokens (a ragged batch's tokens_per_seq)."""
+        return max(1, max(self.new_tokens)) if self.varlen else self.tokens
 
 
 def loguniform_lengths(seed, batch=64, lo=512, hi=262144):
@@ -101,12 +116,17 @@ def named(name):
                         v_scale=2.0 ** -4, seed=9, tokens=8192)
     if name == "chunked_prefill":
         return Workload("chunked_prefill", [4608] * 32, seed=10, tokens=512)
+    if name == "ragged_prefill":
+        new = [8192, 4096, 2048, 1024, 512, 3072, 6144, 700]
+        prefix = [0, 4096, 0, 8192, 0, 1024, 0, 20000]
+        return Workload("ragged_prefill", [p + n for p, n in zip(prefix, new)], seed=11,
+                        new_tokens=new)
     raise KeyError(name)
 
 
 NAMES = ("tiny", "uniform", "mix", "mix_fp8", "loguniform")
 MULTI_TOKEN_NAMES = ("mix_mtp2", "mix_mtp4")
-PREFILL_NAMES = ("prefill", "prefill_fp8", "chunked_prefill")
+PREFILL_NAMES = ("prefill", "prefill_fp8", "chunked_prefill", "ragged_prefill")
 
 
 def _bf16(x):
@@ -164,14 +184,26 @@ def make_inputs(w: Workload, device="cpu", spare_pages=None, kv_interleave=False
     bt = np.full((B, max_blocks), -1, dtype=np.int32)
     for b in range(B):
         bt[b, :n[b]] = perm[cu[b]:cu[b + 1]]
-    Tq = int(w.tokens)
-    if Tq < 1 or np.any(lens < Tq):
-        raise ValueError("every sequence must hold its new tokens")
-    shape = (lambda H: (B, H, D)) if Tq == 1 else (lambda H: (B, Tq, H, D))
-    q = np.random.default_rng(ss[1]).standard_normal((B, Tq, Hq, D), dtype=np.float32).reshape(shape(Hq))
-    k = np.random.default_rng(ss[2]).standard_normal((B, Tq, Hkv, D), dtype=np.float32).reshape(shape(Hkv))
-    v = np.random.default_rng(ss[3]).standard_normal((B, Tq, Hkv, D), dtype=np.float32).reshape(shape(Hkv))
-    positions = (lens - 1) if Tq == 1 else lens[:, None] - Tq + np.arange(Tq)[None, :]
+    if w.varlen:
+        counts = np.asarray(w.new_tokens, dtype=np.int64)
+        if counts.shape != (B,) or np.any(counts < 0) or np.any(lens < counts):
+            raise ValueError("every sequence must hold its new tokens")
+        q_start = np.concatenate([[0], np.cumsum(counts)])
+        N = int(q_start[-1])
+        q = np.random.default_rng(ss[1]).standard_normal((N, Hq, D), dtype=np.float32)
+        k = np.random.default_rng(ss[2]).standard_normal((N, Hkv, D), dtype=np.float32)
+        v = np.random.default_rng(ss[3]).standard_normal((N, Hkv, D), dtype=np.float32)
+        positions = np.concatenate([np.arange(L - n, L) for L, n in zip(lens, counts)]
+                                   + [np.zeros(0, dtype=np.int64)])
+    else:
+        Tq = int(w.tokens)
+        if Tq < 1 or np.any(lens < Tq):
+            raise ValueError("every sequence must hold its new tokens")
+        shape = (lambda H: (B, H, D)) if Tq == 1 else (lambda H: (B, Tq, H, D))
+        q = np.random.default_rng(ss[1]).standard_normal((B, Tq, Hq, D), dtype=np.float32).reshape(shape(Hq))
+        k = np.random.default_rng(ss[2]).standard_normal((B, Tq, Hkv, D), dtype=np.float32).reshape(shape(Hkv))
+        v = np.random.default_rng(ss[3]).standard_normal((B, Tq, Hkv, D), dtype=np.float32).reshape(shape(Hkv))
+        positions = (lens - 1) if Tq == 1 else lens[:, None] - Tq + np.arange(Tq)[None, :]
     wq = 1 + 0.1 * np.random.default_rng(ss[4]).standard_normal(D, dtype=np.float32)
     wk = 1 + 0.1 * np.random.default_rng(ss[5]).standard_normal(D, dtype=np.float32)
     pool_elems = num_pages * Hkv * TILE
@@ -202,7 +234,9 @@ def make_inputs(w: Workload, device="cpu", spare_pages=None, kv_interleave=False
         "block_table": torch.from_numpy(bt).to(device),
         "k_cache": k_cache, "v_cache": v_cache,
         "num_pages": num_pages, "page_stride": page_stride, "head_stride": head_stride,
-        "max_blocks": max_blocks, "total_tiles": T, "tokens": Tq,
+        "max_blocks": max_blocks, "total_tiles": T, "tokens": w.max_new_tokens,
+        **({"q_start": torch.from_numpy(q_start.astype(np.int32)).to(device),
+            "total_tokens": N} if w.varlen else {}),
     }
 
 

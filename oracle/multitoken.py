@@ -13,6 +13,9 @@ the prefix and new tokens 0..j.  Arrays of new tokens are token-major:
 q [B, Tq, Hq, D], k and v [B, Tq, Hkv, D], positions [B, Tq]; outputs are
 [B, Tq, Hq, D] and lse [B, Tq, Hq].
 
+Ragged batches (R22, at the end of this module) give every sequence its own
+number of new tokens, packed along one token axis.
+
 The prologue and the per-sequence KV gather are the single-token ones applied
 to the flattened token list (``step.prologue`` / ``step._sequence_kv``); what
 is new here is the causal limit per token and the chunk partial of a token
@@ -128,3 +131,66 @@ def split_attention_tokens(q_out_bits, pools, pro, seq_lens, block_table, cfg, p
         for j in range(Tq):
             o[b, j], lse[b, j] = combine_lse(po[:, j], pl[:, j])
     return o, lse, partials
+
+
+# ---------------------------------------------------------------------------
+# Ragged batches (reading R22): sequence b has its own count n_b >= 0 of new
+# tokens.  The new tokens of all sequences are packed along one axis: those of
+# sequence b are rows q_start[b] .. q_start[b+1]-1, q_start being the running
+# sum of the counts.  New token j of sequence b sits at position L_b - n_b + j
+# and attends rows [0, L_b - n_b + j], exactly as R20 with Tq = n_b.
+
+def query_starts(new_tokens):
+    """q_start[b] = n_0 + ... + n_{b-1}, b = 0..B (so q_start[B] = N)."""
+    counts = np.asarray(new_tokens, dtype=np.int64)
+    if np.any(counts < 0):
+        raise ValueError("negative new-token count")
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+
+
+def varlen_positions(seq_lens, new_tokens):
+    """Packed positions: the new tokens of sequence b are L_b - n_b, ..., L_b - 1."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    counts = np.asarray(new_tokens, dtype=np.int64)
+    if np.any(lens < counts):
+        raise ValueError("every sequence must hold its new tokens")
+    out = [np.arange(L - n, L) for L, n in zip(lens, counts)]
+    return np.concatenate(out + [np.zeros(0, dtype=np.int64)])
+
+
+def prologue_varlen(q, k, v, positions, new_tokens, wq, wk, block_table, **kw):
+    """The fused prologue on the packed tokens [N, H, D]: the single-token
+    prologue, each token with its own sequence's block-table row."""
+    seq = np.repeat(np.arange(len(new_tokens)), np.asarray(new_tokens, dtype=np.int64))
+    bt = np.asarray(block_table)[seq]
+    return prologue(np.asarray(q), np.asarray(k), np.asarray(v), np.asarray(positions), wq, wk,
+                    bt, **kw)
+
+
+def attention_varlen(q_out_bits, pools, pro, seq_lens, new_tokens, block_table, cfg,
+                     seqs=None, heads=None, tokens=None):
+    """Full-softmax attention of every packed new token over its causal prefix.
+
+    q_out_bits: [N, Hq, D] BF16 bits.  tokens: optional per-sequence lists of
+    token indices j to compute (all by default).  Returns {(b, j, h): (o, lse)}.
+    """
+    Hq = q_out_bits.shape[1]
+    G = Hq // cfg["num_kv_heads"]
+    starts = query_starts(new_tokens)
+    result = {}
+    for b in (range(len(new_tokens)) if seqs is None else seqs):
+        L, n = int(seq_lens[b]), int(new_tokens[b])
+        js = range(n) if tokens is None else tokens[b]
+        by_group = {}
+        for h in (range(Hq) if heads is None else heads):
+            by_group.setdefault(h // G, []).append(h)
+        for g, hlist in by_group.items():
+            K, V = _sequence_kv(pools, pro, b, g, seq_lens, block_table, cfg)
+            for j in js:
+                lim = causal_limit(L, n, j)
+                row = int(starts[b]) + j
+                o, lse = attend_full(bf16_bits_to_f64(q_out_bits[row, hlist]), K[:lim], V[:lim],
+                                     cfg["sm_scale"])
+                for i, h in enumerate(hlist):
+                    result[(b, j, h)] = (o[i], lse[i])
+    return result

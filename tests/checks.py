@@ -80,7 +80,7 @@ def poison_indices(inp, w, kind, spare_pages=True):
     page, and the new tokens' own slots (the prologue must overwrite them
     before attention reads them).
     """
-    Tq = int(getattr(w, "tokens", 1))
+    counts = w.new_tokens if w.varlen else [int(w.tokens)] * w.batch
     bt = inp["block_table"].cpu().numpy()
     lens = [int(L) for L in w.seq_lens]
     Hkv, ps, hs = w.num_kv_heads, inp["page_stride"], inp["head_stride"]
@@ -94,7 +94,7 @@ def poison_indices(inp, w, kind, spare_pages=True):
     for b, L in enumerate(lens):
         t = (L - 1) // PAGE_SIZE
         slots = [(t, r) for r in range(L - t * PAGE_SIZE, PAGE_SIZE)]
-        slots += [(pos // PAGE_SIZE, pos % PAGE_SIZE) for pos in range(L - Tq, L)]
+        slots += [(pos // PAGE_SIZE, pos % PAGE_SIZE) for pos in range(L - int(counts[b]), L)]
         for tile, r in slots:
             page = int(bt[b, tile])
             for g in range(Hkv):

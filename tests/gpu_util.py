@@ -24,7 +24,7 @@ def config_for(w, inp):
                            head_stride=inp["head_stride"], rope_theta=w.rope_theta,
                            rms_eps=w.rms_eps, norm_before_rope=w.norm_before_rope,
                            k_scale=w.k_scale, v_scale=w.v_scale,
-                           tokens_per_seq=getattr(w, "tokens", 1))
+                           tokens_per_seq=w.max_new_tokens)
 
 
 def run_step(w, g, sched, lse=True, cfg=None):

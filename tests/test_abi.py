@@ -239,3 +239,49 @@ def test_out_dtype_validation(lib, out_dtype, out_scale, status):
                              ctypes.byref(c), fake, 16, fake, fake, ctypes.c_void_p(0))
     # a valid configuration fails only at the (too small) workspace, before any launch
     assert got == (B.E_WORKSPACE if status == B.OK else status), lib.lbsr_last_error()
+
+
+def test_tokens_beyond_block_table_reach_rejected(lib):
+    """New tokens must fit the block table: tokens_per_seq > max_blocks * 64 is
+    refused before any launch (a kernel would otherwise walk past the row)."""
+    s = DecodeConfig(8, 8, "bf16", 2, 100, tokens_per_seq=129).shape()
+    p = DecodeConfig(8, 8, "bf16", 2, 100).params()
+    fake = ctypes.c_void_p(0x10000)
+    nul = ctypes.c_void_p(0)
+    got = lib.lbsr_prefill_attention(ctypes.byref(s), ctypes.byref(p), 4, *([fake] * 6), nul, nul,
+                                     nul)
+    assert got == B.E_INVALID and b"max_blocks_per_seq" in lib.lbsr_last_error()
+    s = DecodeConfig(8, 8, "bf16", 2, 100, tokens_per_seq=128).shape()
+    got = lib.lbsr_prefill_attention(ctypes.byref(s), ctypes.byref(p), 4, ctypes.c_void_p(0x10002),
+                                     *([fake] * 5), nul, nul, nul)
+    assert got == B.E_INVALID and b"q_out" in lib.lbsr_last_error()   # shape accepted
+
+
+def test_varlen_entry_points_validate_before_any_launch(lib):
+    """Negative token counts, a missing or misaligned q_start or workspace, a
+    short workspace and too many packed rows return errors without touching a
+    device; the workspace size follows its formula."""
+    cfg = DecodeConfig(64, 8, "bf16", 200, 4000, tokens_per_seq=512)
+    s, p = cfg.shape(), cfg.params()
+    fake, odd, nul = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10002), ctypes.c_void_p(0)
+    n = ctypes.c_size_t()
+    assert lib.lbsr_prefill_varlen_workspace_size(ctypes.byref(s), 8, 100, ctypes.byref(n)) == B.OK
+    assert n.value == 256 + 8 * (-(-100 // 32) + 8)          # 32 tokens per block at G = 8
+    big = 1 << 20
+    attn = lambda total, qs, ws, nb: lib.lbsr_prefill_attention_varlen(
+        ctypes.byref(s), ctypes.byref(p), 8, total, qs, *([fake] * 5), ws, nb, fake, nul, nul, nul)
+    assert attn(-1, fake, fake, big) == B.E_INVALID
+    assert attn(100, nul, fake, big) == B.E_INVALID and b"q_start" in lib.lbsr_last_error()
+    assert attn(100, odd, fake, big) == B.E_INVALID
+    assert attn(100, fake, nul, big) == B.E_INVALID and b"workspace" in lib.lbsr_last_error()
+    assert attn(100, fake, ctypes.c_void_p(0x10040), big) == B.E_INVALID     # not 256-aligned
+    assert attn(100, fake, fake, n.value - 1) == B.E_WORKSPACE
+    assert attn(1 << 26, fake, fake, big) == B.E_UNSUPPORTED      # 2^26 tokens x 80 rows
+    # q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table, k_cache, v_cache, q_out
+    args = [fake] * 11
+    step = lambda qs, a: lib.lbsr_prefill_step_varlen(
+        ctypes.byref(s), ctypes.byref(p), 8, 100, qs, *a, fake, big, fake, nul, nul, nul)
+    assert step(nul, args) == B.E_INVALID
+    a2 = list(args)
+    a2[10] = a2[0]                                         # q_out aliases q
+    assert step(fake, a2) == B.E_INVALID and b"alias" in lib.lbsr_last_error()
