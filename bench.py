@@ -36,6 +36,7 @@ from load_balanced_split_rope_amd import workloads as wl        # noqa: E402
 METRIC = ("decode-attn µs/step + achieved HBM GB/s (% peak), 1x128K+31x4K mix, BF16/FP8")
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0        # dense BF16 matrix-core peak of MI355X
+Q_SCALE = 2.0 ** -5                    # per-tensor q scale of the FP8-score legs (|q| <= ~14)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_attention_traffic.json")
 
 
@@ -65,7 +66,8 @@ def split_kernel_bytes(w):
 class Case:
     """Two independent input sets of one workload on the GPU, plus outputs."""
 
-    def __init__(self, w, dev, kv_interleave=False, out_dtype="bf16", out_scale=1.0):
+    def __init__(self, w, dev, kv_interleave=False, out_dtype="bf16", out_scale=1.0,
+                 qk_dtype="bf16", q_scale=1.0):
         self.w = w
         self.sets = []
         for copy in range(2):
@@ -77,7 +79,7 @@ class Case:
                                    head_stride=g["head_stride"], rope_theta=w.rope_theta,
                                    rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale,
                                    tokens_per_seq=w.tokens, out_dtype=out_dtype,
-                                   out_scale=out_scale)
+                                   out_scale=out_scale, qk_dtype=qk_dtype, q_scale=q_scale)
         self.q_out = torch.empty_like(g["q"])
         self.out = torch.empty(g["q"].shape, dtype=self.cfg.out_torch_dtype, device=dev)
         self.lse = torch.empty(self.cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32,
@@ -237,14 +239,14 @@ def prefill_leg(dev, reps=10, warmup=3):
     each timed with HIP events on the launch stream; the attention kernel is
     matrix-core bound, so its roofline is flops against the BF16 MFMA peak."""
     legs = {}
-    for name in wl.PREFILL_NAMES:
+    for name, qk in [(n, "bf16") for n in wl.PREFILL_NAMES] + [("prefill_fp8", "fp8")]:
         w = wl.named(name)
         g = wl.make_inputs(w, device=dev)
         cfg = lb.DecodeConfig(w.num_q_heads, w.num_kv_heads, w.kv_dtype, g["max_blocks"],
                               g["num_pages"], page_stride=g["page_stride"],
                               head_stride=g["head_stride"], rope_theta=w.rope_theta,
                               rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale,
-                              tokens_per_seq=w.max_new_tokens)
+                              tokens_per_seq=w.max_new_tokens, qk_dtype=qk, q_scale=Q_SCALE)
         q_out = torch.empty_like(g["q"])
         out = torch.empty_like(g["q"])
         lse = torch.empty(g["q"].shape[:-1], dtype=torch.float32, device=dev)
@@ -281,13 +283,15 @@ def prefill_leg(dev, reps=10, warmup=3):
             raise RuntimeError(f"prefill leg {name}: device error word {int(err.item()):#x}")
         f = prefill_flops(w)
         tflops = f / (attn_ms * 1e-3) / 1e12
-        legs[name] = {
-            "workload": WORKLOAD_TEXT[name], "us_per_step": round(step_ms * 1e3, 1),
+        legs[name if qk == "bf16" else name + "_fp8_scores"] = {
+            "workload": WORKLOAD_TEXT[name] + ("" if qk == "bf16" else
+                                               ", FP8 Q.K^T (q scale 2^-5)"),
+            "us_per_step": round(step_ms * 1e3, 1),
             "attention_us": round(attn_ms * 1e3, 1), "flops": f,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": f"prefill_kernel<{w.kv_dtype}>"},
+                         "kernel": f"prefill_kernel<{w.kv_dtype}{', fp8 scores' if qk == 'fp8' else ''}>"},
         }
         del g, q_out, out, lse, step_args, attn_args
         torch.cuda.empty_cache()
@@ -339,14 +343,15 @@ def cpu_baseline(w, dev, min_seconds=10.0):
             "seconds": round(dt, 2)}
 
 
-def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16"):
+def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_dtype="bf16"):
     """Dynamic step time, per-kernel times, and (full) graph time and static sweep.
 
     weighted: calibrate per-XCD weights from traced steps, compare weighted and
     equal shares with interleaved untimed-for-the-headline loops, and time the
     headline with the faster of the two (both figures are reported)."""
     equal = lb.Schedule("dynamic", num_workers=P)
-    case = Case(w, dev, out_dtype=out_dtype, out_scale=2.0 ** -7)
+    case = Case(w, dev, out_dtype=out_dtype, out_scale=2.0 ** -7, qk_dtype=qk_dtype,
+                q_scale=Q_SCALE)
     for i in range(warmup):
         case.step(i, equal)
     r = {}
@@ -553,6 +558,13 @@ def main():
                 "us_per_step": round(ro["ms"] * 1e3, 2),
                 "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, ro["kernel_ms"])},
                 "step_time_vs_bf16_output": round(ro["ms"] / ms, 4),
+            }
+            rq = measure(w8, dev, P, args.steps, args.warmup, False, weighted, qk_dtype="fp8")
+            result["fp8"]["fp8_scores"] = {
+                "workload": "mix_fp8 with FP8 Q.K^T (q quantised with scale 2^-5)",
+                "us_per_step": round(rq["ms"] * 1e3, 2),
+                "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, rq["kernel_ms"])},
+                "step_time_vs_bf16_scores": round(rq["ms"] / ms8, 4),
             }
             result["prefill"] = prefill_leg(dev)
         if not args.no_cpu_baseline:

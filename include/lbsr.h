@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define LBSR_ABI_VERSION 2
+#define LBSR_ABI_VERSION 3
 #define LBSR_NUM_XCDS 8     /* accelerator complex dies of an MI355X */
 #define LBSR_MAX_XCD_WEIGHT 65536
 #define LBSR_HEAD_DIM 128
@@ -75,6 +75,14 @@ typedef enum { LBSR_SCHED_DYNAMIC = 0, LBSR_SCHED_STATIC = 1 } lbsr_sched;
  * explicitly).  FP8: out holds OCP E4M3 codes, code = RNE(clamp(o /
  * out_scale, -448, 448)), one byte per element; lse_out stays fp32. */
 typedef enum { LBSR_OUT_BF16 = 0, LBSR_OUT_FP8_E4M3 = 1 } lbsr_out_dtype;
+/* Arithmetic of Q.K^T with an FP8 cache ([A] "Why does dynamic scheduling
+ * matter in attention?": BF16 and FP8 backends; [B] intro: FP8 E4M3).
+ * BF16: q stays BF16, the K codes are widened exactly, BF16 matrix cores.
+ * FP8_E4M3: q is quantised on load to E4M3 codes RNE(clamp(q * r, -448,
+ * 448)) with r = 1/q_scale rounded to fp32 and the product taken in fp32;
+ * S = sum over channels of code_q * code_k on FP8 matrix cores (16x16x128),
+ * times q_scale * k_scale * sm_scale.  P.V is the same in both. */
+typedef enum { LBSR_QK_BF16 = 0, LBSR_QK_FP8_E4M3 = 1 } lbsr_qk_dtype;
 
 /* Sticky device error bits (int32 at lbsr_ws_layout.error_word). */
 #define LBSR_DEV_ERR_SEQ_LEN 1   /* seq_len outside [1, max_blocks_per_seq*64]: clamped */
@@ -148,6 +156,8 @@ typedef struct {
   float sm_scale;           /* softmax scale; 0 -> 1/sqrt(128) */
   int32_t out_dtype;        /* lbsr_out_dtype of `out` (0 = BF16) */
   float out_scale;          /* FP8 output: value = code * out_scale; > 0; ignored for BF16 */
+  int32_t qk_dtype;         /* lbsr_qk_dtype (0 = BF16); FP8_E4M3 needs an FP8 cache */
+  float q_scale;            /* FP8 Q.K^T: q value = code * q_scale; > 0; ignored for BF16 */
 } lbsr_params;
 
 typedef struct {

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # LBSR_LIB may name another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("LBSR_LIB") or os.path.join(HERE, "liblbsr.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 HEAD_DIM = 128
 PAGE_SIZE = 64
 TILE_ELEMS = HEAD_DIM * PAGE_SIZE
@@ -27,6 +27,7 @@ OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 KV_BF16, KV_FP8_E4M3 = 0, 1
 SCHED_DYNAMIC, SCHED_STATIC = 0, 1
 OUT_BF16, OUT_FP8_E4M3 = 0, 1
+QK_BF16, QK_FP8_E4M3 = 0, 1
 DEV_ERR_SEQ_LEN, DEV_ERR_PAGE, DEV_ERR_POSITION, DEV_ERR_QUERY_START = 1, 2, 4, 8
 
 # Every symbol include/lbsr.h declares.
@@ -66,7 +67,8 @@ class Params(ctypes.Structure):
     _fields_ = [("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float),
                 ("norm_before_rope", ctypes.c_int32), ("k_scale", ctypes.c_float),
                 ("v_scale", ctypes.c_float), ("sm_scale", ctypes.c_float),
-                ("out_dtype", ctypes.c_int32), ("out_scale", ctypes.c_float)]
+                ("out_dtype", ctypes.c_int32), ("out_scale", ctypes.c_float),
+                ("qk_dtype", ctypes.c_int32), ("q_scale", ctypes.c_float)]
 
 
 class SchedCfg(ctypes.Structure):

@@ -149,6 +149,15 @@ lbsr_status check_params(const lbsr_params* p, int32_t kv_dtype) {
       (!(p->k_scale > 0) || !isfinite(p->k_scale) || !(p->v_scale > 0) || !isfinite(p->v_scale)))
     return fail(LBSR_E_INVALID, "k_scale %g / v_scale %g must be finite and > 0",
                 (double)p->k_scale, (double)p->v_scale);
+  if (p->qk_dtype != LBSR_QK_BF16 && p->qk_dtype != LBSR_QK_FP8_E4M3)
+    return fail(LBSR_E_INVALID, "qk_dtype %d unknown", p->qk_dtype);
+  if (p->qk_dtype == LBSR_QK_FP8_E4M3) {
+    if (kv_dtype != LBSR_KV_FP8_E4M3)
+      return fail(LBSR_E_UNSUPPORTED, "qk_dtype FP8 needs an FP8 cache");
+    if (!(p->q_scale > 0) || !isfinite(p->q_scale) || !isfinite(1.0f / p->q_scale))
+      return fail(LBSR_E_INVALID, "q_scale %g must be finite and > 0 with a finite inverse",
+                  (double)p->q_scale);
+  }
   return LBSR_OK;
 }
 
@@ -379,10 +388,16 @@ lbsr_status run_plan_prologue(const lbsr_shape* shape, const lbsr_params* params
       "plan + prologue launch");
 }
 
+bool qk_fp8(const lbsr_params* p) { return p->qk_dtype == LBSR_QK_FP8_E4M3; }
+
+// 1/q_scale rounded to fp32: q codes are RNE(q * this), the product in fp32.
+float inv_q_scale(const lbsr_params* p) { return qk_fp8(p) ? 1.0f / p->q_scale : 1.0f; }
+
 float score_scale_log2(const lbsr_params* p, int32_t kv_dtype) {
   const double sm = p->sm_scale > 0 ? (double)p->sm_scale : 1.0 / sqrt((double)LBSR_HEAD_DIM);
   const double ks = kv_dtype == LBSR_KV_FP8_E4M3 ? (double)p->k_scale : 1.0;
-  return (float)(sm * ks * 1.4426950408889634074);
+  const double qs = qk_fp8(p) ? (double)p->q_scale : 1.0;   // FP8 scores are of q's codes
+  return (float)(sm * ks * qs * 1.4426950408889634074);
 }
 
 lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
@@ -395,10 +410,11 @@ lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_
   const bool out_fp8 = params->out_dtype == LBSR_OUT_FP8_E4M3;
   const double vs = fp8 ? (double)params->v_scale : 1.0;
   const float o_scale = (float)(out_fp8 ? vs / (double)params->out_scale : vs);
-  return hip_status(lbsr::launch_split_attention(geo, fp8, out_fp8, l.num_workers, q_out, kc, vc,
-                                                 bt, plan_ptrs(ws, l), out, lse_out,
+  return hip_status(lbsr::launch_split_attention(geo, fp8, out_fp8, qk_fp8(params),
+                                                 l.num_workers, q_out, kc, vc, bt,
+                                                 plan_ptrs(ws, l), out, lse_out,
                                                  score_scale_log2(params, shape->kv_dtype),
-                                                 o_scale, trace, stream),
+                                                 o_scale, inv_q_scale(params), trace, stream),
                     "split attention launch");
 }
 
@@ -429,7 +445,8 @@ lbsr_status run_prefill(const lbsr_shape* shape, const lbsr_params* params, int3
   return hip_status(lbsr::launch_prefill(geo, fp8, out_fp8, q_out, kc, vc, bt, seq_lens, out,
                                          lse_out, score_scale_log2(params, shape->kv_dtype),
                                          o_scale, error_word, q_start, total_tokens,
-                                         (int32_t*)work, stream),
+                                         (int32_t*)work, qk_fp8(params), inv_q_scale(params),
+                                         stream),
                     "prefill launch");
 }
 

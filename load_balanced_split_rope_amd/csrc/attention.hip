@@ -72,27 +72,35 @@ __device__ __forceinline__ void load_frags(u32x4 (&dst)[TileRegs<kFp8>::kFrags],
 // streams until the end (split kernel 165 -> 161 us BF16, 89 -> 87 us FP8);
 // a wave that waits has its next loads in flight already.  Only valid when
 // every wave runs the same number of tiles (KV heads a multiple of the waves).
-template <bool kFp8, bool kPrefetch, bool kSync>
+//
+// kQk8 (FP8 cache only): the scores on FP8 matrix cores, one 16x16x128
+// instruction per 16 rows, from the K codes as stored and q's codes (qF).
+template <bool kFp8, bool kQk8, bool kPrefetch, bool kSync>
 __device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
-                                            const bf16x8 (&qB)[4], int rem, int lag, int tail,
-                                            int kc, int lane, float score_scale_log2,
-                                            const u32x4* next_k, const u32x4* next_v) {
+                                            const bf16x8 (&qB)[4], const i32x8& qF, int rem,
+                                            int lag, int tail, int kc, int lane,
+                                            float score_scale_log2, const u32x4* next_k,
+                                            const u32x4* next_v) {
   constexpr int NF = TileRegs<kFp8>::kFrags;
   // ---- scores: S^T[token][col], lane holds tokens 16*tb + 4*kc + e ----
   f32x4 S[4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kQk8) {
+      acc = mfma_fp8(k_fp8_operand(R.k[2 * tb], R.k[2 * tb + 1]), qF, acc);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 a;
-      if constexpr (kFp8) {
-        const u32x4 w = R.k[2 * tb + (s >> 1)];
-        a = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
-      } else {
-        a = as_bf16x8(R.k[4 * tb + s]);
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 a;
+        if constexpr (kFp8) {
+          const u32x4 w = R.k[2 * tb + (s >> 1)];
+          a = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+        } else {
+          a = as_bf16x8(R.k[4 * tb + s]);
+        }
+        acc = mfma_bf16(a, qB[s], acc);
       }
-      acc = mfma_bf16(a, qB[s], acc);
     }
     S[tb] = acc;
   }
@@ -163,12 +171,12 @@ __device__ __forceinline__ int xcd_worker(int block, int num_blocks) {
 
 // One worker of the schedule (this workgroup): all chunks of `worker`, every
 // KV head (one wave per head, looping if Hkv > 8).
-template <bool kFp8, bool kSync>
+template <bool kFp8, bool kQk8, bool kSync>
 __device__ __forceinline__ void split_worker(
     int worker, const Geometry& geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const PlanPtrs& plan, void* __restrict__ out, float* __restrict__ lse_out,
-    float score_scale_log2, float out_scale, int out_fp8) {
+    float score_scale_log2, float out_scale, int out_fp8, float inv_q_scale) {
   constexpr int kElemBytes = kFp8 ? 1 : 2;
   const int c_begin = wave_uniform(plan.worker_chunk[worker]);
   const int c_end = wave_uniform(plan.worker_chunk[worker + 1]);
@@ -213,7 +221,6 @@ __device__ __forceinline__ void split_worker(
 #pragma unroll
         for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(u32x4{0, 0, 0, 0});
       }
-
       SoftmaxState st;
 #pragma unroll
       for (int i = 0; i < 8; ++i) st.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -230,16 +237,22 @@ __device__ __forceinline__ void split_worker(
       TileRegs<kFp8> R;
       load_frags<kFp8>(R.k, tile_ptr(k_pool, page), lane);
       load_frags<kFp8>(R.v, tile_ptr(v_pool, page), lane);
+      // q's E4M3 codes (FP8 scores), computed while the first tile streams in
+      i32x8 qF = {0, 0, 0, 0, 0, 0, 0, 0};
+      if constexpr (kQk8) {
+        __builtin_amdgcn_sched_barrier(0);
+        qF = q_fp8_operand(qB, inv_q_scale);
+      }
       // all tiles but the last prefetch their successor; the last one is peeled
       // so the loop body has no conditional loads
       for (int t = t0; t < t1 - 1; ++t) {
         const int next = fetch_page(bt_row, t + 1, geo.num_pages, bad_page);
-        attend_tile<kFp8, true, kSync>(R, st, qB, L - t * kPage, lag, T - 1, kc, lane,
-                                       score_scale_log2, tile_ptr(k_pool, next),
-                                       tile_ptr(v_pool, next));
+        attend_tile<kFp8, kQk8, true, kSync>(R, st, qB, qF, L - t * kPage, lag, T - 1, kc, lane,
+                                             score_scale_log2, tile_ptr(k_pool, next),
+                                             tile_ptr(v_pool, next));
       }
-      attend_tile<kFp8, false, false>(R, st, qB, L - (t1 - 1) * kPage, lag, T - 1, kc, lane,
-                                      score_scale_log2, nullptr, nullptr);
+      attend_tile<kFp8, kQk8, false, false>(R, st, qB, qF, L - (t1 - 1) * kPage, lag, T - 1, kc,
+                                            lane, score_scale_log2, nullptr, nullptr);
       if (bad_page && lane == 0) atomicOr(plan.error_word, (int32_t)kErrPage);
       const float m = st.m;
       const float lsum = st.lsum;
@@ -294,17 +307,17 @@ __device__ __forceinline__ void split_worker(
 // The kernel: one workgroup per worker.  With a trace buffer it records, per
 // worker, [start, end] of the 100 MHz constant clock and the hardware ids of
 // the compute unit it ran on (HW_ID, XCC_ID), for load-balance analysis.
-template <bool kFp8, bool kSync>
+template <bool kFp8, bool kQk8, bool kSync>
 __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
     Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table, PlanPtrs plan,
     void* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
-    float out_scale, int out_fp8, int64_t* __restrict__ trace) {
+    float out_scale, int out_fp8, float inv_q_scale, int64_t* __restrict__ trace) {
   int64_t t_start = 0;
   if (trace != nullptr && threadIdx.x == 0) t_start = (int64_t)wall_clock64();
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  split_worker<kFp8, kSync>(worker, geo, q_out, k_pool, v_pool, block_table, plan, out, lse_out,
-                            score_scale_log2, out_scale, out_fp8);
+  split_worker<kFp8, kQk8, kSync>(worker, geo, q_out, k_pool, v_pool, block_table, plan, out,
+                                  lse_out, score_scale_log2, out_scale, out_fp8, inv_q_scale);
   if (trace != nullptr) {
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -485,10 +498,11 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
   }
 }
 
-hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, int num_workers,
-                                  const void* q_out, const void* k_cache, const void* v_cache,
-                                  const int32_t* block_table, const PlanPtrs& plan, void* out,
-                                  float* lse_out, float score_scale_log2, float out_scale,
+hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, bool qk_fp8,
+                                  int num_workers, const void* q_out, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const PlanPtrs& plan, void* out, float* lse_out,
+                                  float score_scale_log2, float out_scale, float inv_q_scale,
                                   int64_t* trace, hipStream_t stream) {
   // one wave per (KV head, 16-column block), at most 8
   const int virt = geo.num_kv_heads * ((geo.group * geo.tokens + 15) / 16);
@@ -498,14 +512,18 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, i
   auto launch = [&](auto kernel) {
     kernel<<<num_workers, waves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
-        block_table, plan, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0, trace);
+        block_table, plan, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0,
+        inv_q_scale, trace);
   };
-  if (fp8) {
-    if (sync) launch(split_attention_kernel<true, true>);
-    else launch(split_attention_kernel<true, false>);
+  if (fp8 && qk_fp8) {
+    if (sync) launch(split_attention_kernel<true, true, true>);
+    else launch(split_attention_kernel<true, true, false>);
+  } else if (fp8) {
+    if (sync) launch(split_attention_kernel<true, false, true>);
+    else launch(split_attention_kernel<true, false, false>);
   } else {
-    if (sync) launch(split_attention_kernel<false, true>);
-    else launch(split_attention_kernel<false, false>);
+    if (sync) launch(split_attention_kernel<false, false, true>);
+    else launch(split_attention_kernel<false, false, false>);
   }
   return hipGetLastError();
 }

@@ -68,6 +68,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 // Device pointers of the plan arrays inside a workspace.
 struct PlanPtrs {

@@ -19,10 +19,13 @@ hipError_t launch_prologue(const Geometry& geo, bool fp8, const void* q, const v
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, const SchedParams& sp,
                        const PlanPtrs& plan, hipStream_t stream);
 
-hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, int num_workers,
-                                  const void* q_out, const void* k_cache, const void* v_cache,
-                                  const int32_t* block_table, const PlanPtrs& plan, void* out,
-                                  float* lse_out, float score_scale_log2, float out_scale,
+// qk_fp8 (with an FP8 cache): q quantised with inv_q_scale, scores on FP8
+// matrix cores; score_scale_log2 then includes q_scale.
+hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, bool qk_fp8,
+                                  int num_workers, const void* q_out, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const PlanPtrs& plan, void* out, float* lse_out,
+                                  float score_scale_log2, float out_scale, float inv_q_scale,
                                   int64_t* trace, hipStream_t stream);
 
 // out_fp8: `out` holds E4M3 codes of the merged values (which the split
@@ -41,8 +44,8 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
                           const void* k_cache, const void* v_cache, const int32_t* block_table,
                           const int32_t* seq_lens, void* out, float* lse_out,
                           float score_scale_log2, float out_scale, int32_t* error_word,
-                          const int32_t* q_start, int total_tokens, int32_t* work,
-                          hipStream_t stream);
+                          const int32_t* q_start, int total_tokens, int32_t* work, bool qk_fp8,
+                          float inv_q_scale, hipStream_t stream);
 
 // Work-list entries a ragged prefill may need: one per block of new tokens.
 int prefill_max_items(const Geometry& geo, int total_tokens);

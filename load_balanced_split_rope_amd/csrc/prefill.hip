@@ -37,14 +37,14 @@
 
 namespace lbsr {
 
-template <bool kFp8>
+template <bool kFp8, bool kQk8>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, void* __restrict__ out, float* __restrict__ lse_out,
     float score_scale_log2, float out_scale, int out_fp8, int32_t* __restrict__ error_word,
     int num_blocks_q, const int32_t* __restrict__ q_start, int total_tokens,
-    const int32_t* __restrict__ work) {
+    const int32_t* __restrict__ work, float inv_q_scale) {
   constexpr int NF = kFp8 ? 8 : 16;                  // 1 KiB fragments per K (or V) tile
   constexpr int kStage = 2 * NF * kWave;             // u32x4 per stage: K then V
   constexpr int kPerThread = kStage / (kPrefillWaves * kWave);   // 4 (BF16) or 2 (FP8)
@@ -152,6 +152,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
 
   u32x4 pre[kPerThread];
   load_tile(0, pre);
+  // FP8 scores: q's codes for each column block, computed while tile 0 streams in
+  i32x8 qF[kPrefillBlocks];
+#pragma unroll
+  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+    qF[cb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (kQk8) qF[cb] = q_fp8_operand(qB[cb], inv_q_scale);
+  }
   store_tile(0, pre);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
@@ -166,6 +173,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
       for (int cb = 0; cb < kPrefillBlocks; ++cb) S[cb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kQk8) {
+        const i32x8 a = k_fp8_operand(kf[2 * tb * kWave + lane], kf[(2 * tb + 1) * kWave + lane]);
+#pragma unroll
+        for (int cb = 0; cb < kPrefillBlocks; ++cb) S[cb][tb] = mfma_fp8(a, qF[cb], S[cb][tb]);
+        continue;
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8 a;
@@ -341,8 +354,8 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
                           const void* k_cache, const void* v_cache, const int32_t* block_table,
                           const int32_t* seq_lens, void* out, float* lse_out,
                           float score_scale_log2, float out_scale, int32_t* error_word,
-                          const int32_t* q_start, int total_tokens, int32_t* work,
-                          hipStream_t stream) {
+                          const int32_t* q_start, int total_tokens, int32_t* work, bool qk_fp8,
+                          float inv_q_scale, hipStream_t stream) {
   const int nqb = prefill_blocks_q(geo);
   size_t grid = (size_t)nqb * geo.batch * geo.num_kv_heads;
   if (q_start) {
@@ -357,10 +370,11 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
     kernel<<<(unsigned)grid, kPrefillWaves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
         block_table, seq_lens, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0,
-        error_word, nqb, q_start, total_tokens, q_start ? work : nullptr);
+        error_word, nqb, q_start, total_tokens, q_start ? work : nullptr, inv_q_scale);
   };
-  if (fp8) launch(prefill_kernel<true>);
-  else launch(prefill_kernel<false>);
+  if (fp8 && qk_fp8) launch(prefill_kernel<true, true>);
+  else if (fp8) launch(prefill_kernel<true, false>);
+  else launch(prefill_kernel<false, false>);
   return hipGetLastError();
 }
 

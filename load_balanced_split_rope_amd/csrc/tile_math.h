@@ -21,6 +21,38 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// S^T[16 rows][16 cols] += A . B over 128 channels of E4M3 codes (gfx950
+// v_mfma_f32_16x16x128_f8f6f4, no block scales).  A lane l holds 32 codes of
+// row l % 16, B lane l 32 codes of column l % 16; byte j of lane group l / 16
+// pairs with byte j of the same group of the other operand, so any channel
+// order works if both operands use it.  Accumulator layout as mfma_bf16.
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The K operand of 16-row block tb for mfma_fp8: the tile's two FP8
+// fragments 2tb and 2tb+1 (channels 32s + 8kc + j at byte 8s + j).
+__device__ __forceinline__ i32x8 k_fp8_operand(u32x4 lo, u32x4 hi) {
+  return i32x8{(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3],
+               (int32_t)hi[0], (int32_t)hi[1], (int32_t)hi[2], (int32_t)hi[3]};
+}
+
+// The Q operand for mfma_fp8 from the BF16 fragments qB[s] (channels
+// 32s + 8kc + j): E4M3 codes of q * inv_q_scale, rounded to fp32, then to the
+// nearest code (ties to even), saturating at +-448; byte 8s + j, matching K.
+__device__ __forceinline__ i32x8 q_fp8_operand(const bf16x8 (&qB)[4], float inv_q_scale) {
+  i32x8 r;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (float)qB[s][j] * inv_q_scale;
+    r[2 * s] = (int32_t)f32x4_to_e4m3x4(x[0], x[1], x[2], x[3]);
+    r[2 * s + 1] = (int32_t)f32x4_to_e4m3x4(x[4], x[5], x[6], x[7]);
+  }
+  return r;
+}
+
 // 8 E4M3 codes (two dwords) -> 8 BF16 values, exactly.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);

@@ -32,6 +32,8 @@ class DecodeConfig:
     tokens_per_seq: int = 1       # new tokens per sequence (multi-token decode)
     out_dtype: str = "bf16"       # "bf16", or "fp8": E4M3 codes of out / out_scale
     out_scale: float = 1.0
+    qk_dtype: str = "bf16"        # "bf16", or "fp8" (FP8 cache): q quantised with q_scale and
+    q_scale: float = 1.0          # Q.K^T on FP8 matrix cores
 
     def shape(self):
         return B.Shape(self.num_q_heads, self.num_kv_heads, B.HEAD_DIM, B.PAGE_SIZE,
@@ -46,12 +48,14 @@ class DecodeConfig:
         return (batch,) + rest if Tq == 1 else (batch, Tq) + rest
 
     def params(self):
-        if self.out_dtype not in ("bf16", "fp8"):
-            raise ValueError(f"out_dtype {self.out_dtype!r}: 'bf16' or 'fp8'")
+        for name in ("out_dtype", "qk_dtype"):
+            if getattr(self, name) not in ("bf16", "fp8"):
+                raise ValueError(f"{name} {getattr(self, name)!r}: 'bf16' or 'fp8'")
         return B.Params(self.rope_theta, self.rms_eps, int(self.norm_before_rope),
                         self.k_scale, self.v_scale, self.sm_scale,
                         B.OUT_BF16 if self.out_dtype == "bf16" else B.OUT_FP8_E4M3,
-                        self.out_scale)
+                        self.out_scale,
+                        B.QK_BF16 if self.qk_dtype == "bf16" else B.QK_FP8_E4M3, self.q_scale)
 
     @property
     def out_torch_dtype(self):

@@ -43,6 +43,7 @@ from .attention import attend_full, attend_chunk, combine_lse
 from .step import (prologue, cache_slot, gather_kv, decode_attention,
                    split_attention, encode_output)
 from . import multitoken   # several new tokens per sequence (R20)
+from . import qk           # FP8 Q.K^T: q quantised with a per-tensor scale (R23)
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "e4m3_to_f64", "f64_to_e4m3",

@@ -25,7 +25,7 @@ log-sum-exp merge gives it weight 0.
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64
+from .qk import query_values
 from .layout import PAGE_SIZE
 from .attention import attend_full, combine_lse
 from .step import prologue, _sequence_kv
@@ -78,8 +78,8 @@ def decode_attention_tokens(q_out_bits, pools, pro, seq_lens, block_table, cfg,
             K, V = _sequence_kv(pools, pro, b, g, seq_lens, block_table, cfg)
             for j in range(Tq):
                 lim = causal_limit(L, Tq, j)
-                o, lse = attend_full(bf16_bits_to_f64(q_out_bits[b, j, hlist]), K[:lim], V[:lim],
-                                     cfg["sm_scale"])
+                o, lse = attend_full(query_values(q_out_bits[b, j, hlist], cfg), K[:lim],
+                                     V[:lim], cfg["sm_scale"])
                 for i, h in enumerate(hlist):
                     result[(b, j, h)] = (o[i], lse[i])
     return result
@@ -120,7 +120,7 @@ def split_attention_tokens(q_out_bits, pools, pro, seq_lens, block_table, cfg, p
             for g in range(Hkv):
                 K, V = kv[g]
                 for j in range(Tq):
-                    qg = bf16_bits_to_f64(q_out_bits[b, j, g * G:(g + 1) * G])
+                    qg = query_values(q_out_bits[b, j, g * G:(g + 1) * G], cfg)
                     og, lg = chunk_partial(qg, K, V, row0, row1, causal_limit(L, Tq, j),
                                            cfg["sm_scale"])
                     oc[j, g * G:(g + 1) * G] = og
@@ -189,8 +189,8 @@ def attention_varlen(q_out_bits, pools, pro, seq_lens, new_tokens, block_table, 
             for j in js:
                 lim = causal_limit(L, n, j)
                 row = int(starts[b]) + j
-                o, lse = attend_full(bf16_bits_to_f64(q_out_bits[row, hlist]), K[:lim], V[:lim],
-                                     cfg["sm_scale"])
+                o, lse = attend_full(query_values(q_out_bits[row, hlist], cfg), K[:lim],
+                                     V[:lim], cfg["sm_scale"])
                 for i, h in enumerate(hlist):
                     result[(b, j, h)] = (o[i], lse[i])
     return result

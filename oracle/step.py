@@ -24,6 +24,7 @@ Readings used here:
 
 import numpy as np
 
+from .qk import query_values
 from .formats import bf16_bits_to_f64, f64_to_bf16_bits, e4m3_to_f64, f64_to_e4m3
 from .rope_norm import qk_transform
 from .layout import tile_offset, PAGE_SIZE, HEAD_DIM
@@ -167,7 +168,7 @@ def decode_attention(q_out_bits, pools, pro, seq_lens, block_table, cfg,
             by_group.setdefault(h // G, []).append(h)
         for g, hlist in by_group.items():
             K, V = _sequence_kv(pools, pro, b, g, seq_lens, block_table, cfg)
-            qg = bf16_bits_to_f64(q_out_bits[b, hlist])
+            qg = query_values(q_out_bits[b, hlist], cfg)
             o, lse = attend_full(qg, K, V, cfg["sm_scale"])
             for i, h in enumerate(hlist):
                 result[(b, h)] = (o[i], lse[i])
@@ -197,7 +198,7 @@ def split_attention(q_out_bits, pools, pro, seq_lens, block_table, cfg, plan):
             lc = np.zeros(Hq)
             for g in range(Hkv):
                 K, V = kv[g]
-                qg = bf16_bits_to_f64(q_out_bits[b, g * G:(g + 1) * G])
+                qg = query_values(q_out_bits[b, g * G:(g + 1) * G], cfg)
                 og, lg = attend_chunk(qg, K[j0:j1], V[j0:j1], cfg["sm_scale"])
                 oc[g * G:(g + 1) * G] = og
                 lc[g * G:(g + 1) * G] = lg

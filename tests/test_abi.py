@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lbsr_abi_version() == 2
+    assert lib.lbsr_abi_version() == 3
     for st in range(5):
         assert lib.lbsr_status_string(st).startswith(b"LBSR_")
     assert lib.lbsr_status_string(99) == b"unknown lbsr_status"
@@ -219,9 +219,11 @@ def test_workspace_grows_with_tokens(lib):
 
 
 def test_params_struct_matches_header():
-    """lbsr_params: double, float, int32, 3 floats, int32 out_dtype, float out_scale: 40 bytes."""
-    assert ctypes.sizeof(B.Params) == 40
+    """lbsr_params: double, float, int32, 3 floats, int32 out_dtype, float out_scale,
+    int32 qk_dtype, float q_scale: 48 bytes."""
+    assert ctypes.sizeof(B.Params) == 48
     assert B.Params.out_dtype.offset == 28 and B.Params.out_scale.offset == 32
+    assert B.Params.qk_dtype.offset == 36 and B.Params.q_scale.offset == 40
 
 
 @pytest.mark.parametrize("out_dtype,out_scale,status", [
@@ -285,3 +287,26 @@ def test_varlen_entry_points_validate_before_any_launch(lib):
     a2 = list(args)
     a2[10] = a2[0]                                         # q_out aliases q
     assert step(fake, a2) == B.E_INVALID and b"alias" in lib.lbsr_last_error()
+
+
+@pytest.mark.parametrize("kv_dtype,qk_dtype,q_scale,status", [
+    ("fp8", B.QK_BF16, 0.0, B.OK), ("fp8", B.QK_FP8_E4M3, 0.25, B.OK),
+    ("bf16", B.QK_FP8_E4M3, 0.25, B.E_UNSUPPORTED),      # FP8 scores need an FP8 cache
+    ("fp8", B.QK_FP8_E4M3, 0.0, B.E_INVALID), ("fp8", B.QK_FP8_E4M3, float("nan"), B.E_INVALID),
+    ("fp8", B.QK_FP8_E4M3, 1e-45, B.E_INVALID),         # 1/q_scale overflows fp32
+    ("fp8", 5, 1.0, B.E_INVALID),
+])
+def test_qk_dtype_validation(lib, kv_dtype, qk_dtype, q_scale, status):
+    """Checked before any launch: fake pointers are never dereferenced."""
+    cfg = DecodeConfig(64, 8, kv_dtype, 2048, 4300, k_scale=0.5, v_scale=0.5)
+    s, p = cfg.shape(), cfg.params()
+    p.qk_dtype, p.q_scale = qk_dtype, q_scale
+    c = Schedule("dynamic", num_workers=256).cfg()
+    fake = ctypes.c_void_p(0x10000)
+    got = lib.lbsr_attention(ctypes.byref(s), ctypes.byref(p), 32, fake, fake, fake, fake,
+                             ctypes.byref(c), fake, 1 << 30, fake, fake, ctypes.c_void_p(0))
+    if status == B.OK:
+        # valid params: validation proceeds past them (and then needs a device)
+        assert b"qk_dtype" not in lib.lbsr_last_error() and b"q_scale" not in lib.lbsr_last_error()
+    else:
+        assert got == status, lib.lbsr_last_error()

@@ -31,7 +31,7 @@ def run_prefill(w, g, cfg=None):
     return {"q_out": q_out, "out": out, "lse": lse, "error": int(err.item()), "cfg": cfg}
 
 
-def oracle_prefill(w, inp):
+def oracle_prefill(w, inp, extra=None):
     h = host_step_inputs(inp)
     B, Tq, Hq = w.batch, w.tokens, w.num_q_heads
     q = h["q"].reshape(B, Tq, Hq, 128)
@@ -45,6 +45,7 @@ def oracle_prefill(w, inp):
                              norm_before_rope=w.norm_before_rope)
     cfg = oracle_cfg(inp, w)
     cfg["k_scale"], cfg["v_scale"] = np.float32(w.k_scale).item(), np.float32(w.v_scale).item()
+    cfg.update(extra or {})
     q_out = pro["q_out"].reshape(B, Tq, Hq, 128)
     ref = mt.decode_attention_tokens(q_out, host_pools(inp, w), pro, h["seq_lens"],
                                      h["block_table"], cfg)

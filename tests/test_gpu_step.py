@@ -18,9 +18,10 @@ from gpu_util import device, to_device, run_step
 pytestmark = pytest.mark.gpu
 
 
-def oracle_step(w, inp):
+def oracle_step(w, inp, extra=None):
     """The oracle's step; outputs [B, Hq, D] / [B, Hq], or [B, Tq, Hq, D] /
-    [B, Tq, Hq] with several new tokens per sequence."""
+    [B, Tq, Hq] with several new tokens per sequence.  extra: more oracle cfg
+    entries (e.g. the FP8 Q.K^T reading's qk_dtype and q_scale)."""
     h = host_step_inputs(inp)
     pools = host_pools(inp, w)
     kw = dict(theta=w.rope_theta, eps=w.rms_eps, kv_dtype=w.kv_dtype,
@@ -29,6 +30,7 @@ def oracle_step(w, inp):
     cfg = oracle_cfg(inp, w)
     cfg["k_scale"] = np.float32(w.k_scale).item()
     cfg["v_scale"] = np.float32(w.v_scale).item()
+    cfg.update(extra or {})
     B, Hq, Tq = w.batch, w.num_q_heads, w.tokens
     if Tq == 1:
         pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],

@@ -39,7 +39,7 @@ def run_varlen(w, g, cfg=None, q_start=None, total=None):
     return {"q_out": q_out, "out": out, "lse": lse, "error": int(err.item()), "cfg": cfg}
 
 
-def oracle_varlen(w, inp, seqs=None):
+def oracle_varlen(w, inp, seqs=None, extra=None):
     h = host_step_inputs(inp)
     kw = dict(theta=w.rope_theta, eps=w.rms_eps, kv_dtype=w.kv_dtype,
               k_scale=np.float32(w.k_scale).item(), v_scale=np.float32(w.v_scale).item(),
@@ -48,6 +48,7 @@ def oracle_varlen(w, inp, seqs=None):
                              h["wk"], h["block_table"], **kw)
     cfg = oracle_cfg(inp, w)
     cfg["k_scale"], cfg["v_scale"] = kw["k_scale"], kw["v_scale"]
+    cfg.update(extra or {})
     ref = mt.attention_varlen(pro["q_out"], host_pools(inp, w), pro, h["seq_lens"], w.new_tokens,
                               h["block_table"], cfg, seqs=seqs)
     return pro, ref
