@@ -161,3 +161,38 @@ def test_prefill_full_size_sampled(name):
                                            cfg["sm_scale"])
                 check_output(out[b, j, hh], o_ref[0], w.kv_dtype, f"seq {b} token {j} head {hh}")
                 assert abs(lse[b, j, hh] - l_ref[0]) <= 1e-4 + 1e-5 * abs(l_ref[0])
+
+
+@pytest.mark.slow
+def test_prefill_longest_prompt():
+    """One prompt at the 2^18-token maximum (4096 pages, 8 q / 1 KV head) beside a
+    short one: q_out of sampled tokens bit-exact, sampled outputs and lse
+    against the oracle (its prologue runs on every token: all k/v rows are read)."""
+    dev = device()
+    T = 1 << 18
+    w = wl.custom([T, T], num_q_heads=8, num_kv_heads=1, tokens=T, seed=855)
+    g = wl.make_inputs(w, device=dev)
+    pools = host_pools(g, w)
+    print("prefill 2 x 262144 tokens, 8q/1kv", flush=True)
+    res = run_prefill(w, g)
+    assert res["error"] == 0
+    h = host_step_inputs(g)
+    b = 0
+    pro = mt.prologue_tokens(h["q"].reshape(2, T, 8, 128)[[b]], h["k"].reshape(2, T, 1, 128)[[b]],
+                             h["v"].reshape(2, T, 1, 128)[[b]],
+                             h["positions"].reshape(2, T)[[b]], h["wq"], h["wk"],
+                             h["block_table"][[b]], theta=w.rope_theta, eps=w.rms_eps,
+                             kv_dtype="bf16")
+    q_out = pro["q_out"].reshape(1, T, 8, 128)
+    got_q = bits_u16(res["q_out"]).reshape(2, T, 8, 128)
+    pick = [0, 1, 4095, 65536, T // 2 + 7, T - 2, T - 1]
+    assert np.array_equal(got_q[b, pick], q_out[0, pick])
+    cfg = oracle_cfg(g, w)
+    K, V = _sequence_kv(pools, pro, 0, 0, h["seq_lens"][[b]], h["block_table"][[b]], cfg)
+    out, lse = to_f64(res["out"]), to_f64(res["lse"])
+    for j in pick:
+        lim = mt.causal_limit(T, T, j)
+        o_ref, l_ref = attend_full(bf16_bits_to_f64(q_out[0, j]), K[:lim], V[:lim], cfg["sm_scale"])
+        for hh in (0, 5, 7):
+            check_output(out[b, j, hh], o_ref[hh], "bf16", f"token {j} head {hh}")
+            assert abs(lse[b, j, hh] - l_ref[hh]) <= 1e-4 + 1e-5 * abs(l_ref[hh])
