@@ -10,7 +10,8 @@
 // whole group.
 //
 // Mapping on CDNA4 (wave64, matrix cores):
-//   * workgroup = one worker of the schedule; wave = one KV head of it.
+//   * workgroup = one worker of the schedule; wave = one (KV head, block of
+//     16 columns) of it at a time.
 //   * S^T[64 tokens][16 cols] = K[64][128] . Q^T[128][16] with
 //     v_mfma_f32_16x16x32_bf16: column j*G + h is q head h of the group for
 //     new token j, so the 8 heads of the pages' model fill 8 of the 16
@@ -26,7 +27,8 @@
 //     a wave requests the next tile's K and V in one burst after P.V.
 //   * FP8 E4M3 codes are widened to BF16 exactly (v_cvt_scalef32_pk_bf16_fp8
 //     with scale 1); k_scale folds into the softmax scale, v_scale into the
-//     output.
+//     output.  With FP8 scores (kQk8) the K codes feed FP8 matrix cores as
+//     stored, against q's codes; q_scale then folds into the softmax scale.
 //   * row max and row sum: 16 values per lane in registers, then two xor
 //     shuffles across the 4 lanes that hold the same column.
 
