@@ -270,7 +270,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
 // The ragged batch's work list: every (sequence, block of new tokens) with at
 // least one token, sorted by its tile count (the rows its last token attends,
 // in 64-row tiles), longest first -- a counting sort over tile-count buckets
-// (tiles >> shift), in one 1024-thread workgroup.  Layout of `work`: [0] item
+// (tiles >> shift), in one 1024-thread workgroup: wave w takes sequences w,
+// w + 16, ..., its lanes the sequence's blocks.  Layout of `work`: [0] item
 // count, then from byte kPrefillListOffset int2 (sequence, block) pairs, at
 // most max_items of them.  Order within a bucket is arrival order; it decides
 // only which workgroup runs an item, not any result.
@@ -290,7 +291,8 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     int32_t* __restrict__ error_word) {
   __shared__ int s_bucket[kPrefillBuckets];
   __shared__ int s_wave[kPlanThreads / kWave + 1];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  constexpr int kWaves = kPlanThreads / kWave;
   const int tpb = kPrefillColumns / geo.group;
   const int max_len = geo.max_blocks * kPage;
   auto bucket_of = [&](int T, int L, int qb) {
@@ -302,13 +304,13 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   for (int i = tid; i < kPrefillBuckets; i += kPlanThreads) s_bucket[i] = 0;
   __syncthreads();
   bool bad = false;
-  for (int b = tid; b < geo.batch; b += kPlanThreads) {
+  for (int b = wave; b < geo.batch; b += kWaves) {
     int T, L;
     if (!ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L)) {
-      bad = true;
+      bad |= lane == 0;
       continue;
     }
-    for (int qb = 0; qb * tpb < T; ++qb) atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
+    for (int qb = lane; qb * tpb < T; qb += kWave) atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
   }
   __syncthreads();
   // exclusive offsets over the buckets: thread t owns buckets [4t, 4t + 4)
@@ -326,10 +328,10 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   }
   __syncthreads();
   int2* list = (int2*)((char*)work + kPrefillListOffset);
-  for (int b = tid; b < geo.batch; b += kPlanThreads) {
+  for (int b = wave; b < geo.batch; b += kWaves) {
     int T, L;
     if (!ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L)) continue;
-    for (int qb = 0; qb * tpb < T; ++qb) {
+    for (int qb = lane; qb * tpb < T; qb += kWave) {
       const int pos = atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
       if (pos < max_items) list[pos] = make_int2(b, qb);
     }
