@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
   constexpr int kThreads = kMergeWaves * kWave;
   const int slice = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = geo.tokens, G0 = geo.group;
-  if (fold_token_status && slice == 0 && g == 0 && threadIdx.x < T) {
+  if (fold_token_status && slice == 0 && g == 0 && (int)threadIdx.x < T) {
     const int32_t st = plan.token_status[(size_t)b * T + threadIdx.x];
     if (st) atomicOr(plan.error_word, st);
   }
