@@ -261,7 +261,10 @@ def prefill_leg(dev, reps=10, warmup=3):
             attn_args = (cfg, g["q_start"], q_out, g["k_cache"], g["v_cache"], g["block_table"],
                          g["seq_lens"], ws, out, lse, err)
         else:
-            step_fn, attn_fn = lb.prefill_step, lb.prefill_attention
+            # with a workspace: the longest-first work list, as the ragged call
+            ws = lb.alloc_prefill_workspace(cfg, w.batch, w.batch * w.tokens, device=dev)
+            step_fn = lambda *a: lb.prefill_step(*a, workspace=ws)
+            attn_fn = lambda *a: lb.prefill_attention(*a, workspace=ws)
             step_args = (cfg, g["q"], g["k"], g["v"], g["positions"]) + common
             attn_args = (cfg, q_out, g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"],
                          out, lse, err)

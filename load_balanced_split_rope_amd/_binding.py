@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # LBSR_LIB may name another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("LBSR_LIB") or os.path.join(HERE, "liblbsr.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 HEAD_DIM = 128
 PAGE_SIZE = 64
 TILE_ELEMS = HEAD_DIM * PAGE_SIZE
@@ -36,7 +36,7 @@ EXPORTS = (
     "lbsr_workspace_layout", "lbsr_workspace_size", "lbsr_rope_norm_kv_write", "lbsr_plan",
     "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed", "lbsr_prefill_attention",
     "lbsr_prefill_step", "lbsr_prefill_attention_varlen", "lbsr_prefill_step_varlen",
-    "lbsr_prefill_varlen_workspace_size",
+    "lbsr_prefill_workspace_size",
 )
 
 
@@ -115,16 +115,16 @@ def _declare(lib):
                              + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t, _P,
                                             _P, _P]),
         "lbsr_prefill_attention": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
-                                   + [_P] * 9),
+                                   + [_P] * 6 + [ctypes.c_size_t] + [_P] * 4),
         "lbsr_prefill_step": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
-                              + [_P] * 15),
+                              + [_P] * 12 + [ctypes.c_size_t] + [_P] * 4),
         "lbsr_prefill_attention_varlen": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params),
                                                _I32, _I32] + [_P] * 7 + [ctypes.c_size_t]
                                               + [_P] * 4),
         "lbsr_prefill_step_varlen": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32,
                                           _I32] + [_P] * 13 + [ctypes.c_size_t] + [_P] * 4),
-        "lbsr_prefill_varlen_workspace_size": (st, [ctypes.POINTER(Shape), _I32, _I32,
-                                                    ctypes.POINTER(ctypes.c_size_t)]),
+        "lbsr_prefill_workspace_size": (st, [ctypes.POINTER(Shape), _I32, _I32,
+                                             ctypes.POINTER(ctypes.c_size_t)]),
         "lbsr_decode_step_timed": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                                    + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t,
                                                   _P, _P, _P, ctypes.POINTER(ctypes.c_float), _P]),

@@ -494,6 +494,18 @@ lbsr_status validate_varlen(const lbsr_shape* shape, int32_t batch, int32_t tota
   return LBSR_OK;
 }
 
+// The uniform prefill's optional workspace (the sorted work list): null, or
+// large enough for batch * tokens_per_seq tokens.
+lbsr_status validate_uniform_workspace(const lbsr_shape* shape, int32_t batch, void* ws,
+                                       size_t ws_bytes) {
+  if (!ws) return LBSR_OK;
+  LBSR_CHECK(check_ptr(ws, 256, "workspace"));
+  const size_t need = varlen_workspace_bytes(shape, batch, batch * shape->tokens_per_seq);
+  if (ws_bytes < need)
+    return fail(LBSR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return LBSR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -644,15 +656,17 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
 lbsr_status lbsr_prefill_attention(const lbsr_shape* shape, const lbsr_params* params,
                                    int32_t batch, const void* q_out, const void* k_cache,
                                    const void* v_cache, const int32_t* block_table,
-                                   const int32_t* seq_lens, void* out, float* lse_out,
-                                   int32_t* error_word, void* stream) {
+                                   const int32_t* seq_lens, void* workspace, size_t ws_bytes,
+                                   void* out, float* lse_out, int32_t* error_word, void* stream) {
   g_last_error[0] = 0;
   LBSR_CHECK(validate_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table,
                               seq_lens, out, lse_out, error_word));
+  LBSR_CHECK(validate_uniform_workspace(shape, batch, workspace, ws_bytes));
   DeviceInfo d;
   LBSR_CHECK(current_device(&d));
   return run_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table, seq_lens, out,
-                     lse_out, error_word, (hipStream_t)stream);
+                     lse_out, error_word, (hipStream_t)stream, batch * shape->tokens_per_seq,
+                     nullptr, workspace);
 }
 
 lbsr_status lbsr_prefill_step(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
@@ -660,20 +674,21 @@ lbsr_status lbsr_prefill_step(const lbsr_shape* shape, const lbsr_params* params
                               const int32_t* positions, const int32_t* seq_lens,
                               const void* q_norm_w, const void* k_norm_w,
                               const int32_t* block_table, void* k_cache, void* v_cache,
-                              void* q_out, void* out, float* lse_out, int32_t* error_word,
-                              void* stream) {
+                              void* q_out, void* workspace, size_t ws_bytes, void* out,
+                              float* lse_out, int32_t* error_word, void* stream) {
   g_last_error[0] = 0;
   LBSR_CHECK(validate_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
                                block_table, k_cache, v_cache, q_out, error_word));
   LBSR_CHECK(validate_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table,
                               seq_lens, out, lse_out, error_word));
+  LBSR_CHECK(validate_uniform_workspace(shape, batch, workspace, ws_bytes));
   DeviceInfo d;
   LBSR_CHECK(current_device(&d));
   const hipStream_t s = (hipStream_t)stream;
   LBSR_CHECK(run_prologue(shape, params, batch, q, k, v, positions, q_norm_w, k_norm_w,
                           block_table, k_cache, v_cache, q_out, error_word, s));
   return run_prefill(shape, params, batch, q_out, k_cache, v_cache, block_table, seq_lens, out,
-                     lse_out, error_word, s);
+                     lse_out, error_word, s, batch * shape->tokens_per_seq, nullptr, workspace);
 }
 
 lbsr_status lbsr_prefill_attention_varlen(const lbsr_shape* shape, const lbsr_params* params,
@@ -695,8 +710,8 @@ lbsr_status lbsr_prefill_attention_varlen(const lbsr_shape* shape, const lbsr_pa
                      workspace);
 }
 
-lbsr_status lbsr_prefill_varlen_workspace_size(const lbsr_shape* shape, int32_t batch,
-                                               int32_t total_tokens, size_t* bytes) {
+lbsr_status lbsr_prefill_workspace_size(const lbsr_shape* shape, int32_t batch,
+                                        int32_t total_tokens, size_t* bytes) {
   g_last_error[0] = 0;
   if (!bytes) return fail(LBSR_E_INVALID, "bytes is null");
   LBSR_CHECK(check_shape(shape, batch));

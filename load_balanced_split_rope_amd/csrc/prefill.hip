@@ -267,7 +267,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     atomicOr(error_word, (int32_t)kErrSeqLen);
 }
 
-// The ragged batch's work list: every (sequence, block of new tokens) with at
+// The work list of a prefill (ragged, or uniform with q_start null): every
+// (sequence, block of new tokens) with at
 // least one token, sorted by its tile count (the rows its last token attends,
 // in 64-row tiles), longest first -- a counting sort over tile-count buckets
 // (tiles >> shift), in one 1024-thread workgroup: wave w takes sequences w,
@@ -277,7 +278,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
 // only which workgroup runs an item, not any result.
 __device__ inline bool ragged_range(const int32_t* q_start, const int32_t* seq_lens, int b,
                                     int total_tokens, int bound, int max_len, int& T, int& L) {
-  const int s0 = q_start[b], s1 = q_start[b + 1];
+  // no q_start: every sequence has `bound` new tokens (the uniform call)
+  const int s0 = q_start ? q_start[b] : b * bound;
+  const int s1 = q_start ? q_start[b + 1] : s0 + bound;
   if (s0 < 0 || s1 < s0 || s1 > total_tokens || s1 - s0 > bound) return false;
   T = s1 - s0;
   const int L_in = seq_lens[b];
@@ -360,7 +363,7 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
                           float inv_q_scale, hipStream_t stream) {
   const int nqb = prefill_blocks_q(geo);
   size_t grid = (size_t)nqb * geo.batch * geo.num_kv_heads;
-  if (q_start) {
+  if (work) {
     const int max_items = prefill_max_items(geo, total_tokens);
     int shift = 0;
     while ((geo.max_blocks >> shift) >= kPrefillBuckets) ++shift;
@@ -372,7 +375,7 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
     kernel<<<(unsigned)grid, kPrefillWaves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
         block_table, seq_lens, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0,
-        error_word, nqb, q_start, total_tokens, q_start ? work : nullptr, inv_q_scale);
+        error_word, nqb, q_start, total_tokens, work, inv_q_scale);
   };
   if (fp8 && qk_fp8) launch(prefill_kernel<true, true>);
   else if (fp8) launch(prefill_kernel<true, false>);

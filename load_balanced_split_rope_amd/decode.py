@@ -250,9 +250,11 @@ def decode_step_timed(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w,
 
 
 def prefill_attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, seq_lens, out,
-                      lse_out=None, error_word=None, stream=None):
+                      lse_out=None, error_word=None, stream=None, workspace=None):
     """lbsr_prefill_attention: every new token (cfg.tokens_per_seq per sequence)
-    attends its causal prefix; no schedule or workspace."""
+    attends its causal prefix.  workspace (from alloc_prefill_workspace with
+    batch * tokens_per_seq tokens) runs the blocks longest first, which pays
+    when the sequences' lengths differ; None keeps the workspace-free grid."""
     batch = q_out.shape[0]
     Hq, D = cfg.num_q_heads, B.HEAD_DIM
     _need(q_out, "q_out", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
@@ -264,17 +266,20 @@ def prefill_attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, s
         _need(error_word, "error_word", torch.int32, numel=1)
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
     s, p = cfg.shape(), cfg.params()
     B._check(B.lib().lbsr_prefill_attention(
         ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q_out), B._ptr(k_cache), B._ptr(v_cache),
-        B._ptr(block_table), B._ptr(seq_lens), B._ptr(out), B._ptr(lse_out), B._ptr(error_word),
-        B._stream(stream)))
+        B._ptr(block_table), B._ptr(seq_lens), B._ptr(workspace), _nbytes(workspace),
+        B._ptr(out), B._ptr(lse_out), B._ptr(error_word), B._stream(stream)))
 
 
 def prefill_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
                  block_table, k_cache, v_cache, q_out, out, lse_out=None, error_word=None,
-                 stream=None):
-    """lbsr_prefill_step: the prologue on every new token, then prefill attention."""
+                 stream=None, workspace=None):
+    """lbsr_prefill_step: the prologue on every new token, then prefill
+    attention (workspace as for prefill_attention)."""
     batch = q.shape[0]
     Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, B.HEAD_DIM
     _need(q, "q", torch.bfloat16, shape=cfg.tokens_shape(batch, Hq, D))
@@ -292,26 +297,34 @@ def prefill_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_no
         _need(error_word, "error_word", torch.int32, numel=1)
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
     s, p = cfg.shape(), cfg.params()
     B._check(B.lib().lbsr_prefill_step(
         ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
         B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
-        B._ptr(block_table), B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out), B._ptr(out),
-        B._ptr(lse_out), B._ptr(error_word), B._stream(stream)))
+        B._ptr(block_table), B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out),
+        B._ptr(workspace), _nbytes(workspace), B._ptr(out), B._ptr(lse_out),
+        B._ptr(error_word), B._stream(stream)))
 
 
-def prefill_varlen_workspace_size(cfg: DecodeConfig, batch: int, total_tokens: int) -> int:
-    """Bytes of a ragged prefill's workspace (its longest-first work list)."""
+def prefill_workspace_size(cfg: DecodeConfig, batch: int, total_tokens: int) -> int:
+    """Bytes of a prefill's workspace (its longest-first work list): total_tokens
+    is the packed count of a ragged batch, or batch * tokens_per_seq."""
     n = ctypes.c_size_t()
     s = cfg.shape()
-    B._check(B.lib().lbsr_prefill_varlen_workspace_size(ctypes.byref(s), batch, total_tokens,
-                                                        ctypes.byref(n)))
+    B._check(B.lib().lbsr_prefill_workspace_size(ctypes.byref(s), batch, total_tokens,
+                                                 ctypes.byref(n)))
     return n.value
 
 
 def alloc_prefill_workspace(cfg: DecodeConfig, batch: int, total_tokens: int, device="cuda"):
-    n = prefill_varlen_workspace_size(cfg, batch, total_tokens)
+    n = prefill_workspace_size(cfg, batch, total_tokens)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel()
 
 
 def _check_varlen(cfg, q_start, batch, total, workspace):

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lbsr_abi_version() == 3
+    assert lib.lbsr_abi_version() == 4
     for st in range(5):
         assert lib.lbsr_status_string(st).startswith(b"LBSR_")
     assert lib.lbsr_status_string(99) == b"unknown lbsr_status"
@@ -250,12 +250,13 @@ def test_tokens_beyond_block_table_reach_rejected(lib):
     p = DecodeConfig(8, 8, "bf16", 2, 100).params()
     fake = ctypes.c_void_p(0x10000)
     nul = ctypes.c_void_p(0)
-    got = lib.lbsr_prefill_attention(ctypes.byref(s), ctypes.byref(p), 4, *([fake] * 6), nul, nul,
-                                     nul)
+    # q_out, k_cache, v_cache, block_table, seq_lens, workspace, ws_bytes, out, lse, err, stream
+    got = lib.lbsr_prefill_attention(ctypes.byref(s), ctypes.byref(p), 4, *([fake] * 5), nul, 0,
+                                     fake, nul, nul, nul)
     assert got == B.E_INVALID and b"max_blocks_per_seq" in lib.lbsr_last_error()
     s = DecodeConfig(8, 8, "bf16", 2, 100, tokens_per_seq=128).shape()
     got = lib.lbsr_prefill_attention(ctypes.byref(s), ctypes.byref(p), 4, ctypes.c_void_p(0x10002),
-                                     *([fake] * 5), nul, nul, nul)
+                                     *([fake] * 4), nul, 0, fake, nul, nul, nul)
     assert got == B.E_INVALID and b"q_out" in lib.lbsr_last_error()   # shape accepted
 
 
@@ -267,7 +268,7 @@ def test_varlen_entry_points_validate_before_any_launch(lib):
     s, p = cfg.shape(), cfg.params()
     fake, odd, nul = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10002), ctypes.c_void_p(0)
     n = ctypes.c_size_t()
-    assert lib.lbsr_prefill_varlen_workspace_size(ctypes.byref(s), 8, 100, ctypes.byref(n)) == B.OK
+    assert lib.lbsr_prefill_workspace_size(ctypes.byref(s), 8, 100, ctypes.byref(n)) == B.OK
     assert n.value == 256 + 8 * (-(-100 // 32) + 8)          # 32 tokens per block at G = 8
     big = 1 << 20
     attn = lambda total, qs, ws, nb: lib.lbsr_prefill_attention_varlen(
@@ -310,3 +311,21 @@ def test_qk_dtype_validation(lib, kv_dtype, qk_dtype, q_scale, status):
         assert b"qk_dtype" not in lib.lbsr_last_error() and b"q_scale" not in lib.lbsr_last_error()
     else:
         assert got == status, lib.lbsr_last_error()
+
+
+def test_uniform_prefill_workspace_validation(lib):
+    """The uniform calls' workspace is optional; given, it must be 256-byte
+    aligned and hold the work list of batch * tokens_per_seq tokens."""
+    cfg = DecodeConfig(64, 8, "bf16", 200, 4000, tokens_per_seq=512)
+    s, p = cfg.shape(), cfg.params()
+    fake, nul = ctypes.c_void_p(0x10000), ctypes.c_void_p(0)
+    n = ctypes.c_size_t()
+    assert lib.lbsr_prefill_workspace_size(ctypes.byref(s), 8, 8 * 512, ctypes.byref(n)) == B.OK
+    assert n.value == 256 + 8 * (8 * 512 // 32 + 8)
+    call = lambda ws, nb: lib.lbsr_prefill_attention(ctypes.byref(s), ctypes.byref(p), 8,
+                                                     *([fake] * 5), ws, nb, fake, nul, nul, nul)
+    assert call(ctypes.c_void_p(0x10040), n.value) == B.E_INVALID     # not 256-byte aligned
+    assert call(fake, n.value - 1) == B.E_WORKSPACE
+    for ws, nb in ((fake, n.value), (nul, 0)):                        # valid: fails later (no GPU)
+        call(ws, nb)
+        assert b"workspace" not in lib.lbsr_last_error()

@@ -17,16 +17,20 @@ from gpu_util import device, to_device, config_for, run_step
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill(w, g, cfg=None):
+def run_prefill(w, g, cfg=None, sorted_list=True):
+    """lbsr_prefill_step; sorted_list: with a workspace (the longest-first work
+    list), else the workspace-free grid."""
     dev = g["q"].device
     cfg = cfg or config_for(w, g)
     q_out = torch.empty_like(g["q"])
     out = torch.empty(g["q"].shape, dtype=cfg.out_torch_dtype, device=dev)
     lse = torch.empty(cfg.tokens_shape(w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = (lb.alloc_prefill_workspace(cfg, w.batch, w.batch * w.tokens, device=dev)
+          if sorted_list else None)
     lb.prefill_step(cfg, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"], g["q_norm_w"],
                     g["k_norm_w"], g["block_table"], g["k_cache"], g["v_cache"], q_out, out,
-                    lse, err)
+                    lse, err, workspace=ws)
     torch.cuda.synchronize()
     return {"q_out": q_out, "out": out, "lse": lse, "error": int(err.item()), "cfg": cfg}
 
@@ -81,6 +85,19 @@ def test_prefill_matches_oracle(case):
     check_output(to_f64(res["out"]).reshape(ro.shape), ro, w.kv_dtype, "prefill output")
     lse = to_f64(res["lse"]).reshape(rl.shape)
     assert np.all(np.abs(lse - rl) <= 1e-4 + 1e-5 * np.abs(rl)), float(np.max(np.abs(lse - rl)))
+
+
+@pytest.mark.parametrize("case", [0, 1, 3])
+def test_workspace_free_grid_is_bit_identical(case):
+    """Without a workspace the blocks run in another order, on the same
+    arithmetic: outputs, lse and q_out are identical bit for bit."""
+    dev = device()
+    w = wl.custom(seed=800 + case, **CASES[case])
+    inp = wl.make_inputs(w)
+    a = run_prefill(w, to_device(inp, dev), sorted_list=True)
+    b = run_prefill(w, to_device(inp, dev), sorted_list=False)
+    for key in ("q_out", "out", "lse"):
+        assert torch.equal(a[key], b[key]), key
 
 
 def test_prefill_agrees_with_decode_path():

@@ -109,7 +109,7 @@ def test_equal_counts_match_uniform_call():
     lse = torch.empty(cfg.tokens_shape(3, 64), dtype=torch.float32, device=dev)
     lb.prefill_step(cfg, gu["q"], gu["k"], gu["v"], gu["positions"], gu["seq_lens"],
                     gu["q_norm_w"], gu["k_norm_w"], gu["block_table"], gu["k_cache"],
-                    gu["v_cache"], q_out, out, lse)
+                    gu["v_cache"], q_out, out, lse)                   # the workspace-free grid
     torch.cuda.synchronize()
     assert torch.equal(rv["q_out"].view(q_out.shape), q_out)
     assert torch.equal(rv["out"].view(out.shape), out)
