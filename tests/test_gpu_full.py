@@ -16,7 +16,7 @@ from gpu_util import device, run_step, compact_pools, remap_slots
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-FULL = ["uniform", "mix", "mix_fp8", "loguniform", "mix_mtp2"]
+FULL = ["uniform", "mix", "mix_fp8", "loguniform", "mix_mtp2", "mix_mtp4"]
 
 
 def sampled_checks(w, g, res, h, pro):
@@ -83,7 +83,7 @@ def test_full_workload(name):
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["mix", "mix_fp8", "loguniform", "mix_mtp2"])
+@pytest.mark.parametrize("name", ["mix", "mix_fp8", "loguniform", "mix_mtp2", "mix_mtp4"])
 def test_full_zero_query_lse(name):
     """Every (sequence, head) at full size: with q = 0 the lse is ln of the
     number of rows attended (L, or L - Tq + j + 1 for new token j)."""
