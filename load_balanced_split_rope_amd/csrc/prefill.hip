@@ -271,8 +271,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
 // (sequence, block of new tokens) with at
 // least one token, sorted by its tile count (the rows its last token attends,
 // in 64-row tiles), longest first -- a counting sort over tile-count buckets
-// (tiles >> shift), in one 1024-thread workgroup: wave w takes sequences w,
-// w + 16, ..., its lanes the sequence's blocks.  Layout of `work`: [0] item
+// (tiles >> shift), in one 1024-thread workgroup: per-sequence item counts
+// and their prefix sums in LDS (batch + 1 ints), then thread t takes items
+// t, t + 1024, ... (its sequence by binary search over the prefix sums).  Layout of `work`: [0] item
 // count, then from byte kPrefillListOffset int2 (sequence, block) pairs, at
 // most max_items of them.  Order within a bucket is arrival order; it decides
 // only which workgroup runs an item, not any result.
@@ -292,10 +293,10 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     Geometry geo, const int32_t* __restrict__ q_start, const int32_t* __restrict__ seq_lens,
     int total_tokens, int32_t* __restrict__ work, int max_items, int shift,
     int32_t* __restrict__ error_word) {
+  extern __shared__ int s_cu[];                     // batch + 1: items before each sequence
   __shared__ int s_bucket[kPrefillBuckets];
   __shared__ int s_wave[kPlanThreads / kWave + 1];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  constexpr int kWaves = kPlanThreads / kWave;
+  const int tid = threadIdx.x, B = geo.batch;
   const int tpb = kPrefillColumns / geo.group;
   const int max_len = geo.max_blocks * kPage;
   auto bucket_of = [&](int T, int L, int qb) {
@@ -304,16 +305,44 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     const int k = tiles >> shift;
     return kPrefillBuckets - 1 - (k < kPrefillBuckets ? k : kPrefillBuckets - 1);  // longest first
   };
+  // items (blocks of new tokens) per sequence; none for a malformed range
+  bool bad = false;
+  for (int b = tid; b < B; b += kPlanThreads) {
+    int T, L;
+    const bool ok = ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L);
+    bad |= !ok;
+    s_cu[b] = ok ? (T + tpb - 1) / tpb : 0;
+  }
   for (int i = tid; i < kPrefillBuckets; i += kPlanThreads) s_bucket[i] = 0;
   __syncthreads();
-  bool bad = false;
-  for (int b = wave; b < geo.batch; b += kWaves) {
-    int T, L;
-    if (!ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L)) {
-      bad |= lane == 0;
-      continue;
+  int carry = 0;                                    // exclusive prefix sums, 1024 at a time
+  for (int base = 0; base < B; base += kPlanThreads) {
+    const int b = base + tid;
+    const int n = b < B ? s_cu[b] : 0;
+    int sum = 0;
+    const int incl = block_inclusive_scan(n, s_wave, sum);
+    if (b < B) s_cu[b] = carry + incl - n;
+    carry += sum;
+  }
+  if (tid == 0) s_cu[B] = carry;
+  __syncthreads();
+  const int N = carry;
+  // item i -> (sequence, block): the last b with s_cu[b] <= i (empty sequences skipped)
+  auto locate = [&](int i, int& b, int& qb, int& T, int& L) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_cu[mid] <= i) lo = mid;
+      else hi = mid - 1;
     }
-    for (int qb = lane; qb * tpb < T; qb += kWave) atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
+    b = lo;
+    qb = i - s_cu[b];
+    ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L);
+  };
+  for (int i = tid; i < N; i += kPlanThreads) {
+    int b, qb, T, L;
+    locate(i, b, qb, T, L);
+    atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
   }
   __syncthreads();
   // exclusive offsets over the buckets: thread t owns buckets [4t, 4t + 4)
@@ -331,17 +360,15 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   }
   __syncthreads();
   int2* list = (int2*)((char*)work + kPrefillListOffset);
-  for (int b = wave; b < geo.batch; b += kWaves) {
-    int T, L;
-    if (!ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L)) continue;
-    for (int qb = lane; qb * tpb < T; qb += kWave) {
-      const int pos = atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
-      if (pos < max_items) list[pos] = make_int2(b, qb);
-    }
+  for (int i = tid; i < N; i += kPlanThreads) {
+    int b, qb, T, L;
+    locate(i, b, qb, T, L);
+    const int pos = atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
+    if (pos < max_items) list[pos] = make_int2(b, qb);
   }
   // overlapping ranges (a malformed q_start) can give more items than the list holds
-  if (tid == 0) work[0] = total < max_items ? total : max_items;
-  if (error_word && (bad || (tid == 0 && total > max_items)))
+  if (tid == 0) work[0] = N < max_items ? N : max_items;
+  if (error_word && (bad || (tid == 0 && N > max_items)))
     atomicOr(error_word, (int32_t)kErrQueryStart);
 }
 
@@ -367,8 +394,9 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
     const int max_items = prefill_max_items(geo, total_tokens);
     int shift = 0;
     while ((geo.max_blocks >> shift) >= kPrefillBuckets) ++shift;
-    prefill_plan_kernel<<<1, kPlanThreads, 0, stream>>>(geo, q_start, seq_lens, total_tokens,
-                                                         work, max_items, shift, error_word);
+    const size_t lds = sizeof(int) * ((size_t)geo.batch + 1);
+    prefill_plan_kernel<<<1, kPlanThreads, lds, stream>>>(geo, q_start, seq_lens, total_tokens,
+                                                           work, max_items, shift, error_word);
     grid = (size_t)max_items * geo.num_kv_heads;
   }
   auto launch = [&](auto kernel) {
