@@ -198,3 +198,23 @@ def test_ragged_prefill_full_size_sampled():
         r = int(starts[seqs[i]]) + j
         check_output(out[r, hh], o, "bf16", f"seq {seqs[i]} token {j} head {hh}")
         assert abs(lse[r, hh] - l) <= 1e-4 + 1e-5 * abs(l)
+
+
+@pytest.mark.slow
+def test_ragged_largest_batch():
+    """16384 sequences (the batch limit) with 0 to 3 new tokens each: the plan's
+    per-sequence prefix sums fill its LDS; sampled sequences against the oracle."""
+    dev = device()
+    rng = np.random.default_rng(905)
+    B = 16384
+    counts = rng.integers(0, 4, B).tolist()
+    lens = (np.array(counts) + rng.integers(1, 200, B)).tolist()
+    w = wl.custom(lens, num_q_heads=8, num_kv_heads=1, seed=905, new_tokens=counts)
+    inp = wl.make_inputs(w)
+    print(f"ragged batch of {B}, {sum(counts)} new tokens", flush=True)
+    res = run_varlen(w, to_device(inp, dev))
+    assert res["error"] == 0
+    seqs = sorted({0, B - 1} | {int(b) for b in rng.choice(np.nonzero(np.array(counts))[0], 40)})
+    pro, ref = oracle_varlen(w, inp, seqs=seqs)
+    assert np.array_equal(bits_u16(res["q_out"]), pro["q_out"])
+    check_against(w, res, ref)
