@@ -471,8 +471,8 @@ lbsr_status validate_prefill(const lbsr_shape* shape, const lbsr_params* params,
   return LBSR_OK;
 }
 
-// Bytes of a ragged prefill's workspace: header + one int2 per work item.
-size_t varlen_workspace_bytes(const lbsr_shape* shape, int32_t batch, int32_t total_tokens) {
+// Bytes of a prefill's workspace: header + one int2 per work item.
+size_t prefill_workspace_bytes(const lbsr_shape* shape, int32_t batch, int32_t total_tokens) {
   const int64_t tpb = lbsr::kPrefillColumns / (shape->num_q_heads / shape->num_kv_heads);
   const int64_t items = (total_tokens + tpb - 1) / tpb + batch;
   return (size_t)lbsr::kPrefillListOffset + 8 * (size_t)items;
@@ -488,7 +488,7 @@ lbsr_status validate_varlen(const lbsr_shape* shape, int32_t batch, int32_t tota
     return fail(LBSR_E_UNSUPPORTED, "total_tokens %d is too many rows", total_tokens);
   LBSR_CHECK(check_ptr(q_start, 4, "q_start"));
   LBSR_CHECK(check_ptr(ws, 256, "workspace"));
-  const size_t need = varlen_workspace_bytes(shape, batch, total_tokens);
+  const size_t need = prefill_workspace_bytes(shape, batch, total_tokens);
   if (ws_bytes < need)
     return fail(LBSR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return LBSR_OK;
@@ -500,7 +500,7 @@ lbsr_status validate_uniform_workspace(const lbsr_shape* shape, int32_t batch, v
                                        size_t ws_bytes) {
   if (!ws) return LBSR_OK;
   LBSR_CHECK(check_ptr(ws, 256, "workspace"));
-  const size_t need = varlen_workspace_bytes(shape, batch, batch * shape->tokens_per_seq);
+  const size_t need = prefill_workspace_bytes(shape, batch, batch * shape->tokens_per_seq);
   if (ws_bytes < need)
     return fail(LBSR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return LBSR_OK;
@@ -716,7 +716,7 @@ lbsr_status lbsr_prefill_workspace_size(const lbsr_shape* shape, int32_t batch,
   if (!bytes) return fail(LBSR_E_INVALID, "bytes is null");
   LBSR_CHECK(check_shape(shape, batch));
   if (total_tokens < 0) return fail(LBSR_E_INVALID, "total_tokens %d < 0", total_tokens);
-  *bytes = varlen_workspace_bytes(shape, batch, total_tokens);
+  *bytes = prefill_workspace_bytes(shape, batch, total_tokens);
   return LBSR_OK;
 }
 
