@@ -31,6 +31,8 @@
 //     therefore dispatched from a work list that a one-workgroup plan sorts
 //     by tile count, longest first, with no empty entries (prefill_plan_kernel).
 
+#include <type_traits>
+
 #include "launch.h"
 #include "plan.h"
 #include "tile_math.h"
@@ -161,9 +163,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
   }
   store_tile(0, pre);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile: scores, online softmax, P.V.  Only the block's last tile can
+  // reach past the sequence end, so the V-row masking is compiled into that
+  // step alone (applied to every tile it costs two VALU ops per V dword).
+  auto tile_step = [&](int t, auto last_c) {
+    constexpr bool kLast = decltype(last_c)::value;
     const int stage = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1, pre);
+    if constexpr (!kLast) load_tile(t + 1, pre);
     const u32x4* kf = s_kv[stage];
     const u32x4* vf = s_kv[stage] + NF * kWave;
 
@@ -201,11 +207,19 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
       softmax_tile(S[cb], st[cb], limit_first - row0 < kPage, limit[cb] - row0, kc,
                    score_scale_log2, pB[cb]);
 
-    // ---- P.V, with rows at or past the sequence end zeroed in the last tile ----
-    const int rem = L - row0;
+    // ---- P.V; in the last tile, rows at or past the sequence end are zeroed ----
     uint32_t keep[2][4];
-    const bool tail = rem < kPage;
-    if (tail) v_keep_masks<kFp8>(rem, kc, keep);
+    if constexpr (kLast) {
+      const int rem = L - row0;
+      if (rem < kPage) {
+        v_keep_masks<kFp8>(rem, kc, keep);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) keep[s][x] = ~0u;
+      }
+    }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
@@ -213,14 +227,14 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
         bf16x8 a;
         if constexpr (kFp8) {
           u32x4 w = vf[db * kWave + lane];
-          if (tail) {
+          if constexpr (kLast) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) w[x] &= keep[0][x];
           }
           a = s ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
         } else {
           u32x4 w = vf[(2 * db + s) * kWave + lane];
-          if (tail) {
+          if constexpr (kLast) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) w[x] &= keep[s][x];
           }
@@ -231,9 +245,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
           st[cb].O[db] = mfma_bf16(a, pB[cb][s], st[cb].O[db]);
       }
     }
-    if (t + 1 < ntiles) store_tile(stage ^ 1, pre);
-    __syncthreads();
-  }
+    if constexpr (!kLast) {
+      store_tile(stage ^ 1, pre);
+      __syncthreads();
+    }
+  };
+  for (int t = 0; t + 1 < ntiles; ++t) tile_step(t, std::false_type{});
+  tile_step(ntiles - 1, std::true_type{});
   if (bad_page && error_word) atomicOr(error_word, (int32_t)kErrPage);
 
   // ---- output ----
