@@ -112,6 +112,21 @@ class Case:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
+    def step_distribution(self, sched, steps):
+        """Whole-step times, each step bracketed by HIP events on the launch
+        stream (the steps still run back to back): median, p10 and p90 in us."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            self.step(i, sched)
+            b.record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        p10, p50, p90 = np.percentile(us, [10, 50, 90])
+        return {"steps": steps, "median_us": round(float(p50), 2), "p10_us": round(float(p10), 2),
+                "p90_us": round(float(p90), 2)}
+
     def kernel_times(self, sched, reps):
         """Per-launch ms (schedule + prologue, split, merge): HIP events on the launch stream."""
         ms = np.array([lb.decode_step_timed(*self.args(i, sched)) for i in range(reps)])
@@ -375,6 +390,7 @@ def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_
             dyn = cand
     r["schedule"] = dyn
     r["ms"] = case.timed_steps(dyn, steps, warmup)
+    r["step_dist"] = case.step_distribution(dyn, steps)
     _, kmean = case.kernel_times(dyn, max(20, min(steps, 100)))
     r["kernel_ms"] = kmean
     r["balance"] = {"dynamic": load_balance(case.trace(dyn))}
@@ -460,6 +476,7 @@ def main():
                        "XCD-weighted shares" if r["schedule"].xcd_weights else "equal shares"),
                    "parallelism": "1 GPU"},
         "us_per_step": round(ms * 1e3, 2),
+        "step_us_distribution": r["step_dist"],
         "xcd_weights": r.get("xcd_weights"),
         "xcd_rates_tiles_per_us": r.get("xcd_rates"),
         "xcd_weighting_ab": r.get("ab"),
@@ -493,6 +510,7 @@ def main():
                 "workload": "mix_fp8: the same mix with an FP8 E4M3 cache "
                             "(k scale 2^-5, v scale 2^-4)",
                 "us_per_step": round(ms8 * 1e3, 2),
+                "step_us_distribution": r8["step_dist"],
                 "xcd_weights": r8.get("xcd_weights"),
                 "xcd_weighting_ab": r8.get("ab"),
                 "us_per_step_graph": round(r8["graph_ms"] * 1e3, 2),
