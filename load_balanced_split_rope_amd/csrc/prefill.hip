@@ -39,6 +39,53 @@
 
 namespace lbsr {
 
+// The online softmax of one tile as softmax_tile computes it, with the score
+// scale applied inside the exponent: the column max is taken over the raw
+// scores and scaled once (c > 0, so fl(max s * c) = max fl(s * c): the same
+// running max), and p = 2^fma(s, c, -m), one instruction per score where
+// softmax_tile spends a multiply and a subtract.  p differs from softmax_tile's
+// only by the rounding of s * c that the fma skips (the row at the max gets
+// 2^r with |r| <= half an ulp of m instead of exactly 1).
+__device__ __forceinline__ void softmax_tile_fma(const f32x4 (&S)[4], SoftmaxState& st, bool mask,
+                                                 int lim, int kc, float c, bf16x8 (&pB)[2]) {
+  float x[16];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * tb + e] = S[tb][e];
+  if (mask) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (16 * tb + 4 * kc + e >= lim) x[4 * tb + e] = -__builtin_inff();
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  mx = max_xor32(max_xor16(mx)) * c;
+  if (__any(mx > st.m + 8.f)) {                          // wave-uniform
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - (m_new == -__builtin_inff() ? 0.f : m_new));
+    st.lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.O[i] *= alpha;
+    st.m = m_new;
+  }
+  const float nbase = st.m == -__builtin_inff() ? 0.f : -st.m;
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] = fast_exp2(__builtin_fmaf(x[i], c, nbase));
+    psum += x[i];
+  }
+  st.lsum += psum;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)x[8 * s + e];
+}
+
 template <bool kFp8, bool kQk8>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
@@ -204,8 +251,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     const int row0 = t * kPage;
 #pragma unroll
     for (int cb = 0; cb < kPrefillBlocks; ++cb)
-      softmax_tile(S[cb], st[cb], limit_first - row0 < kPage, limit[cb] - row0, kc,
-                   score_scale_log2, pB[cb]);
+      softmax_tile_fma(S[cb], st[cb], limit_first - row0 < kPage, limit[cb] - row0, kc,
+                       score_scale_log2, pB[cb]);
 
     // ---- P.V; in the last tile, rows at or past the sequence end are zeroed ----
     uint32_t keep[2][4];
