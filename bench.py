@@ -249,12 +249,16 @@ def prefill_flops(w):
     return 4 * 128 * w.num_q_heads * tot
 
 
-def prefill_leg(dev, reps=10, warmup=3):
+def prefill_leg(dev, reps=10, warmup=3, names=None):
     """lbsr_prefill_step (prologue + attention) and lbsr_prefill_attention alone,
     each timed with HIP events on the launch stream; the attention kernel is
-    matrix-core bound, so its roofline is flops against the BF16 MFMA peak."""
+    matrix-core bound, so its roofline is flops against the BF16 MFMA peak.
+    names: only these prefill workloads (BF16 scores), e.g. for a counter pass."""
     legs = {}
-    for name, qk in [(n, "bf16") for n in wl.PREFILL_NAMES] + [("prefill_fp8", "fp8")]:
+    runs = [(n, "bf16") for n in wl.PREFILL_NAMES] + [("prefill_fp8", "fp8")]
+    if names:
+        runs = [(n, "bf16") for n in names]
+    for name, qk in runs:
         w = wl.named(name)
         g = wl.make_inputs(w, device=dev)
         cfg = lb.DecodeConfig(w.num_q_heads, w.num_kv_heads, w.kv_dtype, g["max_blocks"],
@@ -429,11 +433,18 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill leg (prefill, prefill_fp8, chunked_prefill, "
                          "ragged_prefill), as JSON")
+    ap.add_argument("--prefill-names", default="",
+                    help="with --prefill-only: comma-separated prefill workloads to run "
+                         "(BF16 scores only), e.g. 'prefill' for a counter pass")
     ap.add_argument("--no-xcd-weights", action="store_true",
                     help="equal worker shares only (skip the per-XCD rate calibration)")
     ap.add_argument("--quick", action="store_true",
                     help="headline workload only: no graph, static sweep, FP8 or CPU legs")
     args = ap.parse_args()
+    prefill_names = [n for n in args.prefill_names.split(",") if n]
+    bad = [n for n in prefill_names if n not in wl.PREFILL_NAMES]
+    if bad:
+        ap.error(f"--prefill-names: unknown prefill workloads {bad}; known: {list(wl.PREFILL_NAMES)}")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path here "
               "is single-GPU and has no multi-GPU mode", file=sys.stderr)
@@ -449,7 +460,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": 5}))
         return
     if args.prefill_only:
-        print(json.dumps({"prefill": prefill_leg(dev)}), flush=True)
+        print(json.dumps({"prefill": prefill_leg(dev, names=prefill_names or None)}), flush=True)
         return
     P = lb.device_workers(0)
     full = not args.quick
