@@ -184,6 +184,7 @@ class Case:
 WORKLOAD_TEXT = {
     "mix": "mix: 1 x 131072 + 31 x 4096 tokens",
     "mix_fp8": "mix_fp8: 1 x 131072 + 31 x 4096 tokens, FP8 E4M3 cache",
+    "tiny": "tiny: 4 sequences of 1, 63, 64 and 200 tokens, 8 q / 1 KV heads (latency-bound)",
     "uniform": "uniform: 32 x 4096 tokens",
     "loguniform": "loguniform: 64 sequences, lengths log-uniform in [512, 262144], FP8 cache",
     "mix_mtp2": "mix_mtp2: 1 x 131072 + 31 x 4096 tokens, 2 new tokens per sequence",
@@ -565,7 +566,7 @@ def main():
             # equals the dynamic plan (expected ratio ~1), and the log-uniform
             # mixed batch with an FP8 cache
             controls = {}
-            for name in ("uniform", "loguniform"):
+            for name in ("tiny", "uniform", "loguniform"):
                 wc = wl.named(name)
                 steps_c = args.steps if name == "uniform" else max(10, args.steps // 4)
                 rc = measure(wc, dev, P, steps_c, args.warmup, False, False)
@@ -576,6 +577,7 @@ def main():
                 cbc = compulsory_bytes(wc)["total"]
                 controls[name] = {
                     "workload": WORKLOAD_TEXT[name], "us_per_step": round(rc["ms"] * 1e3, 2),
+                    "step_us_distribution": rc["step_dist"],
                     "value_GBs": round(cbc / (rc["ms"] * 1e-3) / 1e9, 1),
                     "hbm_frac_step": round(cbc / (rc["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "static_default_us_per_step": round(st * 1e3, 2),
