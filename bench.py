@@ -572,6 +572,8 @@ def main():
                 rc = measure(wc, dev, P, steps_c, args.warmup, False, False)
                 cc = Case(wc, dev)
                 st = case_static_ms(cc, P, steps_c)
+                # the launch-bound case: the step replayed as one captured graph
+                graph_ms = cc.graph_ms(rc["schedule"], steps_c) if name == "tiny" else None
                 del cc
                 torch.cuda.empty_cache()
                 cbc = compulsory_bytes(wc)["total"]
@@ -584,6 +586,8 @@ def main():
                     "dynamic_speedup_vs_static_default": round(st / rc["ms"], 3),
                     "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, rc["kernel_ms"])},
                 }
+                if graph_ms is not None:
+                    controls[name]["us_per_step_graph"] = round(graph_ms * 1e3, 2)
             result["controls"] = controls
             ro = measure(w, dev, P, args.steps, args.warmup, False, weighted, out_dtype="fp8")
             result["fp8_output"] = {
