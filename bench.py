@@ -589,6 +589,29 @@ def main():
                 if graph_ms is not None:
                     controls[name]["us_per_step_graph"] = round(graph_ms * 1e3, 2)
             result["controls"] = controls
+            # the merge folded into the split launch (opt-in), against two launches
+            fold = {}
+            for name in ("tiny", "uniform", "mix"):
+                wf = wl.named(name)
+                cf = Case(wf, dev)
+                s2 = lb.Schedule("dynamic", num_workers=P)
+                s1 = lb.Schedule("dynamic", num_workers=P, fold_merge=True)
+                for i in range(5):
+                    cf.step(i, s2)
+                    cf.step(i, s1)
+                t2, t1 = [], []
+                for _ in range(3):
+                    t2.append(cf.timed_steps(s2, 40, 2))
+                    t1.append(cf.timed_steps(s1, 40, 2))
+                fold[name] = {"workload": WORKLOAD_TEXT[name],
+                              "two_launches_us": round(float(np.median(t2)) * 1e3, 2),
+                              "folded_us": round(float(np.median(t1)) * 1e3, 2)}
+                if name == "tiny":
+                    fold[name]["two_launches_graph_us"] = round(cf.graph_ms(s2, 40) * 1e3, 2)
+                    fold[name]["folded_graph_us"] = round(cf.graph_ms(s1, 40) * 1e3, 2)
+                del cf
+                torch.cuda.empty_cache()
+            result["fold_merge"] = fold
             ro = measure(w, dev, P, args.steps, args.warmup, False, weighted, out_dtype="fp8")
             result["fp8_output"] = {
                 "workload": WORKLOAD_TEXT["mix"] + ", BF16 cache, output stored as E4M3 codes "

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define LBSR_ABI_VERSION 4
+#define LBSR_ABI_VERSION 5
 #define LBSR_NUM_XCDS 8     /* accelerator complex dies of an MI355X */
 #define LBSR_MAX_XCD_WEIGHT 65536
 #define LBSR_HEAD_DIM 128
@@ -160,11 +160,16 @@ typedef struct {
   float q_scale;            /* FP8 Q.K^T: q value = code * q_scale; > 0; ignored for BF16 */
 } lbsr_params;
 
+/* lbsr_sched_cfg.flags */
+#define LBSR_SCHED_FOLD_MERGE 1 /* merge split sequences inside the split-attention
+                                 * launch (see lbsr_attention); one new token per
+                                 * sequence (tokens_per_seq = 1) only */
+
 typedef struct {
   int32_t sched;         /* lbsr_sched */
   int32_t num_workers;   /* dynamic: P workers in [1, 1024]; 0 -> the device's CU count */
   int32_t static_splits; /* static: S splits per sequence in [1, 1024]; 0 -> max(1, P / batch) */
-  int32_t reserved;      /* must be 0 */
+  int32_t flags;         /* 0, or LBSR_SCHED_FOLD_MERGE */
   /* dynamic only: relative streaming speed of the compute units of each XCD
    * (see lbsr_plan).  All 0 -> every worker gets an equal share; else every
    * entry in [1, LBSR_MAX_XCD_WEIGHT].  Ignored (must be 0) for static. */
@@ -182,6 +187,8 @@ typedef struct {
   size_t token_status; /* int32[batch]: prologue error bits per token (decode step) */
   size_t partial_o;    /* float[C_max][Hq][128]: normalised partial outputs */
   size_t partial_lse;  /* float[C_max][Hq]: partial log2-sum-exp (internal) */
+  size_t arrivals;     /* int32[batch][Hkv]: chunks of each (sequence, KV head) done, for
+                        * LBSR_SCHED_FOLD_MERGE; the plan clears them (internal) */
   size_t total;        /* bytes the workspace needs */
   int32_t num_workers; /* W: workers (= attention workgroups) */
   int32_t max_chunks;  /* C_max = W + batch - 1 (dynamic) or batch * S (static) */
@@ -280,7 +287,14 @@ lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq
  *   q_out [batch][Hq][128] BF16   out [batch][Hq][128] BF16, or E4M3 codes
  *   (params->out_dtype)           lse_out nullable float[batch][Hq]
  * Rows at or past L_b of a sequence's last page are never used, whatever
- * they hold.  Deterministic: no atomics.
+ * they hold.  Deterministic.
+ * The merge is a second launch by default.  With cfg->flags =
+ * LBSR_SCHED_FOLD_MERGE ([A] "Why does dynamic scheduling matter in
+ * attention?" chains its kernels to cut launch gaps) there is one launch: the
+ * wave that finishes the last chunk of a (sequence, KV head) -- counted with
+ * a device-scope atomic after a device-scope fence -- merges its rows in
+ * chunk order.  Which wave that is varies, the arithmetic does not: results
+ * are deterministic either way (but not bit-identical between the two forms).
  */
 lbsr_status lbsr_attention(const lbsr_shape *shape, const lbsr_params *params, int32_t batch,
                            const void *q_out, const void *k_cache, const void *v_cache,

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # LBSR_LIB may name another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("LBSR_LIB") or os.path.join(HERE, "liblbsr.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 HEAD_DIM = 128
 PAGE_SIZE = 64
 TILE_ELEMS = HEAD_DIM * PAGE_SIZE
@@ -26,6 +26,7 @@ MAX_XCD_WEIGHT = 65536
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 KV_BF16, KV_FP8_E4M3 = 0, 1
 SCHED_DYNAMIC, SCHED_STATIC = 0, 1
+SCHED_FOLD_MERGE = 1           # lbsr_sched_cfg.flags: merge inside the split launch
 OUT_BF16, OUT_FP8_E4M3 = 0, 1
 QK_BF16, QK_FP8_E4M3 = 0, 1
 DEV_ERR_SEQ_LEN, DEV_ERR_PAGE, DEV_ERR_POSITION, DEV_ERR_QUERY_START = 1, 2, 4, 8
@@ -73,7 +74,7 @@ class Params(ctypes.Structure):
 
 class SchedCfg(ctypes.Structure):
     _fields_ = [("sched", ctypes.c_int32), ("num_workers", ctypes.c_int32),
-                ("static_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("static_splits", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("xcd_weight", ctypes.c_int32 * NUM_XCDS)]
 
 
@@ -82,7 +83,7 @@ class WsLayout(ctypes.Structure):
                 ("worker_chunk", ctypes.c_size_t), ("chunks", ctypes.c_size_t),
                 ("seq_chunk", ctypes.c_size_t), ("seq_len_eff", ctypes.c_size_t),
                 ("token_status", ctypes.c_size_t), ("partial_o", ctypes.c_size_t), ("partial_lse", ctypes.c_size_t),
-                ("total", ctypes.c_size_t), ("num_workers", ctypes.c_int32),
+                ("arrivals", ctypes.c_size_t), ("total", ctypes.c_size_t), ("num_workers", ctypes.c_int32),
                 ("max_chunks", ctypes.c_int32), ("static_splits", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 

@@ -180,7 +180,16 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
   if (!out) return fail(LBSR_E_INVALID, "out is NULL");
   if (cfg->sched != LBSR_SCHED_DYNAMIC && cfg->sched != LBSR_SCHED_STATIC)
     return fail(LBSR_E_INVALID, "sched %d unknown", cfg->sched);
-  if (cfg->reserved != 0) return fail(LBSR_E_INVALID, "cfg.reserved must be 0");
+  if (cfg->flags & ~LBSR_SCHED_FOLD_MERGE)
+    return fail(LBSR_E_INVALID, "cfg.flags 0x%x has unknown bits", (unsigned)cfg->flags);
+  if (cfg->flags & LBSR_SCHED_FOLD_MERGE) {
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    if (shape->tokens_per_seq != 1)
+      return fail(LBSR_E_UNSUPPORTED, "LBSR_SCHED_FOLD_MERGE needs tokens_per_seq = 1, not %d",
+                  shape->tokens_per_seq);
+    if (G & (G - 1))
+      return fail(LBSR_E_UNSUPPORTED, "LBSR_SCHED_FOLD_MERGE needs a power-of-two group, not %d", G);
+  }
   // a sequence gets at most one chunk per worker or split; the merge handles 1024
   if (cfg->num_workers < 0 || cfg->num_workers > 1024)
     return fail(LBSR_E_INVALID, "num_workers %d out of [0, 1024]", cfg->num_workers);
@@ -237,6 +246,7 @@ lbsr_status compute_layout(const lbsr_shape* shape, int32_t batch, const lbsr_sc
   out->token_status = off; off = align256(off + 4 * (size_t)batch * Tq);
   out->partial_o = off;    off = align256(off + 4 * (size_t)cmax * Tq * Hq * LBSR_HEAD_DIM);
   out->partial_lse = off;  off = align256(off + 4 * (size_t)cmax * Tq * Hq);
+  out->arrivals = off;     off = align256(off + 4 * (size_t)batch * shape->num_kv_heads);
   out->total = off;
   out->num_workers = (int32_t)W;
   out->max_chunks = (int32_t)cmax;
@@ -256,6 +266,7 @@ lbsr::PlanPtrs plan_ptrs(void* ws, const lbsr_ws_layout& l) {
   p.token_status = (int32_t*)(base + l.token_status);
   p.partial_o = (float*)(base + l.partial_o);
   p.partial_lse = (float*)(base + l.partial_lse);
+  p.arrivals = (int32_t*)(base + l.arrivals);
   return p;
 }
 
@@ -352,6 +363,8 @@ lbsr_status run_prologue(const lbsr_shape* shape, const lbsr_params* params, int
                     "prologue launch");
 }
 
+bool folded(const lbsr_sched_cfg* cfg) { return (cfg->flags & LBSR_SCHED_FOLD_MERGE) != 0; }
+
 lbsr::SchedParams sched_params(const lbsr_shape* shape, const lbsr_sched_cfg* cfg,
                                const lbsr_ws_layout& l) {
   lbsr::SchedParams sp{};
@@ -361,6 +374,7 @@ lbsr::SchedParams sched_params(const lbsr_shape* shape, const lbsr_sched_cfg* cf
   sp.splits = l.static_splits;
   sp.weighted = sp.dynamic && cfg->xcd_weight[0] != 0;  // validated: all zero or all positive
   for (int x = 0; x < lbsr::kXcds; ++x) sp.xcd_weight[x] = sp.weighted ? cfg->xcd_weight[x] : 1;
+  sp.fold_groups = folded(cfg) ? shape->num_kv_heads : 0;
   return sp;
 }
 
@@ -403,15 +417,15 @@ float score_scale_log2(const lbsr_params* p, int32_t kv_dtype) {
 lbsr_status run_split(const lbsr_shape* shape, const lbsr_params* params, int32_t batch,
                       const void* q_out, const void* kc, const void* vc, const int32_t* bt,
                       const lbsr_ws_layout& l, void* ws, void* out, float* lse_out,
-                      int64_t* trace, hipStream_t stream) {
+                      int64_t* trace, bool fold, bool fold_status, hipStream_t stream) {
   const lbsr::Geometry geo = geometry(shape, batch);
   const bool fp8 = shape->kv_dtype == LBSR_KV_FP8_E4M3;
   // outputs and partials carry o / out_scale (FP8 output), V's scale folded in
   const bool out_fp8 = params->out_dtype == LBSR_OUT_FP8_E4M3;
   const double vs = fp8 ? (double)params->v_scale : 1.0;
   const float o_scale = (float)(out_fp8 ? vs / (double)params->out_scale : vs);
-  return hip_status(lbsr::launch_split_attention(geo, fp8, out_fp8, qk_fp8(params),
-                                                 l.num_workers, q_out, kc, vc, bt,
+  return hip_status(lbsr::launch_split_attention(geo, fp8, out_fp8, qk_fp8(params), fold,
+                                                 fold_status, l.num_workers, q_out, kc, vc, bt,
                                                  plan_ptrs(ws, l), out, lse_out,
                                                  score_scale_log2(params, shape->kv_dtype),
                                                  o_scale, inv_q_scale(params), trace, stream),
@@ -593,7 +607,8 @@ lbsr_status lbsr_attention(const lbsr_shape* shape, const lbsr_params* params, i
   LBSR_CHECK(current_device(&d));
   const hipStream_t s = (hipStream_t)stream;
   LBSR_CHECK(run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
-                       lse_out, nullptr, s));
+                       lse_out, nullptr, folded(cfg), false, s));
+  if (folded(cfg)) return LBSR_OK;   // merged inside the split launch
   return run_combine(shape, params, batch, l, workspace, out, lse_out, false, s);
 }
 
@@ -640,9 +655,11 @@ static lbsr_status decode_step_impl(const lbsr_shape* shape, const lbsr_params* 
   mark(1);
   if (st == LBSR_OK)
     st = run_split(shape, params, batch, q_out, k_cache, v_cache, block_table, l, workspace, out,
-                   lse_out, trace, s);
+                   lse_out, trace, folded(cfg), true, s);
   mark(2);
-  if (st == LBSR_OK) st = run_combine(shape, params, batch, l, workspace, out, lse_out, true, s);
+  // folded: merged inside the split launch (its time then shows as 0 here)
+  if (st == LBSR_OK && !folded(cfg))
+    st = run_combine(shape, params, batch, l, workspace, out, lse_out, true, s);
   mark(3);
   if (kernel_ms) {
     if (st == LBSR_OK) st = hip_status(hipEventSynchronize(ev[3]), "hipEventSynchronize");

@@ -32,6 +32,8 @@
 //   * row max and row sum: 16 values per lane in registers, then two xor
 //     shuffles across the 4 lanes that hold the same column.
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "tile_math.h"
@@ -171,14 +173,121 @@ __device__ __forceinline__ int xcd_worker(int block, int num_blocks) {
   return start + j;
 }
 
+// The folded merge (LBSR_SCHED_FOLD_MERGE, one new token per sequence): one
+// wave merges the n chunk rows of (sequence b, KV head g) -- the G heads of
+// the group -- as the merge kernel does: weights 2^(lse - max) / sum per head
+// over the rows, then the weighted sum of the partial rows in row order.  A
+// row of the group is 32 G float4 ([16 slices of 8 channels][G heads][2
+// float4]); lane l owns float4 l + 64 j, j < kNf = 32 G / 64 (one for G <= 2),
+// all of head (l % 2G) / 2.  G is a power of two (the API checks), so lanes
+// h, h + G, h + 2G, ... share head h and reduce with xor shuffles.  Loads are
+// issued 8 lse / 16 float4 at a time, so a wave keeps them in flight.
+template <int kNf>
+__device__ inline void fold_merge(const Geometry& geo, const PlanPtrs& plan, int b, int g, int c0,
+                                  int n, void* __restrict__ out, float* __restrict__ lse_out,
+                                  int out_fp8, int lane) {
+  const int G = geo.group, Hq = geo.num_q_heads;
+  const size_t head0 = (size_t)g * G;
+  const float* lse = plan.partial_lse + (size_t)c0 * Hq + head0;   // row r: lse[r * Hq + h]
+  // 1. per head h = lane % G: max over the rows, then the sum of 2^(lse - max)
+  const int h = lane % G, rsub = lane / G, rstep = kWave / G;
+  float mx = -__builtin_inff();
+  for (int r0 = rsub; r0 < n; r0 += 8 * rstep) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * rstep;
+      x[u] = lse[(size_t)(r < n ? r : n - 1) * Hq + h];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r0 + u * rstep < n) mx = fmaxf(mx, x[u]);
+  }
+  for (int d = G; d < kWave; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+  float sum = 0.f;
+  for (int r0 = rsub; r0 < n; r0 += 8 * rstep) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * rstep;
+      x[u] = lse[(size_t)(r < n ? r : n - 1) * Hq + h];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r0 + u * rstep < n) sum += fast_exp2(x[u] - mx);
+  }
+  for (int d = G; d < kWave; d <<= 1) sum += __shfl_xor(sum, d, kWave);
+  if (lane < G && lse_out) lse_out[(size_t)b * Hq + head0 + lane] = (mx + __builtin_amdgcn_logf(sum)) * kLn2;
+
+  // 2. the weighted sum over the rows, kRows rows of kNf float4 per round
+  constexpr int kRows = 16 / kNf;
+  const int per_row = 32 * G;                          // float4 of a group's row
+  const bool fv = lane < per_row;                      // G = 1: 32 float4, lanes 32.. idle
+  const int hh = (lane % (2 * G)) >> 1;                // the head of every float4 this lane owns
+  const float hmx = __shfl(mx, hh, kWave);             // lane hh holds head hh's max and sum
+  const float hinv = 1.0f / __shfl(sum, hh, kWave);
+  const f32x4* po = (const f32x4*)plan.partial_o + ((size_t)c0 * Hq + head0) * 32 + lane;
+  const size_t row_stride = (size_t)Hq * 32;           // float4 per chunk row
+  f32x4 acc[kNf];
+#pragma unroll
+  for (int j = 0; j < kNf; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < n; r0 += kRows) {
+    float lw[kRows];
+    f32x4 o[kRows][kNf];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const size_t r = (size_t)(r0 + u < n ? r0 + u : n - 1);
+      lw[u] = lse[r * Hq + hh];
+#pragma unroll
+      for (int j = 0; j < kNf; ++j) o[u][j] = fv ? po[r * row_stride + 64 * j] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      if (r0 + u < n) {
+        const float w = fast_exp2(lw[u] - hmx) * hinv;
+#pragma unroll
+        for (int j = 0; j < kNf; ++j) acc[j] += w * o[u][j];
+      }
+    }
+  }
+  if (!fv) return;
+  const size_t orow = (size_t)b * Hq + head0 + hh;
+#pragma unroll
+  for (int j = 0; j < kNf; ++j) {
+    const int f = lane + 64 * j;
+    const int d = (f / (2 * G)) * 8 + (f & 1) * 4;
+    if (out_fp8) {
+      *(uint32_t*)((uint8_t*)out + orow * kHeadDim + d) =
+          f32x4_to_e4m3x4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    } else {
+      bf16x4 rr;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) rr[x] = (__bf16)acc[j][x];
+      *(bf16x4*)((uint16_t*)out + orow * kHeadDim + d) = rr;
+    }
+  }
+}
+
+// kNf for the group size G (a power of two <= 16).
+__device__ inline void fold_merge_group(const Geometry& geo, const PlanPtrs& plan, int b, int g,
+                                        int c0, int n, void* __restrict__ out,
+                                        float* __restrict__ lse_out, int out_fp8, int lane) {
+  switch (geo.group) {
+    case 16: fold_merge<8>(geo, plan, b, g, c0, n, out, lse_out, out_fp8, lane); break;
+    case 8: fold_merge<4>(geo, plan, b, g, c0, n, out, lse_out, out_fp8, lane); break;
+    case 4: fold_merge<2>(geo, plan, b, g, c0, n, out, lse_out, out_fp8, lane); break;
+    default: fold_merge<1>(geo, plan, b, g, c0, n, out, lse_out, out_fp8, lane); break;
+  }
+}
+
 // One worker of the schedule (this workgroup): all chunks of `worker`, every
 // KV head (one wave per head, looping if Hkv > 8).
-template <bool kFp8, bool kQk8, bool kSync>
+template <bool kFp8, bool kQk8, bool kSync, bool kFold>
 __device__ __forceinline__ void split_worker(
     int worker, const Geometry& geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table,
     const PlanPtrs& plan, void* __restrict__ out, float* __restrict__ lse_out,
-    float score_scale_log2, float out_scale, int out_fp8, float inv_q_scale) {
+    float score_scale_log2, float out_scale, int out_fp8, float inv_q_scale, int fold_status) {
   constexpr int kElemBytes = kFp8 ? 1 : 2;
   const int c_begin = wave_uniform(plan.worker_chunk[worker]);
   const int c_end = wave_uniform(plan.worker_chunk[worker + 1]);
@@ -302,6 +411,32 @@ __device__ __forceinline__ void split_worker(
           if (kc == 0) plan.partial_lse[(size_t)c * HqT + (size_t)g * GT + gc] = lse2;
         }
       }
+      if constexpr (kFold) {
+        // One new token per sequence: vg is the KV head.  A split sequence's
+        // (b, g) is finished by the wave that stores its last partial: each
+        // wave publishes its partial (device-scope fence), then counts it;
+        // the one that brings the count to the chunk total takes the others'
+        // partials (fence) and merges.  No wave waits for another.
+        const int n = wave_uniform(plan.seq_chunk[b + 1] - plan.seq_chunk[b]);
+        bool finisher = single;
+        if (!single) {
+          __threadfence();
+          int old = 0;
+          if (lane == 0) old = atomicAdd(&plan.arrivals[(size_t)b * geo.num_kv_heads + g], 1);
+          old = __shfl(old, 0, kWave);
+          if (old == n - 1) {
+            __threadfence();
+            fold_merge_group(geo, plan, b, g, wave_uniform(plan.seq_chunk[b]), n, out, lse_out,
+                             out_fp8, lane);
+            finisher = true;
+          }
+        }
+        // the prologue's status of this token, folded once per sequence (decode step only)
+        if (fold_status && finisher && g == 0 && lane == 0) {
+          const int32_t st = plan.token_status[b];
+          if (st) atomicOr(plan.error_word, st);
+        }
+      }
     }
   }
 }
@@ -309,17 +444,18 @@ __device__ __forceinline__ void split_worker(
 // The kernel: one workgroup per worker.  With a trace buffer it records, per
 // worker, [start, end] of the 100 MHz constant clock and the hardware ids of
 // the compute unit it ran on (HW_ID, XCC_ID), for load-balance analysis.
-template <bool kFp8, bool kQk8, bool kSync>
+template <bool kFp8, bool kQk8, bool kSync, bool kFold>
 __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
     Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table, PlanPtrs plan,
     void* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
-    float out_scale, int out_fp8, float inv_q_scale, int64_t* __restrict__ trace) {
+    float out_scale, int out_fp8, float inv_q_scale, int fold_status, int64_t* __restrict__ trace) {
   int64_t t_start = 0;
   if (trace != nullptr && threadIdx.x == 0) t_start = (int64_t)wall_clock64();
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  split_worker<kFp8, kQk8, kSync>(worker, geo, q_out, k_pool, v_pool, block_table, plan, out,
-                                  lse_out, score_scale_log2, out_scale, out_fp8, inv_q_scale);
+  split_worker<kFp8, kQk8, kSync, kFold>(worker, geo, q_out, k_pool, v_pool, block_table, plan, out,
+                                  lse_out, score_scale_log2, out_scale, out_fp8, inv_q_scale,
+                                  fold_status);
   if (trace != nullptr) {
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -501,7 +637,8 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
 }
 
 hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, bool qk_fp8,
-                                  int num_workers, const void* q_out, const void* k_cache,
+                                  bool fold, bool fold_status, int num_workers, const void* q_out,
+                                  const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
                                   const PlanPtrs& plan, void* out, float* lse_out,
                                   float score_scale_log2, float out_scale, float inv_q_scale,
@@ -515,18 +652,23 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, b
     kernel<<<num_workers, waves * kWave, 0, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
         block_table, plan, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0,
-        inv_q_scale, trace);
+        inv_q_scale, fold_status ? 1 : 0, trace);
   };
-  if (fp8 && qk_fp8) {
-    if (sync) launch(split_attention_kernel<true, true, true>);
-    else launch(split_attention_kernel<true, true, false>);
-  } else if (fp8) {
-    if (sync) launch(split_attention_kernel<true, false, true>);
-    else launch(split_attention_kernel<true, false, false>);
-  } else {
-    if (sync) launch(split_attention_kernel<false, false, true>);
-    else launch(split_attention_kernel<false, false, false>);
-  }
+  auto pick = [&](auto fold_c) {
+    constexpr bool F = decltype(fold_c)::value;
+    if (fp8 && qk_fp8) {
+      if (sync) launch(split_attention_kernel<true, true, true, F>);
+      else launch(split_attention_kernel<true, true, false, F>);
+    } else if (fp8) {
+      if (sync) launch(split_attention_kernel<true, false, true, F>);
+      else launch(split_attention_kernel<true, false, false, F>);
+    } else {
+      if (sync) launch(split_attention_kernel<false, false, true, F>);
+      else launch(split_attention_kernel<false, false, false, F>);
+    }
+  };
+  if (fold) pick(std::true_type{});
+  else pick(std::false_type{});
   return hipGetLastError();
 }
 

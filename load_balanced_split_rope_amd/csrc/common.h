@@ -59,6 +59,8 @@ struct SchedParams {
   int32_t splits;        // S (static)
   int32_t weighted;      // dynamic: 1 if xcd_weight is used
   int32_t xcd_weight[kXcds];
+  int32_t fold_groups;   // KV heads when the merge is folded into the split launch
+                         // (the plan clears batch x fold_groups arrival counters), else 0
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -81,6 +83,7 @@ struct PlanPtrs {
   int32_t* token_status;  // [B] the fused prologue's per-token error bits
   float* partial_o;       // [C_max][Hq][128]
   float* partial_lse;     // [C_max][Hq], log2 domain
+  int32_t* arrivals;      // [B][Hkv] chunks done, for the folded merge
 };
 
 // Geometry every kernel needs, passed by value.

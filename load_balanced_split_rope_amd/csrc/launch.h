@@ -21,8 +21,12 @@ hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_blocks, const
 
 // qk_fp8 (with an FP8 cache): q quantised with inv_q_scale, scores on FP8
 // matrix cores; score_scale_log2 then includes q_scale.
+// fold: merge split sequences inside this launch (one new token per
+// sequence); fold_status: also fold the prologue's per-token status words
+// into the error word (decode step).
 hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, bool qk_fp8,
-                                  int num_workers, const void* q_out, const void* k_cache,
+                                  bool fold, bool fold_status, int num_workers, const void* q_out,
+                                  const void* k_cache,
                                   const void* v_cache, const int32_t* block_table,
                                   const PlanPtrs& plan, void* out, float* lse_out,
                                   float score_scale_log2, float out_scale, float inv_q_scale,

@@ -172,6 +172,8 @@ __device__ inline void plan_body(const int32_t* __restrict__ seq_lens, int batch
     plan.worker_chunk[W] = carry;
     plan.seq_chunk[batch] = carry;
   }
+  // the folded merge's arrival counters start from zero every step
+  for (int i = tid; i < batch * sp.fold_groups; i += kPlanThreads) plan.arrivals[i] = 0;
 }
 
 

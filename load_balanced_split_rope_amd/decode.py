@@ -79,11 +79,14 @@ class Schedule:
 
     xcd_weights: None (equal shares) or 8 integer weights in [1, 65536], the
     relative streaming rate of each XCD's compute units (dynamic only).
+    fold_merge: merge split sequences inside the split-attention launch
+    (LBSR_SCHED_FOLD_MERGE; one new token per sequence) instead of a second launch.
     """
     kind: str = "dynamic"
     num_workers: int = 0
     static_splits: int = 0
     xcd_weights: tuple = None
+    fold_merge: bool = False
 
     def cfg(self):
         if self.kind not in ("dynamic", "static"):
@@ -92,7 +95,8 @@ class Schedule:
         if len(wts) != B.NUM_XCDS:
             raise ValueError(f"xcd_weights needs {B.NUM_XCDS} entries, got {len(wts)}")
         return B.SchedCfg(B.SCHED_DYNAMIC if self.kind == "dynamic" else B.SCHED_STATIC,
-                          self.num_workers, self.static_splits, 0,
+                          self.num_workers, self.static_splits,
+                          B.SCHED_FOLD_MERGE if self.fold_merge else 0,
                           (ctypes.c_int32 * B.NUM_XCDS)(*wts))
 
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lbsr_abi_version() == 4
+    assert lib.lbsr_abi_version() == 5
     for st in range(5):
         assert lib.lbsr_status_string(st).startswith(b"LBSR_")
     assert lib.lbsr_status_string(99) == b"unknown lbsr_status"
@@ -50,8 +50,10 @@ def test_workspace_layout_dynamic_and_static():
     lay = workspace_layout(cfg_mix(), 32, Schedule("dynamic", num_workers=256))
     assert lay.num_workers == 256 and lay.max_chunks == 256 + 31
     offs = [lay.error_word, lay.cu_tiles, lay.worker_chunk, lay.chunks, lay.seq_chunk,
-            lay.seq_len_eff, lay.token_status, lay.partial_o, lay.partial_lse, lay.total]
+            lay.seq_len_eff, lay.token_status, lay.partial_o, lay.partial_lse, lay.arrivals,
+            lay.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.total - lay.arrivals >= 4 * 32 * 8
     assert lay.partial_lse - lay.partial_o >= 4 * 287 * 64 * 128
     st = workspace_layout(cfg_mix(), 32, Schedule("static", num_workers=256))
     assert st.static_splits == 8 and st.num_workers == 256 and st.max_chunks == 256
@@ -84,7 +86,7 @@ def test_batch_and_schedule_validation(lib):
         (20000, B.SchedCfg(0, 256, 0, 0), B.E_UNSUPPORTED),
         (32, B.SchedCfg(5, 256, 0, 0), B.E_INVALID),
         (32, B.SchedCfg(0, -1, 0, 0), B.E_INVALID),
-        (32, B.SchedCfg(0, 256, 0, 1), B.E_INVALID),
+        (32, B.SchedCfg(0, 256, 0, 2), B.E_INVALID),          # unknown flag bit
     ]:
         assert lib.lbsr_workspace_layout(ctypes.byref(s), batch, ctypes.byref(cfg),
                                          ctypes.byref(out)) == status
@@ -329,3 +331,21 @@ def test_uniform_prefill_workspace_validation(lib):
     for ws, nb in ((fake, n.value), (nul, 0)):                        # valid: fails later (no GPU)
         call(ws, nb)
         assert b"workspace" not in lib.lbsr_last_error()
+
+
+@pytest.mark.parametrize("Hq,Hkv,tokens,status", [
+    (64, 8, 1, B.OK),                 # the pages' shape, one new token
+    (8, 1, 1, B.OK),
+    (64, 4, 1, B.OK),                 # group 16
+    (64, 8, 2, B.E_UNSUPPORTED),      # multi-token steps keep the merge launch
+    (48, 8, 1, B.E_UNSUPPORTED),      # group 6: not a power of two
+])
+def test_fold_merge_validation(lib, Hq, Hkv, tokens, status):
+    """LBSR_SCHED_FOLD_MERGE: one new token per sequence and a power-of-two group."""
+    cfg = DecodeConfig(Hq, Hkv, "bf16", max_blocks_per_seq=64, num_pages=100, tokens_per_seq=tokens)
+    s = cfg.shape()
+    c = Schedule("dynamic", num_workers=256, fold_merge=True).cfg()
+    assert c.flags == B.SCHED_FOLD_MERGE
+    out = B.WsLayout()
+    got = lib.lbsr_workspace_layout(ctypes.byref(s), 16, ctypes.byref(c), ctypes.byref(out))
+    assert got == status, lib.lbsr_last_error()
