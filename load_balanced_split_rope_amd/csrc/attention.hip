@@ -420,10 +420,31 @@ __device__ __forceinline__ void split_worker(
         const int n = wave_uniform(plan.seq_chunk[b + 1] - plan.seq_chunk[b]);
         bool finisher = single;
         if (!single) {
-          __threadfence();
-          int old = 0;
-          if (lane == 0) old = atomicAdd(&plan.arrivals[(size_t)b * geo.num_kv_heads + g], 1);
-          old = __shfl(old, 0, kWave);
+          int old;
+          if constexpr (kSync) {
+            // Lockstep: every wave of the workgroup finishes this chunk here.
+            // Each waits for its own partial stores, then one thread
+            // publishes them all (one device-scope fence per chunk, not per
+            // wave) and counts the chunk for the sequence.  With more KV
+            // heads than waves the waves make several passes over the chunks
+            // (heads p * waves + 0 .. waves - 1 in pass p); each pass has its
+            // own counter, at the pass's first head: thread 0's vg.
+            __shared__ int s_old;
+            __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this wave's stores done
+            __syncthreads();
+            if (threadIdx.x == 0) {
+              __threadfence();
+              s_old = atomicAdd(&plan.arrivals[(size_t)b * geo.num_kv_heads + vg], 1);
+            }
+            __syncthreads();
+            old = s_old;
+            __syncthreads();                             // s_old is rewritten next chunk
+          } else {
+            __threadfence();
+            old = 0;
+            if (lane == 0) old = atomicAdd(&plan.arrivals[(size_t)b * geo.num_kv_heads + g], 1);
+            old = __shfl(old, 0, kWave);
+          }
           if (old == n - 1) {
             __threadfence();
             fold_merge_group(geo, plan, b, g, wave_uniform(plan.seq_chunk[b]), n, out, lse_out,

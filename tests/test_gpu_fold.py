@@ -31,6 +31,16 @@ def test_small_steps_folded(case, si):
     check_step(w, folded(SCHEDS[si]), "folded merge")
 
 
+@pytest.mark.parametrize("P", [3, 40, 256])
+def test_more_kv_heads_than_waves_folded(P):
+    """16 KV heads on 8 waves: two lockstep passes over each chunk, each with
+    its own arrival counter."""
+    w = wl.custom([3000, 70, 900, 129], num_q_heads=32, num_kv_heads=16, seed=25)
+    check_step(w, lb.Schedule("dynamic", num_workers=P, fold_merge=True), "16 KV heads folded")
+    w8 = wl.custom([2000, 65], num_q_heads=32, num_kv_heads=16, kv_dtype="fp8", seed=26)
+    check_step(w8, lb.Schedule("static", num_workers=P, fold_merge=True), "16 KV heads static")
+
+
 def test_random_small_batches_folded():
     rng = np.random.default_rng(77)
     for i in range(12):
