@@ -290,11 +290,16 @@ lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq
  * they hold.  Deterministic.
  * The merge is a second launch by default.  With cfg->flags =
  * LBSR_SCHED_FOLD_MERGE ([A] "Why does dynamic scheduling matter in
- * attention?" chains its kernels to cut launch gaps) there is one launch: the
- * wave that finishes the last chunk of a (sequence, KV head) -- counted with
- * a device-scope atomic after a device-scope fence -- merges its rows in
- * chunk order.  Which wave that is varies, the arithmetic does not: results
- * are deterministic either way (but not bit-identical between the two forms).
+ * attention?" chains its kernels to cut launch gaps) there is one launch:
+ * every finished chunk is published with a device-scope fence and counted
+ * with a device-scope atomic, and the workgroup (or, when the KV heads do not
+ * divide evenly over its waves, the wave) that completes a sequence's count
+ * merges its rows in chunk order.  Which one that is varies, the arithmetic
+ * does not: results are deterministic either way (but not bit-identical
+ * between the two forms).  One new token per sequence; the workspace's
+ * arrival counters are cleared by lbsr_plan / the step's plan.  On MI355X a
+ * device-scope release writes back an L2, so this form is slower than two
+ * launches except for small, launch-bound batches.
  */
 lbsr_status lbsr_attention(const lbsr_shape *shape, const lbsr_params *params, int32_t batch,
                            const void *q_out, const void *k_cache, const void *v_cache,
