@@ -137,3 +137,28 @@ def test_standalone_attention_folded():
     torch.cuda.synchronize()
     assert torch.equal(out, res["out"]) and torch.equal(lse, res["lse"])
     assert lb.read_error(cfg, w.batch, sched, ws) == 0
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,kv_dtype", [
+    ([65, 1000, 4097, 3], 64, 8, "bf16"),
+    ([2000, 70, 129], 16, 2, "fp8"),
+])
+@pytest.mark.parametrize("workers", [5, 256])
+def test_folded_fp8_output(lens, Hq, Hkv, kv_dtype, workers):
+    """The folded merge writes E4M3 codes of o / out_scale like the merge kernel:
+    within the tolerance plus half an E4M3 step of the oracle."""
+    from checks import check_output_fp8
+    from test_gpu_out_fp8 import fp8_cfg
+    from test_gpu_step import oracle_step
+    dev = device()
+    w = wl.custom(lens, num_q_heads=Hq, num_kv_heads=Hkv, kv_dtype=kv_dtype, seed=27)
+    inp = wl.make_inputs(w)
+    poison_cache(inp, w)
+    out_scale = 2.0 ** -6 * 1.37
+    g = to_device(inp, dev)
+    res = run_step(w, g, lb.Schedule("dynamic", num_workers=workers, fold_merge=True),
+                   cfg=fp8_cfg(w, g, out_scale))
+    assert res["error"] == 0
+    _, ro, rl = oracle_step(w, inp)
+    check_output_fp8(res["out"].cpu().numpy(), ro, w.kv_dtype, out_scale)
+    assert np.all(np.abs(to_f64(res["lse"]) - rl) <= 1e-4 + 1e-5 * np.abs(rl))
