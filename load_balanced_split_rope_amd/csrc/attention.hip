@@ -289,8 +289,8 @@ __device__ __forceinline__ void split_worker(
     const PlanPtrs& plan, void* __restrict__ out, float* __restrict__ lse_out,
     float score_scale_log2, float out_scale, int out_fp8, float inv_q_scale, int fold_status) {
   constexpr int kElemBytes = kFp8 ? 1 : 2;
-  const int c_begin = wave_uniform(plan.worker_chunk[worker]);
-  const int c_end = wave_uniform(plan.worker_chunk[worker + 1]);
+  const int c_begin = read_invariant(plan.worker_chunk + worker);
+  const int c_end = read_invariant(plan.worker_chunk + worker + 1);
   if (c_begin >= c_end) return;
 
   const int lane = threadIdx.x & 63;
@@ -312,12 +312,18 @@ __device__ __forceinline__ void split_worker(
     const int lag = T - 1 - tok;                // it attends rows < L - lag
     for (int c = c_begin; c < c_end; ++c) {
       const int32_t* ch = plan.chunks + 4 * (size_t)c;
-      const int b = wave_uniform(ch[0]);
-      const int t0 = wave_uniform(ch[1]);
-      const int t1 = wave_uniform(ch[2]);
-      const int L = wave_uniform(plan.seq_len_eff[b]);
-      const bool single = wave_uniform(plan.seq_chunk[b + 1] - plan.seq_chunk[b]) == 1;
+      const int b = read_invariant(ch);
+      const int t0 = read_invariant(ch + 1);
+      const int t1 = read_invariant(ch + 2);
+      // the first page's read goes out beside the sequence's length and chunk
+      // count, one round trip after the chunk record
       const int32_t* bt_row = block_table + (size_t)b * geo.max_blocks;
+      bool bad_page = false;
+      int page = fetch_page(bt_row, t0, geo.num_pages, bad_page);
+      const int L = read_invariant(plan.seq_len_eff + b);
+      const int c_first = read_invariant(plan.seq_chunk + b);   // the sequence's chunks
+      const int nchunks = read_invariant(plan.seq_chunk + b + 1) - c_first;
+      const bool single = nchunks == 1;
 
       // Q^T operand: column col = q head g*G + hl of new token tok (zero past
       // the G*Tq columns in use), channels 32*s + 8*kc .. +8 for step s.
@@ -343,8 +349,6 @@ __device__ __forceinline__ void split_worker(
         return (const u32x4*)(pool + ((size_t)page * geo.page_stride + head_off) * kElemBytes);
       };
 
-      bool bad_page = false;
-      int page = fetch_page(bt_row, t0, geo.num_pages, bad_page);
       TileRegs<kFp8> R;
       load_frags<kFp8>(R.k, tile_ptr(k_pool, page), lane);
       load_frags<kFp8>(R.v, tile_ptr(v_pool, page), lane);
@@ -417,7 +421,6 @@ __device__ __forceinline__ void split_worker(
         // wave publishes its partial (device-scope fence), then counts it;
         // the one that brings the count to the chunk total takes the others'
         // partials (fence) and merges.  No wave waits for another.
-        const int n = wave_uniform(plan.seq_chunk[b + 1] - plan.seq_chunk[b]);
         bool finisher = single;
         if (!single) {
           int old;
@@ -445,10 +448,9 @@ __device__ __forceinline__ void split_worker(
             if (lane == 0) old = atomicAdd(&plan.arrivals[(size_t)b * geo.num_kv_heads + g], 1);
             old = __shfl(old, 0, kWave);
           }
-          if (old == n - 1) {
+          if (old == nchunks - 1) {
             __threadfence();
-            fold_merge_group(geo, plan, b, g, wave_uniform(plan.seq_chunk[b]), n, out, lse_out,
-                             out_fp8, lane);
+            fold_merge_group(geo, plan, b, g, c_first, nchunks, out, lse_out, out_fp8, lane);
             finisher = true;
           }
         }

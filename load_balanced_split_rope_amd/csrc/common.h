@@ -128,6 +128,15 @@ __device__ __forceinline__ T wave_uniform(T x) {
   return __builtin_amdgcn_readfirstlane(x);
 }
 
+// A wave-uniform read of memory that no kernel writes while the reading kernel
+// runs (a plan written by an earlier launch): through the constant address
+// space the compiler issues it as a scalar load, counted apart from the vector
+// loads, so waiting for it does not also wait for vector loads issued earlier.
+template <typename T>
+__device__ __forceinline__ T read_invariant(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
