@@ -39,6 +39,15 @@
 
 namespace lbsr {
 
+// maximum with lane l ^ kXor (16 or 32), by the gfx950 lane-swap instructions
+template <int kXor>
+__device__ __forceinline__ float lane_maximum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = kXor == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                            : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // The online softmax of one tile as softmax_tile computes it, with the score
 // scale applied inside the exponent: the column max is taken over the raw
 // scores and scaled once (c > 0, so fl(max s * c) = max fl(s * c): the same
@@ -60,10 +69,13 @@ __device__ __forceinline__ void softmax_tile_fma(const f32x4 (&S)[4], SoftmaxSta
       for (int e = 0; e < 4; ++e)
         if (16 * tb + 4 * kc + e >= lim) x[4 * tb + e] = -__builtin_inff();
   }
+  // IEEE maximum (NaN-propagating): a chain of v_maximum3_f32, without the
+  // operand quieting that fmaxf needs; equal to fmaxf on the finite and -inf
+  // scores, and a NaN score reaches the output through P either way
   float mx = x[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-  mx = max_xor32(max_xor16(mx)) * c;
+  for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
+  mx = lane_maximum<32>(lane_maximum<16>(mx)) * c;
   if (__any(mx > st.m + 8.f)) {                          // wave-uniform
     const float m_new = fmaxf(st.m, mx);
     const float alpha = fast_exp2(st.m - (m_new == -__builtin_inff() ? 0.f : m_new));
