@@ -557,7 +557,7 @@ def main():
             r4 = measure(w4, dev, P, args.steps, args.warmup, False, weighted)
             result["mtp4"] = {
                 "workload": WORKLOAD_TEXT["mix_mtp4"] + " (32 (token, head) columns per KV head: "
-                            "two 16-column blocks on neighbouring waves)",
+                            "both 16-column blocks on the head's wave, one accumulator parked in LDS)",
                 "us_per_step": round(r4["ms"] * 1e3, 2),
                 "kernel_us": {k: round(float(v) * 1e3, 2) for k, v in zip(names, r4["kernel_ms"])},
                 "step_time_vs_one_token": round(r4["ms"] / ms, 4),

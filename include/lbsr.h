@@ -124,9 +124,10 @@ typedef enum { LBSR_QK_BF16 = 0, LBSR_QK_FP8_E4M3 = 1 } lbsr_qk_dtype;
  * positions [batch][Tq], lse_out [batch][Tq][Hq] -- and seq_lens[b] counts all
  * Tq of them.  New token j of sequence b sits at position L_b - Tq + j and
  * attends rows [0, L_b - Tq + j]: the cached prefix and new tokens 0..j.
- * The Tq * G queries of one KV head share each KV read: up to 16 of them in
- * one wave; more (up to 64) run as blocks of 16 on neighbouring waves that
- * read the same tiles together.  The merge stages (chunks of a sequence) x
+ * The Tq * G queries of one KV head share each KV read: up to 32 of them in
+ * one wave (two blocks of 16, one block's accumulator parked in LDS, 16 KiB of
+ * LDS per wave); more (up to 64) run as blocks of 16 on neighbouring waves
+ * that read the same tiles together.  The merge stages (chunks of a sequence) x
  * (G * Tq) weights in 64 KiB of LDS: a larger product (e.g. 1024 workers
  * with G * Tq = 32) is LBSR_E_UNSUPPORTED.  Tq = 1 is the ordinary step and
  * the layouts reduce to the ones written below.

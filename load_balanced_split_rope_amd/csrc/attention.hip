@@ -58,6 +58,91 @@ __device__ __forceinline__ void load_frags(u32x4 (&dst)[TileRegs<kFp8>::kFrags],
     dst[f] = __builtin_nontemporal_load(tile + f * kWave + lane);
 }
 
+// The pieces of one tile step.  Scores S^T[token][col] (lane holds tokens
+// 16*tb + 4*kc + e of its column) from the K fragments and q's operand.
+template <bool kFp8, bool kQk8>
+__device__ __forceinline__ void tile_scores(const TileRegs<kFp8>& R, const bf16x8 (&qB)[4],
+                                            const i32x8& qF, f32x4 (&S)[4]) {
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kQk8) {
+      acc = mfma_fp8(k_fp8_operand(R.k[2 * tb], R.k[2 * tb + 1]), qF, acc);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 a;
+        if constexpr (kFp8) {
+          const u32x4 w = R.k[2 * tb + (s >> 1)];
+          a = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+        } else {
+          a = as_bf16x8(R.k[4 * tb + s]);
+        }
+        acc = mfma_bf16(a, qB[s], acc);
+      }
+    }
+    S[tb] = acc;
+  }
+}
+
+// Rows past the sequence end hold anything (even NaN): zero their V.
+template <bool kFp8>
+__device__ __forceinline__ void zero_v_tail(TileRegs<kFp8>& R, int rem, int kc) {
+  constexpr int NF = TileRegs<kFp8>::kFrags;
+  uint32_t keep[2][4];
+  v_keep_masks<kFp8>(rem, kc, keep);
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) R.v[f][j] &= keep[0][j];
+  } else {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R.v[2 * db + s][j] &= keep[s][j];
+  }
+}
+
+// O^T[channel][col] += V^T . P^T
+template <bool kFp8>
+__device__ __forceinline__ void tile_pv(const TileRegs<kFp8>& R, const bf16x8 (&pB)[2],
+                                        f32x4 (&O)[8]) {
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 a;
+      if constexpr (kFp8) {
+        const u32x4 w = R.v[db];
+        a = s ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+      } else {
+        a = as_bf16x8(R.v[2 * db + s]);
+      }
+      O[db] = mfma_bf16(a, pB[s], O[db]);
+    }
+  }
+}
+
+// After a tile's last P.V: request the next tile into the same registers, and
+// in lockstep meet the other waves (no memory wait: the loads stay in flight).
+template <bool kFp8, bool kSync>
+__device__ __forceinline__ void prefetch_tile(TileRegs<kFp8>& R, const u32x4* next_k,
+                                              const u32x4* next_v, int lane) {
+  // keep the scheduler from hoisting the next loads above the MFMAs that
+  // still read these registers (that would need a second register set)
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<kFp8>(R.k, next_k, lane);
+  load_frags<kFp8>(R.v, next_v, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kSync) {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One 64-token tile: scores, online softmax update, P.V.  `rem` = rows of the
 // tile before the sequence end (1..64); the lane's column attends rows below
 // rem - lag (lag = Tq - 1 - new-token index), and `tail` = Tq - 1 is the
@@ -85,80 +170,77 @@ __device__ __forceinline__ void attend_tile(TileRegs<kFp8>& R, SoftmaxState& st,
                                             int lag, int tail, int kc, int lane,
                                             float score_scale_log2, const u32x4* next_k,
                                             const u32x4* next_v) {
-  constexpr int NF = TileRegs<kFp8>::kFrags;
-  // ---- scores: S^T[token][col], lane holds tokens 16*tb + 4*kc + e ----
   f32x4 S[4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (kQk8) {
-      acc = mfma_fp8(k_fp8_operand(R.k[2 * tb], R.k[2 * tb + 1]), qF, acc);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 a;
-        if constexpr (kFp8) {
-          const u32x4 w = R.k[2 * tb + (s >> 1)];
-          a = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
-        } else {
-          a = as_bf16x8(R.k[4 * tb + s]);
-        }
-        acc = mfma_bf16(a, qB[s], acc);
-      }
-    }
-    S[tb] = acc;
-  }
-
-  // ---- online softmax (log2 domain); some column's last row may fall in this tile ----
+  tile_scores<kFp8, kQk8>(R, qB, qF, S);
+  // online softmax (log2 domain); some column's last row may fall in this tile
   bf16x8 pB[2];
   softmax_tile(S, st, rem - tail < kPage, rem - lag, kc, score_scale_log2, pB);
+  if (rem < kPage) zero_v_tail<kFp8>(R, rem, kc);
+  tile_pv<kFp8>(R, pB, st.O);
+  if constexpr (kPrefetch) prefetch_tile<kFp8, kSync>(R, next_k, next_v, lane);
+}
 
-  // ---- rows past the sequence end hold anything (even NaN): zero their V ----
-  if (rem < kPage) {
-    uint32_t keep[2][4];
-    v_keep_masks<kFp8>(rem, kc, keep);
-    if constexpr (kFp8) {
+// Two 16-column blocks of one KV head on one wave (G*Tq in 17..32): both
+// read the tile's K and V registers, so a CU streams all 8 heads' tiles at
+// once instead of 4 heads on two waves each.  Only one block's accumulator
+// fits beside the tile in registers; the other block's O waits in the wave's
+// LDS slot `o_lds` ([8][64] f32x4), its m and running sum in `other`.  The
+// blocks alternate: the tile starts with the block in registers (`cur`), the
+// two swap after its P.V, and the second block's accumulator stays in
+// registers for the next tile.  q of both blocks is read from `q_lds`
+// ([2][4][64] u32x4: block, step, lane; for FP8 scores [2][2][64], q's codes).
+struct PairOther {
+  float m, lsum;
+};
+
+template <bool kFp8, bool kQk8, bool kPrefetch, bool kSync>
+__device__ __forceinline__ void attend_tile_pair(TileRegs<kFp8>& R, SoftmaxState& st,
+                                                 PairOther& other, int& cur,
+                                                 const u32x4* q_lds, f32x4* o_lds, int rem,
+                                                 const int (&lag)[2], int tail, int kc, int lane,
+                                                 float score_scale_log2, const u32x4* next_k,
+                                                 const u32x4* next_v) {
+  if (rem < kPage) zero_v_tail<kFp8>(R, rem, kc);
+  const bool mask = rem - tail < kPage;
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
+  for (int half = 0; half < 2; ++half) {
+    const int j = half ? 1 - cur : cur;
+    if (half == 1) {
+      // swap the accumulators a quarter at a time: read the parked block's,
+      // then park this one's at the same addresses (in order within the wave)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) R.v[f][j] &= keep[0][j];
+      for (int qt = 0; qt < 4; ++qt) {
+        const f32x4 a = o_lds[(2 * qt) * kWave + lane];
+        const f32x4 b = o_lds[(2 * qt + 1) * kWave + lane];
+        o_lds[(2 * qt) * kWave + lane] = st.O[2 * qt];
+        o_lds[(2 * qt + 1) * kWave + lane] = st.O[2 * qt + 1];
+        st.O[2 * qt] = a;
+        st.O[2 * qt + 1] = b;
+      }
+      const float m = st.m, l = st.lsum;
+      st.m = other.m;
+      st.lsum = other.lsum;
+      other.m = m;
+      other.lsum = l;
+    }
+    bf16x8 qB[4];
+    i32x8 qF = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (kQk8) {
+      const u32x4 lo = q_lds[(2 * j) * kWave + lane], hi = q_lds[(2 * j + 1) * kWave + lane];
+      qF = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     } else {
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) R.v[2 * db + s][j] &= keep[s][j];
+      for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(q_lds[(4 * j + s) * kWave + lane]);
     }
+    f32x4 S[4];
+    tile_scores<kFp8, kQk8>(R, qB, qF, S);
+    bf16x8 pB[2];
+    softmax_tile(S, st, mask, rem - (j ? lag[1] : lag[0]), kc, score_scale_log2, pB);
+    tile_pv<kFp8>(R, pB, st.O);
   }
-
-  // ---- O^T[channel][col] += V^T . P^T ----
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 a;
-      if constexpr (kFp8) {
-        const u32x4 w = R.v[db];
-        a = s ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
-      } else {
-        a = as_bf16x8(R.v[2 * db + s]);
-      }
-      st.O[db] = mfma_bf16(a, pB[s], st.O[db]);
-    }
-  }
-  if constexpr (kPrefetch) {
-    // keep the scheduler from hoisting the next loads above the MFMAs that
-    // still read these registers (that would need a second register set)
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags<kFp8>(R.k, next_k, lane);
-    load_frags<kFp8>(R.v, next_v, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kSync) {
-      __builtin_amdgcn_s_barrier();   // no memory wait: the loads stay in flight
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+  cur = 1 - cur;
+  if constexpr (kPrefetch) prefetch_tile<kFp8, kSync>(R, next_k, next_v, lane);
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD
@@ -280,6 +362,60 @@ __device__ inline void fold_merge_group(const Geometry& geo, const PlanPtrs& pla
   }
 }
 
+// A chunk's result for one lane's column (gc < G*Tq; other lanes only take
+// part in the sums): the output row itself for a one-chunk sequence (BF16, or
+// E4M3 codes of o / out_scale), else a partial row and its log2-sum-exp for
+// the merge.
+__device__ __forceinline__ void store_chunk_column(const Geometry& geo, const PlanPtrs& plan,
+                                                   const f32x4 (&O)[8], float m, float lsum,
+                                                   int b, int c, int g, int gc, int tok, int hl,
+                                                   bool single, void* __restrict__ out,
+                                                   float* __restrict__ lse_out, float out_scale,
+                                                   int out_fp8, int kc) {
+  const int Hq = geo.num_q_heads, G = geo.group, T = geo.tokens, GT = G * T;
+  // l = 0: no row of this chunk is visible to the column (an early new
+  // token whose limit lies before the chunk): an empty partial, o = 0 and
+  // lse = -inf, which the merge weighs 0.  A sequence's first chunk
+  // holds row 0, so a single-chunk sequence never gets here with l = 0.
+  const float l = sum_xor32(sum_xor16(lsum));
+  const float scale = l > 0.f ? out_scale / l : 0.f;
+  const float lse2 = l > 0.f ? m + __builtin_amdgcn_logf(l) : -__builtin_inff();  // log2
+  if (gc < GT) {
+    const size_t orow = ((size_t)b * T + tok) * Hq + (size_t)g * G + hl;  // out / lse_out row
+    if (single && out_fp8) {
+      // E4M3 codes of o / out_scale (folded into scale): 4 bytes per db
+      uint8_t* o = (uint8_t*)out + orow * kHeadDim + 4 * kc;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f32x4 x = O[db] * scale;
+        *(uint32_t*)(o + 16 * db) = f32x4_to_e4m3x4(x[0], x[1], x[2], x[3]);
+      }
+      if (kc == 0 && lse_out) lse_out[orow] = lse2 * kLn2;
+    } else if (single) {
+      uint16_t* o = (uint16_t*)out + orow * kHeadDim + 4 * kc;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(O[db][e] * scale);
+        *(bf16x4*)(o + 16 * db) = v4;
+      }
+      if (kc == 0 && lse_out) lse_out[orow] = lse2 * kLn2;
+    } else {
+      // partial row layout of (chunk c, KV group g): [16 slices of 8
+      // channels][G*Tq columns][8 channels], so that any run of slices is
+      // contiguous for the merge; chunk c's rows are Hq*Tq long
+      const size_t HqT = (size_t)Hq * T;
+      float* po = plan.partial_o + ((size_t)c * HqT + (size_t)g * GT) * kHeadDim +
+                  gc * 8 + 4 * (kc & 1);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *(f32x4*)(po + (2 * db + (kc >> 1)) * 8 * GT) = O[db] * scale;
+      if (kc == 0) plan.partial_lse[(size_t)c * HqT + (size_t)g * GT + gc] = lse2;
+    }
+  }
+}
+
 // One worker of the schedule (this workgroup): all chunks of `worker`, every
 // KV head (one wave per head, looping if Hkv > 8).
 template <bool kFp8, bool kQk8, bool kSync, bool kFold>
@@ -369,52 +505,8 @@ __device__ __forceinline__ void split_worker(
       attend_tile<kFp8, kQk8, false, false>(R, st, qB, qF, L - (t1 - 1) * kPage, lag, T - 1, kc,
                                             lane, score_scale_log2, nullptr, nullptr);
       if (bad_page && lane == 0) atomicOr(plan.error_word, (int32_t)kErrPage);
-      const float m = st.m;
-      const float lsum = st.lsum;
-      const f32x4* O = st.O;
-
-      // ---- finish the chunk ----
-      // l = 0: no row of this chunk is visible to the column (an early new
-      // token whose limit lies before the chunk): an empty partial, o = 0 and
-      // lse = -inf, which the merge weighs 0.  A sequence's first chunk
-      // holds row 0, so a single-chunk sequence never gets here with l = 0.
-      const float l = sum_xor32(sum_xor16(lsum));
-      const float scale = l > 0.f ? out_scale / l : 0.f;
-      const float lse2 = l > 0.f ? m + __builtin_amdgcn_logf(l) : -__builtin_inff();  // log2
-      if (gc < GT) {
-        const size_t orow = ((size_t)b * T + tok) * Hq + (size_t)g * G + hl;  // out / lse_out row
-        if (single && out_fp8) {
-          // E4M3 codes of o / out_scale (folded into scale): 4 bytes per db
-          uint8_t* o = (uint8_t*)out + orow * kHeadDim + 4 * kc;
-#pragma unroll
-          for (int db = 0; db < 8; ++db) {
-            const f32x4 x = O[db] * scale;
-            *(uint32_t*)(o + 16 * db) = f32x4_to_e4m3x4(x[0], x[1], x[2], x[3]);
-          }
-          if (kc == 0 && lse_out) lse_out[orow] = lse2 * kLn2;
-        } else if (single) {
-          uint16_t* o = (uint16_t*)out + orow * kHeadDim + 4 * kc;
-#pragma unroll
-          for (int db = 0; db < 8; ++db) {
-            bf16x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(O[db][e] * scale);
-            *(bf16x4*)(o + 16 * db) = v4;
-          }
-          if (kc == 0 && lse_out) lse_out[orow] = lse2 * kLn2;
-        } else {
-          // partial row layout of (chunk c, KV group g): [16 slices of 8
-          // channels][G*Tq columns][8 channels], so that any run of slices is
-          // contiguous for the merge; chunk c's rows are Hq*Tq long
-          const size_t HqT = (size_t)Hq * T;
-          float* po = plan.partial_o + ((size_t)c * HqT + (size_t)g * GT) * kHeadDim +
-                      gc * 8 + 4 * (kc & 1);
-#pragma unroll
-          for (int db = 0; db < 8; ++db)
-            *(f32x4*)(po + (2 * db + (kc >> 1)) * 8 * GT) = O[db] * scale;
-          if (kc == 0) plan.partial_lse[(size_t)c * HqT + (size_t)g * GT + gc] = lse2;
-        }
-      }
+      store_chunk_column(geo, plan, st.O, st.m, st.lsum, b, c, g, gc, tok, hl, single, out,
+                         lse_out, out_scale, out_fp8, kc);
       if constexpr (kFold) {
         // One new token per sequence: vg is the KV head.  A split sequence's
         // (b, g) is finished by the wave that stores its last partial: each
@@ -467,6 +559,150 @@ __device__ __forceinline__ void split_worker(
 // The kernel: one workgroup per worker.  With a trace buffer it records, per
 // worker, [start, end] of the 100 MHz constant clock and the hardware ids of
 // the compute unit it ran on (HW_ID, XCC_ID), for load-balance analysis.
+// One worker with two 16-column blocks per KV head (G*Tq in 17..32), both on
+// the head's wave (attend_tile_pair): one wave per KV head, looping if
+// Hkv > 8.  Each wave owns a 16 KiB slice of the dynamic LDS: q of both
+// blocks (8 KiB), then the parked block's accumulator (8 KiB).
+constexpr int kPairSlotU32x4 = 16 * kWave;   // u32x4 per wave
+
+template <bool kFp8, bool kQk8, bool kSync>
+__device__ __forceinline__ void split_worker_pair(
+    int worker, const Geometry& geo, const uint16_t* __restrict__ q_out,
+    const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_table, const PlanPtrs& plan, void* __restrict__ out,
+    float* __restrict__ lse_out, float score_scale_log2, float out_scale, int out_fp8,
+    float inv_q_scale) {
+  constexpr int kElemBytes = kFp8 ? 1 : 2;
+  extern __shared__ u32x4 s_pair[];
+  const int c_begin = read_invariant(plan.worker_chunk + worker);
+  const int c_end = read_invariant(plan.worker_chunk + worker + 1);
+  if (c_begin >= c_end) return;
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int kc = lane >> 4;
+  const int nwaves = blockDim.x >> 6;
+  const int Hq = geo.num_q_heads, G = geo.group, T = geo.tokens;
+  const int GT = G * T;
+  u32x4* q_lds = s_pair + (size_t)wave * kPairSlotU32x4;
+  f32x4* o_lds = (f32x4*)(q_lds + 8 * kWave);
+  // this lane's column in each block: (new token, head in the group), lag
+  int gc[2], tok[2], hl[2], lag[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    gc[j] = 16 * j + col;
+    tok[j] = gc[j] < GT ? gc[j] / G : 0;
+    hl[j] = gc[j] - tok[j] * G;
+    lag[j] = T - 1 - tok[j];
+  }
+
+  for (int g = wave; g < geo.num_kv_heads; g += nwaves) {
+    for (int c = c_begin; c < c_end; ++c) {
+      const int32_t* ch = plan.chunks + 4 * (size_t)c;
+      const int b = read_invariant(ch);
+      const int t0 = read_invariant(ch + 1);
+      const int t1 = read_invariant(ch + 2);
+      const int32_t* bt_row = block_table + (size_t)b * geo.max_blocks;
+      bool bad_page = false;
+      int page = fetch_page(bt_row, t0, geo.num_pages, bad_page);
+      const int L = read_invariant(plan.seq_len_eff + b);
+      const int c_first = read_invariant(plan.seq_chunk + b);
+      const bool single = read_invariant(plan.seq_chunk + b + 1) - c_first == 1;
+
+      const size_t head_off = (size_t)g * geo.head_stride;
+      auto tile_ptr = [&](const uint8_t* pool, int pg) {
+        return (const u32x4*)(pool + ((size_t)pg * geo.page_stride + head_off) * kElemBytes);
+      };
+      TileRegs<kFp8> R;
+      load_frags<kFp8>(R.k, tile_ptr(k_pool, page), lane);
+      load_frags<kFp8>(R.v, tile_ptr(v_pool, page), lane);
+
+      // q of both blocks (zero past the G*Tq columns) into the wave's slot,
+      // as BF16 fragments or, for FP8 scores, as q's E4M3 codes
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 qB[4];
+        if (gc[j] < GT) {
+          const u32x4* qp = (const u32x4*)(q_out + (((size_t)b * T + tok[j]) * Hq +
+                                                     (size_t)g * G + hl[j]) * kHeadDim) + kc;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(qp[4 * s]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) qB[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+        }
+        if constexpr (kQk8) {
+          const i32x8 qF = q_fp8_operand(qB, inv_q_scale);
+          q_lds[(2 * j) * kWave + lane] = u32x4{(uint32_t)qF[0], (uint32_t)qF[1],
+                                                (uint32_t)qF[2], (uint32_t)qF[3]};
+          q_lds[(2 * j + 1) * kWave + lane] = u32x4{(uint32_t)qF[4], (uint32_t)qF[5],
+                                                    (uint32_t)qF[6], (uint32_t)qF[7]};
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) q_lds[(4 * j + s) * kWave + lane] = __builtin_bit_cast(u32x4, qB[s]);
+        }
+      }
+      // block 0 starts in registers, block 1 parked, both empty
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o_lds[db * kWave + lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+      SoftmaxState st;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.m = -__builtin_inff();
+      st.lsum = 0.f;
+      PairOther other{-__builtin_inff(), 0.f};
+      int cur = 0;
+
+      for (int t = t0; t < t1 - 1; ++t) {
+        const int next = fetch_page(bt_row, t + 1, geo.num_pages, bad_page);
+        attend_tile_pair<kFp8, kQk8, true, kSync>(R, st, other, cur, q_lds, o_lds, L - t * kPage,
+                                                  lag, T - 1, kc, lane, score_scale_log2,
+                                                  tile_ptr(k_pool, next), tile_ptr(v_pool, next));
+      }
+      attend_tile_pair<kFp8, kQk8, false, false>(R, st, other, cur, q_lds, o_lds,
+                                                 L - (t1 - 1) * kPage, lag, T - 1, kc, lane,
+                                                 score_scale_log2, nullptr, nullptr);
+      if (bad_page && lane == 0) atomicOr(plan.error_word, (int32_t)kErrPage);
+
+      // the block in registers, then the parked one
+      const int jr = cur, jp = 1 - cur;
+      store_chunk_column(geo, plan, st.O, st.m, st.lsum, b, c, g, jr ? gc[1] : gc[0],
+                         jr ? tok[1] : tok[0], jr ? hl[1] : hl[0], single, out, lse_out,
+                         out_scale, out_fp8, kc);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) st.O[db] = o_lds[db * kWave + lane];
+      store_chunk_column(geo, plan, st.O, other.m, other.lsum, b, c, g, jp ? gc[1] : gc[0],
+                         jp ? tok[1] : tok[0], jp ? hl[1] : hl[0], single, out, lse_out,
+                         out_scale, out_fp8, kc);
+    }
+  }
+}
+
+template <bool kFp8, bool kQk8, bool kSync>
+__global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_pair_kernel(
+    Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const int32_t* __restrict__ block_table, PlanPtrs plan,
+    void* __restrict__ out, float* __restrict__ lse_out, float score_scale_log2,
+    float out_scale, int out_fp8, float inv_q_scale, int fold_status, int64_t* __restrict__ trace) {
+  (void)fold_status;
+  int64_t t_start = 0;
+  if (trace != nullptr && threadIdx.x == 0) t_start = (int64_t)wall_clock64();
+  const int worker = xcd_worker(blockIdx.x, gridDim.x);
+  split_worker_pair<kFp8, kQk8, kSync>(worker, geo, q_out, k_pool, v_pool, block_table, plan, out,
+                                       lse_out, score_scale_log2, out_scale, out_fp8, inv_q_scale);
+  if (trace != nullptr) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t* tr = trace + 4 * (size_t)worker;
+      tr[0] = t_start;
+      tr[1] = (int64_t)wall_clock64();
+      tr[2] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_REG_HW_ID
+      tr[3] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID
+    }
+  }
+}
+
 template <bool kFp8, bool kQk8, bool kSync, bool kFold>
 __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
     Geometry geo, const uint16_t* __restrict__ q_out, const uint8_t* __restrict__ k_pool,
@@ -666,13 +902,18 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, b
                                   const PlanPtrs& plan, void* out, float* lse_out,
                                   float score_scale_log2, float out_scale, float inv_q_scale,
                                   int64_t* trace, hipStream_t stream) {
-  // one wave per (KV head, 16-column block), at most 8
-  const int virt = geo.num_kv_heads * ((geo.group * geo.tokens + 15) / 16);
+  // one wave per (KV head, 16-column block), at most 8; with two blocks per
+  // head (and no folded merge, which takes one new token), one wave per head
+  // runs both
+  const int ncb = (geo.group * geo.tokens + 15) / 16;
+  const bool pair = ncb == 2 && !fold;
+  const int virt = geo.num_kv_heads * (pair ? 1 : ncb);
   const int waves = virt < kMaxAttnWaves ? virt : kMaxAttnWaves;
   // lockstep only when every wave gets the same number of them
   const bool sync = virt % waves == 0;
+  const size_t lds = pair ? (size_t)waves * kPairSlotU32x4 * sizeof(u32x4) : 0;
   auto launch = [&](auto kernel) {
-    kernel<<<num_workers, waves * kWave, 0, stream>>>(
+    kernel<<<num_workers, waves * kWave, lds, stream>>>(
         geo, (const uint16_t*)q_out, (const uint8_t*)k_cache, (const uint8_t*)v_cache,
         block_table, plan, out, lse_out, score_scale_log2, out_scale, out_fp8 ? 1 : 0,
         inv_q_scale, fold_status ? 1 : 0, trace);
@@ -690,8 +931,22 @@ hipError_t launch_split_attention(const Geometry& geo, bool fp8, bool out_fp8, b
       else launch(split_attention_kernel<false, false, false, F>);
     }
   };
-  if (fold) pick(std::true_type{});
-  else pick(std::false_type{});
+  if (pair) {
+    if (fp8 && qk_fp8) {
+      if (sync) launch(split_attention_pair_kernel<true, true, true>);
+      else launch(split_attention_pair_kernel<true, true, false>);
+    } else if (fp8) {
+      if (sync) launch(split_attention_pair_kernel<true, false, true>);
+      else launch(split_attention_pair_kernel<true, false, false>);
+    } else {
+      if (sync) launch(split_attention_pair_kernel<false, false, true>);
+      else launch(split_attention_pair_kernel<false, false, false>);
+    }
+  } else if (fold) {
+    pick(std::true_type{});
+  } else {
+    pick(std::false_type{});
+  }
   return hipGetLastError();
 }
 

@@ -55,6 +55,8 @@ CASES = [
     dict(seq_lens=[65, 1000, 4097, 3], num_q_heads=64, num_kv_heads=8),
     dict(seq_lens=[2000, 70, 129], num_q_heads=16, num_kv_heads=2, kv_dtype="fp8"),
     dict(seq_lens=[130, 1500], num_q_heads=64, num_kv_heads=8, tokens=2),
+    dict(seq_lens=[130, 1500, 66], num_q_heads=64, num_kv_heads=8, tokens=4,
+         kv_dtype="fp8"),                                    # two blocks per wave
 ]
 
 

@@ -39,6 +39,7 @@ DECODE = [
     dict(seq_lens=[65, 1000, 4097, 3], num_q_heads=64, num_kv_heads=8),
     dict(seq_lens=[2000, 70, 129], num_q_heads=32, num_kv_heads=2),
     dict(seq_lens=[130, 1500], num_q_heads=64, num_kv_heads=8, tokens=2),
+    dict(seq_lens=[130, 1500, 67], num_q_heads=64, num_kv_heads=8, tokens=4),   # two blocks per wave
 ]
 
 

@@ -101,9 +101,15 @@ MULTI = [
     dict(seq_lens=[16, 64 * 9 + 1], num_q_heads=8, num_kv_heads=8, tokens=16),   # group 1
     dict(seq_lens=[300, 65], num_q_heads=32, num_kv_heads=4, tokens=2, norm_before_rope=True,
          kv_dtype="fp8"),
-    # more than 16 columns per KV head: blocks of 16 on neighbouring waves
+    # 17 to 32 columns per KV head: both blocks of 16 on the head's wave, one
+    # accumulator parked in LDS; lockstep with 8 and 16 KV heads, not with 12
     dict(seq_lens=[5, 66, 1000, 131], num_q_heads=64, num_kv_heads=8, tokens=4),        # 32
     dict(seq_lens=[3, 700, 64 * 3 + 2], num_q_heads=8, num_kv_heads=1, tokens=3),       # 24
+    dict(seq_lens=[5, 66, 1000, 64 * 20 + 1], num_q_heads=64, num_kv_heads=8, tokens=4,
+         kv_dtype="fp8"),                                                                # 32
+    dict(seq_lens=[17, 64 * 7 + 2, 2500], num_q_heads=32, num_kv_heads=16, tokens=16),  # 32
+    dict(seq_lens=[9, 800, 64 * 4 + 1], num_q_heads=36, num_kv_heads=12, tokens=8),     # 24
+    # more: blocks of 16 on neighbouring waves
     dict(seq_lens=[8, 520, 2000], num_q_heads=16, num_kv_heads=2, tokens=8, kv_dtype="fp8"),  # 64
     dict(seq_lens=[40, 300], num_q_heads=12, num_kv_heads=4, tokens=11),               # 33
 ]
