@@ -734,9 +734,9 @@ __global__ __launch_bounds__(kMaxAttnWaves * kWave) void split_attention_kernel(
 // in parallel: workgroup (s, g, b) owns slice run s of sequence b -- 16/S of
 // the 16 slices, one contiguous 128G*4/S-byte piece of every row -- where S
 // grows with n up to the grid's slice count, and rows beyond one round are
-// read in further rounds.  A piece is 32G/S float4 (at most 64), so one wave
-// instruction covers 64/(32G/S) rows, and each lane keeps kMergeUnroll rows
-// in flight.  The first round of row
+// read in further rounds.  A piece is 32G/S float4 (at most 128); a lane holds
+// kP = 1 or 2 of them, so one wave instruction covers 64 kP/(32G/S) rows, and
+// each lane keeps kMergeUnroll rows in flight.  The first round of row
 // reads is issued before the lse are staged in LDS and turned into weights
 // 2^(lse - max) / sum per head, so the two overlap.  Per-(wave, row-lane)
 // sums are added in a fixed order: deterministic.
@@ -763,6 +763,7 @@ constexpr int kMergeLseUnroll = LBSR_MERGE_LSE_UNROLL;
 // heads), most of them short-lived; 4 of them per CU (<= 128 VGPRs per wave)
 // keep the whole grid resident at once, which measured faster than deeper
 // per-thread unrolling at lower occupancy.
+template <int kP>
 __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry geo, PlanPtrs plan,
                                                                     void* __restrict__ out,
                                                                     float* __restrict__ lse_out,
@@ -790,34 +791,40 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
   // in one round of reads, at most gridDim.x; surplus workgroups leave.
   int nslices = min_slices;
   while (nslices < (int)gridDim.x &&
-         count > kMergeWaves * (kWave / (G * 32 / nslices)) * kMergeUnroll)
+         count > kMergeWaves * (kWave / (G * 32 / nslices / kP)) * kMergeUnroll)
     nslices *= 2;
   if (slice >= nslices) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const size_t head0 = (size_t)g * G;
   extern __shared__ float s_w[];                           // [count][G]: lse, then weights
-  __shared__ f32x4 s_acc[kThreads];                        // one partial sum per lane
+  __shared__ f32x4 s_acc[kP][kThreads];                    // kP partial sums per lane
 
   // Loads below are unconditional (indices clamped into range, results of the
   // clamped ones discarded) so that a thread's loads issue back to back.
-  const int per_row = G * 32 / nslices;   // float4 of one row's piece (<= 64)
-  const int rows_per_inst = kWave / per_row;
-  const int r_sub_raw = lane / per_row;
+  // A lane holds kP float4 of a row's piece: e and e + per_lane.
+  const int per_row = G * 32 / nslices;   // float4 of one row's piece (<= 64 kP)
+  const int per_lane = per_row / kP;
+  const int rows_per_inst = kWave / per_lane;
+  const int r_sub_raw = lane / per_lane;
   const bool active = r_sub_raw < rows_per_inst;
   const int r_sub = active ? r_sub_raw : 0;
-  const int e = active ? lane - r_sub_raw * per_row : 0;   // float4 inside the piece
+  const int e = active ? lane - r_sub_raw * per_lane : 0;   // float4 inside the piece
   // a row is [16 slices of 8 channels][G columns][2 float4]; float4 f of the
   // row (f = slice * per_row + e) holds column (f % 2G) / 2
-  const int hh = ((slice * per_row + e) % (2 * G)) >> 1;
+  int hh[kP];
+#pragma unroll
+  for (int p = 0; p < kP; ++p) hh[p] = ((slice * per_row + e + p * per_lane) % (2 * G)) >> 1;
   const f32x4* po = (const f32x4*)plan.partial_o + head0 * 32 + slice * per_row + e;
   const int rows_per_round = kMergeWaves * rows_per_inst * kMergeUnroll;
   auto row_of = [&](int base, int u) { return base + (u * kMergeWaves + wave) * rows_per_inst + r_sub; };
-  f32x4 o[kMergeUnroll];
+  f32x4 o[kMergeUnroll][kP];
   auto load_round = [&](int base) {
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const int i = min(row_of(base, u), count - 1);
-      o[u] = po[(size_t)(c0 + i) * Hq * 32];   // row c0 + i of this piece
+#pragma unroll
+      for (int p = 0; p < kP; ++p)
+        o[u][p] = po[(size_t)(c0 + i) * Hq * 32 + p * per_lane];   // row c0 + i of this piece
     }
   };
 
@@ -861,22 +868,29 @@ __global__ __launch_bounds__(kMergeWaves * kWave, 4) void merge_kernel(Geometry 
   __syncthreads();
 
   // 3. weighted sum of this channel slice over the rows
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[kP];
+#pragma unroll
+  for (int p = 0; p < kP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < count; base += rows_per_round) {
     if (base > 0) load_round(base);
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const int i = row_of(base, u);
-      const float wgt = (active && i < count) ? s_w[min(i, count - 1) * G + hh] : 0.f;
-      acc += wgt * o[u];
+#pragma unroll
+      for (int p = 0; p < kP; ++p) {
+        const float wgt = (active && i < count) ? s_w[min(i, count - 1) * G + hh[p]] : 0.f;
+        acc[p] += wgt * o[u][p];
+      }
     }
   }
-  s_acc[tid] = acc;
+#pragma unroll
+  for (int p = 0; p < kP; ++p) s_acc[p][tid] = acc[p];
   __syncthreads();
   for (int t = tid; t < per_row; t += kThreads) {
+    const int p = kP == 1 ? 0 : t / per_lane, t2 = t - p * per_lane;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < kMergeWaves; ++w)
-      for (int r = 0; r < rows_per_inst; ++r) sum += s_acc[w * kWave + r * per_row + t];
+      for (int r = 0; r < rows_per_inst; ++r) sum += s_acc[p][w * kWave + r * per_lane + t2];
     // float4 f = slice * per_row + t of the row: 8-channel slice f / 2G,
     // column (f % 2G) / 2, channels 4 * (f % 2) ..
     const int f = slice * per_row + t;
@@ -954,16 +968,23 @@ hipError_t launch_combine(const Geometry& geo, const PlanPtrs& plan, void* out, 
                           int max_chunks_per_seq, bool out_fp8, bool fold_token_status,
                           hipStream_t stream) {
   // S slices: a power of two dividing 32 with 32G/S <= 64 float4 per row
-  // slice, G = group * Tq columns per (chunk, KV group), at most 64
+  // slice, G = group * Tq columns per (chunk, KV group), at most 64.  Where
+  // that takes 16 or more slices (G > 16), a lane holds two float4 of a piece
+  // at half the slices: the 4-token mix's merge went from 4096 workgroups
+  // (27 us) to 2048 (19.4 us).  At 16 columns the halving (2048 -> 1024
+  // workgroups) measured 1 us slower: the longest sequence's rows then fall
+  // to half as many workgroups.
   const int cols = geo.group * geo.tokens;
   int slices = LBSR_MERGE_MIN_SLICES;
   while (slices < 32 && 32 * cols / slices > kWave) slices *= 2;
+  const bool two = slices >= 16;
+  if (two) slices /= 2;
   const int max_slices = slices > LBSR_MERGE_MAX_SLICES ? slices : LBSR_MERGE_MAX_SLICES;
   dim3 grid(max_slices, geo.num_kv_heads, geo.batch);
   const size_t lds = (size_t)max_chunks_per_seq * cols * sizeof(float);
-  merge_kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, out, lse_out, slices,
-                                                           out_fp8 ? 1 : 0,
-                                                           fold_token_status ? 1 : 0);
+  auto kernel = two ? merge_kernel<2> : merge_kernel<1>;
+  kernel<<<grid, kMergeWaves * kWave, lds, stream>>>(geo, plan, out, lse_out, slices,
+                                                     out_fp8 ? 1 : 0, fold_token_status ? 1 : 0);
   return hipGetLastError();
 }
 
