@@ -321,10 +321,20 @@ def prefill_leg(dev, reps=10, warmup=3, names=None):
     return legs
 
 
+def oracle_threads():
+    """BLAS threads for the oracle leg: the host's cores, or the CPU share the
+    environment grants (OMP_NUM_THREADS), whichever is smaller."""
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
+
+
 def cpu_baseline(w, dev, min_seconds=10.0):
     """The fp64 oracle on the host: the whole step (plan, prologue, attention over
     every sequence and head) on a fresh input set of the workload, drawn by the
-    seeded generator on the device and copied to the host untouched."""
+    seeded generator on the device and copied to the host untouched.  Timed
+    with BLAS on the host's cores (repeated for about min_seconds), and once
+    more with BLAS on one thread, for reference."""
     import oracle
     from threadpoolctl import threadpool_limits
     g = wl.make_inputs(w, device=dev)
@@ -345,25 +355,63 @@ def cpu_baseline(w, dev, min_seconds=10.0):
     cfg = {"kv_dtype": w.kv_dtype, "k_scale": w.k_scale, "v_scale": w.v_scale,
            "sm_scale": 1 / np.sqrt(128.0), "page_stride": page_stride,
            "head_stride": head_stride, "num_kv_heads": w.num_kv_heads}
+
+    def one_step():
+        oracle.plan_dynamic(lens, 256)
+        pro = oracle.prologue(bits["q"], bits["k"], bits["v"], host["positions"].numpy(),
+                              bits["q_norm_w"], bits["k_norm_w"], bt, theta=w.rope_theta,
+                              eps=w.rms_eps, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
+                              v_scale=w.v_scale)
+        oracle.decode_attention(pro["q_out"], (kp, vp), pro, lens, bt, cfg)
+
+    threads = oracle_threads()
     reps, dt = 0, 0.0
-    with threadpool_limits(1):
-        while dt < min_seconds:       # repeat the whole step for ~10 s of CPU work
+    with threadpool_limits(threads):
+        while dt < min_seconds:       # repeat the whole step for ~min_seconds of wall time
             t0 = time.perf_counter()
-            oracle.plan_dynamic(lens, 256)
-            pro = oracle.prologue(bits["q"], bits["k"], bits["v"], host["positions"].numpy(),
-                                  bits["q_norm_w"], bits["k_norm_w"], bt, theta=w.rope_theta,
-                                  eps=w.rms_eps, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
-                                  v_scale=w.v_scale)
-            oracle.decode_attention(pro["q_out"], (kp, vp), pro, lens, bt, cfg)
+            one_step()
             dt += time.perf_counter() - t0
             reps += 1
-    nbytes = compulsory_bytes(w)["total"] * reps
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        one_step()
+        dt1 = time.perf_counter() - t0
+    nbytes = compulsory_bytes(w)["total"]
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"the whole {w.name} step (plan, prologue for {w.batch} tokens, "
                       f"full-softmax attention for all {w.batch} sequences x "
-                      f"{w.num_q_heads} heads), fp64 numpy, BLAS limited to 1 thread, "
-                      f"repeated {reps} times",
-            "seconds": round(dt, 2)}
+                      f"{w.num_q_heads} heads), fp64 numpy, BLAS on {threads} threads "
+                      f"(host reports {os.cpu_count()} CPUs), repeated {reps} times",
+            "seconds": round(dt, 2),
+            "one_thread": {"value": round(nbytes / dt1 / 1e9, 4), "unit": "GB/s",
+                           "seconds": round(dt1, 2)}}
+
+
+def stream_ceiling(dev, nbytes=1 << 30, reps=10):
+    """The streaming-read probe over 1 GiB (the split kernel's load pattern,
+    one 8-wave workgroup per CU): median GB/s over ``reps`` launches timed
+    with HIP events on the launch stream."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        lb.stream_read(buf, sink)
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        lb.stream_read(buf, sink)
+        e1.record(st)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del buf, sink
+    torch.cuda.empty_cache()
+    med = float(np.median(ms))
+    return {"bytes": nbytes, "us": round(med * 1e3, 2), "GBs": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "launches": reps,
+            "pattern": "non-temporal 16-byte loads, one 32 KiB burst per wave, 8 waves per "
+                       "workgroup, one workgroup per CU"}
 
 
 def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_dtype="bf16"):
@@ -474,6 +522,7 @@ def main():
     value = cb["total"] / (ms * 1e-3) / 1e9
     split_ms = float(r["kernel_ms"][1])
     split_gbs = split_kernel_bytes(w) / (split_ms * 1e-3) / 1e9
+    ceiling = stream_ceiling(dev)
     names = ("plan_prologue", "split_attention", "merge")
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -499,7 +548,9 @@ def main():
                      "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, w.kv_dtype),
                      "kernel": f"split_attention_kernel<{w.kv_dtype}>",
-                     "algorithmic_bytes": split_kernel_bytes(w)},
+                     "algorithmic_bytes": split_kernel_bytes(w),
+                     "frac_of_stream_ceiling": round(split_gbs / ceiling["GBs"], 4)},
+        "stream_read_ceiling": ceiling,
         "cpu_baseline": None,
         "load_balance": r["balance"],
     }

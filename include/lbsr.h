@@ -38,7 +38,8 @@
  *     must stay alive until the stream has passed the launch.
  *   - Host-side validation happens before any launch; on failure nothing is
  *     launched, a status is returned and lbsr_last_error() holds a message.
- *   - No entry point synchronises, except lbsr_decode_step_timed (bench).
+ *   - No entry point synchronises, except lbsr_decode_step_timed (bench) and
+ *     the two readers lbsr_read_plan / lbsr_read_device_error (tests, tools).
  *   - Device-side preconditions are checked in the kernels without faulting:
  *     a violating input is clamped or skipped and a bit is OR-ed into the
  *     workspace's sticky error word (see LBSR_DEV_ERR_*).
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LBSR_ABI_VERSION 5
+#define LBSR_ABI_VERSION 6
 #define LBSR_NUM_XCDS 8     /* accelerator complex dies of an MI355X */
 #define LBSR_MAX_XCD_WEIGHT 65536
 #define LBSR_HEAD_DIM 128
@@ -275,8 +276,13 @@ lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq
                       void *stream);
 
 /*
- * Split attention + merge over the schedule in `workspace` (run lbsr_plan
- * first with the same shape, batch and cfg).  For sequence b, q head h and
+ * Split attention + merge over the schedule in `workspace` ([A] "Why does
+ * dynamic scheduling matter in attention?": the 64-token tiles dealt out by
+ * the schedule are attended on the compute units they were given to, and a
+ * split sequence's pieces are merged; [A] "Two new HPC backends in the vLLM
+ * ecosystem": q heads grouped over shared KV heads; [B] intro and [A]: BF16
+ * or FP8 E4M3 cache).  Run lbsr_plan first with the same shape, batch and
+ * cfg.  For sequence b, q head h and
  * KV head g = h / (Hq/Hkv), over the rows j < L_b (with Tq > 1: new token t
  * over the rows j <= L_b - Tq + t, and [b] below reads [b][t]):
  *   out[b][h] = sum_j softmax_j(sm_scale * <q_out[b][h], K_j>) V_j      (BF16)
@@ -290,15 +296,18 @@ lbsr_status lbsr_plan(const lbsr_shape *shape, int32_t batch, const int32_t *seq
  * Rows at or past L_b of a sequence's last page are never used, whatever
  * they hold.  Deterministic.
  * The merge is a second launch by default.  With cfg->flags =
- * LBSR_SCHED_FOLD_MERGE ([A] "Why does dynamic scheduling matter in
- * attention?" chains its kernels to cut launch gaps) there is one launch:
+ * LBSR_SCHED_FOLD_MERGE ([A] "Turning the FP8 MoE pipeline into a single
+ * execution path" chains kernels to cut the gaps between launches; the same
+ * aim applied here) there is one launch:
  * every finished chunk is published with a device-scope fence and counted
  * with a device-scope atomic, and the workgroup (or, when the KV heads do not
  * divide evenly over its waves, the wave) that completes a sequence's count
  * merges its rows in chunk order.  Which one that is varies, the arithmetic
  * does not: results are deterministic either way (but not bit-identical
  * between the two forms).  One new token per sequence; the workspace's
- * arrival counters are cleared by lbsr_plan / the step's plan.  On MI355X a
+ * arrival counters are cleared by lbsr_plan / the step's plan, and the last
+ * arrival of each (sequence, KV head) puts its counter back to zero, so one
+ * plan may serve several lbsr_attention calls in stream order.  On MI355X a
  * device-scope release writes back an L2, so this form is slower than two
  * launches except for small, launch-bound batches.
  */
@@ -309,7 +318,11 @@ lbsr_status lbsr_attention(const lbsr_shape *shape, const lbsr_params *params, i
                            void *stream);
 
 /*
- * One whole decode step on `stream` (arguments as for the three calls above):
+ * One whole decode step ([A] "Why does dynamic scheduling matter in
+ * attention?": the prologue fused into one pass, then the per-step
+ * length-proportional schedule and the split attention; [B] "Code analysis
+ * 2": entered directly with caller-provided outputs, so a HIP graph can
+ * capture it) on `stream` (arguments as for the three calls above):
  * the schedule and the prologue in one launch, then split attention and the
  * merge.  Same results as lbsr_plan, lbsr_rope_norm_kv_write and
  * lbsr_attention in turn; the prologue's error bits end up in the
@@ -447,6 +460,49 @@ lbsr_status lbsr_decode_step_timed(const lbsr_shape *shape, const lbsr_params *p
                                    const lbsr_sched_cfg *cfg, void *workspace,
                                    size_t ws_bytes, void *out, float *lse_out,
                                    void *stream, float *kernel_ms, int64_t *trace);
+
+/* Host arrays lbsr_read_plan fills; any may be NULL to skip it.  Sizes come
+ * from lbsr_workspace_layout for the same shape, batch and cfg. */
+typedef struct {
+  int32_t *cu_tiles;     /* [batch + 1] */
+  int32_t *worker_chunk; /* [num_workers + 1] */
+  int32_t *chunks;       /* [max_chunks][4]; the first worker_chunk[num_workers] rows hold the plan */
+  int32_t *seq_chunk;    /* [batch + 1] */
+  int32_t *seq_len_eff;  /* [batch] */
+} lbsr_plan_host;
+
+/*
+ * Test / tool helper: the schedule ([A] "Why does dynamic scheduling matter
+ * in attention?") that lbsr_plan or a decode step last wrote into
+ * `workspace` (device), copied to the host arrays of *out; *num_chunks (host,
+ * nullable) receives the chunk count.  Waits for `stream` first, then copies
+ * synchronously.  Validates like lbsr_plan (LBSR_E_WORKSPACE if ws_bytes is
+ * too small for the layout).  Not for production paths.
+ */
+lbsr_status lbsr_read_plan(const lbsr_shape *shape, int32_t batch, const lbsr_sched_cfg *cfg,
+                           const void *workspace, size_t ws_bytes, lbsr_plan_host *out,
+                           int32_t *num_chunks, void *stream);
+
+/*
+ * Test / tool helper: the sticky LBSR_DEV_ERR_* bits of a decode workspace
+ * (its first int32, the error word of every layout) into *code (host).  Waits
+ * for `stream` first.  The device-side checks of a step ([A] "Why does
+ * dynamic scheduling matter in attention?": lengths, pages and positions the
+ * schedule and the cache write rely on) report here instead of faulting.
+ */
+lbsr_status lbsr_read_device_error(const void *workspace, int32_t *code, void *stream);
+
+/*
+ * Benchmark helper, not an operation of the method: reads `bytes` (a positive
+ * multiple of 32 KiB) of device memory at `buf` (16-byte aligned) the way the
+ * split-attention kernel reads K/V tiles -- non-temporal 16-byte loads, one
+ * 32 KiB burst per wave, 8 waves per workgroup, `workgroups` workgroups (0 ->
+ * the device's CU count) -- and writes one checksum word per workgroup to
+ * `sink` (device, uint32[workgroups]).  Its rate is the streaming ceiling the
+ * split kernel's bandwidth is reported against.  Asynchronous on `stream`.
+ */
+lbsr_status lbsr_stream_read(const void *buf, size_t bytes, int32_t workgroups, uint32_t *sink,
+                             void *stream);
 
 #ifdef __cplusplus
 }

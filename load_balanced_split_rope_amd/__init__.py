@@ -12,12 +12,12 @@ from .decode import (DecodeConfig, Schedule, device_workers, workspace_layout,
                      decode_step_timed, read_plan, read_error, xcd_rates,
                      xcd_weights_from_rates, prefill_attention, prefill_step,
                      prefill_attention_varlen, prefill_step_varlen,
-                     prefill_workspace_size, alloc_prefill_workspace)
+                     prefill_workspace_size, alloc_prefill_workspace, stream_read)
 
 __all__ = [
     "LbsrError", "LibraryNotBuilt", "EXPORTS", "LIB_PATH", "DecodeConfig", "Schedule",
     "device_workers", "workspace_layout", "alloc_workspace", "rope_norm_kv_write", "plan",
     "attention", "decode_step", "decode_step_timed", "read_plan", "read_error", "xcd_rates",
     "xcd_weights_from_rates", "prefill_attention", "prefill_step", "prefill_attention_varlen",
-    "prefill_step_varlen", "prefill_workspace_size", "alloc_prefill_workspace",
+    "prefill_step_varlen", "prefill_workspace_size", "alloc_prefill_workspace", "stream_read",
 ]

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # LBSR_LIB may name another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("LBSR_LIB") or os.path.join(HERE, "liblbsr.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 HEAD_DIM = 128
 PAGE_SIZE = 64
 TILE_ELEMS = HEAD_DIM * PAGE_SIZE
@@ -37,7 +37,8 @@ EXPORTS = (
     "lbsr_workspace_layout", "lbsr_workspace_size", "lbsr_rope_norm_kv_write", "lbsr_plan",
     "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed", "lbsr_prefill_attention",
     "lbsr_prefill_step", "lbsr_prefill_attention_varlen", "lbsr_prefill_step_varlen",
-    "lbsr_prefill_workspace_size",
+    "lbsr_prefill_workspace_size", "lbsr_read_plan", "lbsr_read_device_error",
+    "lbsr_stream_read",
 )
 
 
@@ -88,6 +89,12 @@ class WsLayout(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class PlanHost(ctypes.Structure):
+    _fields_ = [("cu_tiles", ctypes.c_void_p), ("worker_chunk", ctypes.c_void_p),
+                ("chunks", ctypes.c_void_p), ("seq_chunk", ctypes.c_void_p),
+                ("seq_len_eff", ctypes.c_void_p)]
+
+
 _lib = None
 _lib_lock = threading.Lock()
 
@@ -129,6 +136,11 @@ def _declare(lib):
         "lbsr_decode_step_timed": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                                    + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, ctypes.c_size_t,
                                                   _P, _P, _P, ctypes.POINTER(ctypes.c_float), _P]),
+        "lbsr_read_plan": (st, [ctypes.POINTER(Shape), _I32, ctypes.POINTER(SchedCfg), _P,
+                                ctypes.c_size_t, ctypes.POINTER(PlanHost), ctypes.POINTER(_I32),
+                                _P]),
+        "lbsr_read_device_error": (st, [_P, ctypes.POINTER(_I32), _P]),
+        "lbsr_stream_read": (st, [_P, ctypes.c_size_t, _I32, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -789,4 +789,65 @@ lbsr_status lbsr_decode_step_timed(const lbsr_shape* shape, const lbsr_params* p
                           lse_out, stream, kernel_ms, trace);
 }
 
+lbsr_status lbsr_read_plan(const lbsr_shape* shape, int32_t batch, const lbsr_sched_cfg* cfg,
+                           const void* workspace, size_t ws_bytes, lbsr_plan_host* out,
+                           int32_t* num_chunks, void* stream) {
+  g_last_error[0] = 0;
+  if (!out) return fail(LBSR_E_INVALID, "out is NULL");
+  lbsr_ws_layout l;
+  LBSR_CHECK(compute_layout(shape, batch, cfg, &l));
+  LBSR_CHECK(check_workspace(const_cast<void*>(workspace), ws_bytes, l));
+  LBSR_CHECK(hip_status(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize"));
+  const char* base = (const char*)workspace;
+  const struct {
+    int32_t* dst;
+    size_t off, count;
+    const char* what;
+  } arrays[] = {
+      {out->cu_tiles, l.cu_tiles, (size_t)batch + 1, "cu_tiles"},
+      {out->worker_chunk, l.worker_chunk, (size_t)l.num_workers + 1, "worker_chunk"},
+      {out->chunks, l.chunks, 4 * (size_t)l.max_chunks, "chunks"},
+      {out->seq_chunk, l.seq_chunk, (size_t)batch + 1, "seq_chunk"},
+      {out->seq_len_eff, l.seq_len_eff, (size_t)batch, "seq_len_eff"},
+  };
+  for (const auto& a : arrays)
+    if (a.dst)
+      LBSR_CHECK(hip_status(hipMemcpy(a.dst, base + a.off, 4 * a.count, hipMemcpyDeviceToHost),
+                            a.what));
+  if (num_chunks) {
+    // the chunk count is the last worker's end: worker_chunk[num_workers]
+    LBSR_CHECK(hip_status(hipMemcpy(num_chunks, base + l.worker_chunk + 4 * (size_t)l.num_workers,
+                                    4, hipMemcpyDeviceToHost),
+                          "chunk count"));
+  }
+  return LBSR_OK;
+}
+
+lbsr_status lbsr_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                             void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(check_ptr(buf, 16, "buf"));
+  LBSR_CHECK(check_ptr(sink, 4, "sink"));
+  const int64_t blk = lbsr::stream_read_block_bytes();
+  if (bytes == 0 || bytes % blk != 0)
+    return fail(LBSR_E_INVALID, "bytes (%zu) must be a positive multiple of %lld", bytes,
+                (long long)blk);
+  if (workgroups < 0 || workgroups > (1 << 20))
+    return fail(LBSR_E_INVALID, "workgroups %d outside [0, 2^20]", workgroups);
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  const int wg = workgroups ? workgroups : d.cu_count;
+  return hip_status(lbsr::launch_stream_read(buf, bytes, wg, sink, (hipStream_t)stream),
+                    "stream_read_kernel launch");
+}
+
+lbsr_status lbsr_read_device_error(const void* workspace, int32_t* code, void* stream) {
+  g_last_error[0] = 0;
+  if (!code) return fail(LBSR_E_INVALID, "code is NULL");
+  LBSR_CHECK(check_ptr(workspace, 256, "workspace"));
+  LBSR_CHECK(hip_status(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize"));
+  // the error word is the workspace's first array, at offset 0 for every layout
+  return hip_status(hipMemcpy(code, workspace, 4, hipMemcpyDeviceToHost), "error word");
+}
+
 }  // extern "C"

@@ -529,7 +529,11 @@ __device__ __forceinline__ void split_worker(
             __syncthreads();
             if (threadIdx.x == 0) {
               __threadfence();
-              s_old = atomicAdd(&plan.arrivals[(size_t)b * geo.num_kv_heads + vg], 1);
+              int32_t* ctr = &plan.arrivals[(size_t)b * geo.num_kv_heads + vg];
+              s_old = atomicAdd(ctr, 1);
+              // The last arrival puts the count back to 0, so a later launch
+              // over the same plan (another layer of the step) counts afresh.
+              if (s_old == nchunks - 1) atomicExch(ctr, 0);
             }
             __syncthreads();
             old = s_old;
@@ -537,7 +541,11 @@ __device__ __forceinline__ void split_worker(
           } else {
             __threadfence();
             old = 0;
-            if (lane == 0) old = atomicAdd(&plan.arrivals[(size_t)b * geo.num_kv_heads + g], 1);
+            if (lane == 0) {
+              int32_t* ctr = &plan.arrivals[(size_t)b * geo.num_kv_heads + g];
+              old = atomicAdd(ctr, 1);
+              if (old == nchunks - 1) atomicExch(ctr, 0);   // last arrival: reset for reuse
+            }
             old = __shfl(old, 0, kWave);
           }
           if (old == nchunks - 1) {

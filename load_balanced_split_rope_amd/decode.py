@@ -397,33 +397,45 @@ def prefill_step_varlen(cfg: DecodeConfig, q_start, q, k, v, positions, seq_lens
         B._stream(stream)))
 
 
-def read_plan(cfg: DecodeConfig, batch: int, sched: Schedule, workspace):
-    """Copy the plan arrays out of a workspace (synchronises; for tests and tools)."""
+def read_plan(cfg: DecodeConfig, batch: int, sched: Schedule, workspace, stream=None):
+    """The plan arrays of a workspace, through lbsr_read_plan (synchronises the
+    stream; for tests and tools)."""
     lay = workspace_layout(cfg, batch, sched)
-    ws = workspace.cpu().numpy()
-
-    def arr(off, n):
-        return ws[off:off + 4 * n].view(np.int32).copy()
-
     W = lay.num_workers
-    worker_chunk = arr(lay.worker_chunk, W + 1)
-    n_chunks = int(worker_chunk[-1])
-    return {
-        "error_word": int(arr(lay.error_word, 1)[0]),
-        "cu_tiles": arr(lay.cu_tiles, batch + 1),
-        "worker_chunk": worker_chunk,
-        "chunks": arr(lay.chunks, 4 * n_chunks).reshape(-1, 4),
-        "seq_chunk": arr(lay.seq_chunk, batch + 1),
-        "seq_len_eff": arr(lay.seq_len_eff, batch),
-        "num_workers": W,
-        "max_chunks": lay.max_chunks,
-    }
+    arrs = {"cu_tiles": np.zeros(batch + 1, np.int32),
+            "worker_chunk": np.zeros(W + 1, np.int32),
+            "chunks": np.zeros((lay.max_chunks, 4), np.int32),
+            "seq_chunk": np.zeros(batch + 1, np.int32),
+            "seq_len_eff": np.zeros(batch, np.int32)}
+    host = B.PlanHost(*(a.ctypes.data for a in arrs.values()))
+    n = ctypes.c_int32(0)
+    s = cfg.shape()
+    B._check(B.lib().lbsr_read_plan(ctypes.byref(s), batch, ctypes.byref(sched.cfg()),
+                                    B._ptr(workspace), workspace.numel(), ctypes.byref(host),
+                                    ctypes.byref(n), B._stream(stream)))
+    arrs["chunks"] = arrs["chunks"][:n.value].copy()
+    return {"error_word": read_error(cfg, batch, sched, workspace, stream), **arrs,
+            "num_workers": W, "max_chunks": lay.max_chunks}
 
 
-def read_error(cfg: DecodeConfig, batch: int, sched: Schedule, workspace):
-    """The workspace's sticky device error bits (synchronises)."""
-    lay = workspace_layout(cfg, batch, sched)
-    return int(workspace[lay.error_word:lay.error_word + 4].cpu().numpy().view(np.int32)[0])
+def read_error(cfg: DecodeConfig, batch: int, sched: Schedule, workspace, stream=None):
+    """The workspace's sticky device error bits, through lbsr_read_device_error
+    (synchronises the stream)."""
+    code = ctypes.c_int32(0)
+    B._check(B.lib().lbsr_read_device_error(B._ptr(workspace), ctypes.byref(code),
+                                            B._stream(stream)))
+    return int(code.value)
+
+
+def stream_read(buf, sink, workgroups=0, stream=None):
+    """The streaming-read probe (lbsr_stream_read): reads all of ``buf`` (a
+    device tensor whose size is a multiple of 32 KiB) with the split kernel's
+    load pattern; ``sink`` is a device uint32-sized buffer of at least
+    ``workgroups`` (or CU count) words.  Asynchronous."""
+    if buf.device.type != "cuda" or sink.device.type != "cuda":
+        raise ValueError("stream_read needs device tensors")
+    B._check(B.lib().lbsr_stream_read(B._ptr(buf), _nbytes(buf), int(workgroups), B._ptr(sink),
+                                      B._stream(stream)))
 
 
 def xcd_rates(traces, plans):

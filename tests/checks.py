@@ -4,7 +4,13 @@ Tolerance (reading R14 of the values the step must match):
 * BF16 cache: every element |got - ref| <= 2e-2 + 1e-2 |ref|, and for the
   attention output also ||got - ref||_2 / ||ref||_2 <= 1e-2 (the elementwise
   bound alone is looser than the signal at long lengths).
-* FP8 cache: every element |got - ref| <= 6e-2 on the attention output.
+* FP8 cache: every element |got - ref| <= 6e-2 on the attention output, and
+  ||got - ref||_2 / ||ref||_2 <= 2e-2.  The same codes are decoded exactly on
+  both sides, so the relative error is of the size the BF16 path shows; the
+  elementwise bound alone passes an all-zero output once |o| < 6e-2, which
+  N(0,1) values reach at a few thousand rows.
+* FP8 output: the codes within the bound above plus half an E4M3 step of the
+  value, and in L2 within the half-step norm plus the cache's relative bound.
 * The schedule and every cache index: bit-exact.
 """
 
@@ -14,7 +20,7 @@ import torch
 from oracle import tile_offset, PAGE_SIZE, BF16_NAN_BITS, E4M3_NAN_CODE
 
 BF16_ATOL, BF16_RTOL, BF16_REL_L2 = 2e-2, 1e-2, 1e-2
-FP8_ATOL = 6e-2
+FP8_ATOL, FP8_REL_L2 = 6e-2, 2e-2
 
 
 def to_f64(t):
@@ -42,6 +48,8 @@ def check_output(got, ref, kv_dtype, what="output", rel_l2=True):
             assert rl2 <= BF16_REL_L2, f"{what}: relative L2 {rl2:.3e} > {BF16_REL_L2}"
     else:
         assert max_abs <= FP8_ATOL, f"{what}: max abs {max_abs:.3e} > {FP8_ATOL}"
+        if rel_l2:
+            assert rl2 <= FP8_REL_L2, f"{what}: relative L2 {rl2:.3e} > {FP8_REL_L2}"
     return max_abs, rl2
 
 
@@ -53,10 +61,13 @@ def e4m3_step(x):
     return np.ldexp(1.0, (np.maximum(e, -6) - 3).astype(np.int64))
 
 
-def check_output_fp8(codes, ref, kv_dtype, out_scale, what="output"):
+def check_output_fp8(codes, ref, kv_dtype, out_scale, what="output", rel_l2=True):
     """FP8 output (R21): the decoded codes times out_scale must lie within the
     R14 tolerance of the fp64 result plus half an E4M3 step of the output;
-    where |ref| / out_scale exceeds 448 the code must be the saturated one."""
+    where |ref| / out_scale exceeds 448 the code must be the saturated one.
+    In L2 (unsaturated elements): ||got - ref|| <= ||half steps|| + r ||ref||,
+    r the cache's relative L2 bound -- rounding moves each element by at most
+    half a step, so the triangle inequality gives this bound."""
     from oracle import e4m3_to_f64
     got = e4m3_to_f64(np.asarray(codes, dtype=np.uint8)) * out_scale
     ref = np.asarray(ref, dtype=np.float64)
@@ -70,6 +81,12 @@ def check_output_fp8(codes, ref, kv_dtype, out_scale, what="output"):
     err = np.abs(got - ref)
     bad = (err > tol) & ~sat
     assert not bad.any(), f"{what}: {int(bad.sum())} codes out of tolerance, max err {err.max():.3e}"
+    if rel_l2 and (~sat).any():
+        r = BF16_REL_L2 if kv_dtype == "bf16" else FP8_REL_L2
+        half = 0.5 * e4m3_step(np.minimum(np.abs(x[~sat]), 448)) * out_scale
+        lim = np.linalg.norm(half) + r * np.linalg.norm(ref[~sat])
+        dist = np.linalg.norm(got[~sat] - ref[~sat])
+        assert dist <= lim, f"{what}: L2 distance {dist:.3e} > {lim:.3e}"
     return float(err[~sat].max()) if (~sat).any() else 0.0
 
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lbsr_abi_version() == 5
+    assert lib.lbsr_abi_version() == 6
     for st in range(5):
         assert lib.lbsr_status_string(st).startswith(b"LBSR_")
     assert lib.lbsr_status_string(99) == b"unknown lbsr_status"
@@ -349,3 +349,55 @@ def test_fold_merge_validation(lib, Hq, Hkv, tokens, status):
     out = B.WsLayout()
     got = lib.lbsr_workspace_layout(ctypes.byref(s), 16, ctypes.byref(c), ctypes.byref(out))
     assert got == status, lib.lbsr_last_error()
+
+
+def test_readers_validate_before_touching_the_device(lib):
+    """lbsr_read_plan / lbsr_read_device_error check their arguments on the
+    host before any synchronisation or copy."""
+    cfg = cfg_mix()
+    s = cfg.shape()
+    sched = Schedule("dynamic", num_workers=256)
+    c = sched.cfg()
+    lay = workspace_layout(cfg, 32, sched)
+    host = B.PlanHost()
+    n = ctypes.c_int32()
+    fake = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
+    cases = [
+        (lambda: lib.lbsr_read_plan(ctypes.byref(s), 32, ctypes.byref(c), fake, lay.total, None,
+                                    ctypes.byref(n), None), B.E_INVALID),       # out NULL
+        (lambda: lib.lbsr_read_plan(ctypes.byref(s), 32, ctypes.byref(c), None, lay.total,
+                                    ctypes.byref(host), ctypes.byref(n), None), B.E_INVALID),
+        (lambda: lib.lbsr_read_plan(ctypes.byref(s), 32, ctypes.byref(c), ctypes.c_void_p((1 << 20) + 4),
+                                    lay.total, ctypes.byref(host), ctypes.byref(n), None),
+         B.E_INVALID),                                                           # misaligned
+        (lambda: lib.lbsr_read_plan(ctypes.byref(s), 32, ctypes.byref(c), fake, lay.total - 1,
+                                    ctypes.byref(host), ctypes.byref(n), None), B.E_WORKSPACE),
+        (lambda: lib.lbsr_read_plan(ctypes.byref(s), 0, ctypes.byref(c), fake, lay.total,
+                                    ctypes.byref(host), ctypes.byref(n), None), B.E_INVALID),
+        (lambda: lib.lbsr_read_device_error(fake, None, None), B.E_INVALID),    # code NULL
+        (lambda: lib.lbsr_read_device_error(None, ctypes.byref(n), None), B.E_INVALID),
+        (lambda: lib.lbsr_read_device_error(ctypes.c_void_p((1 << 20) + 8), ctypes.byref(n), None),
+         B.E_INVALID),
+    ]
+    for i, (call, want) in enumerate(cases):
+        assert call() == want, (i, lib.lbsr_last_error())
+        assert lib.lbsr_last_error() != b""
+
+
+def test_plan_host_struct_matches_header():
+    """lbsr_plan_host: five host pointers in the header's order."""
+    assert [f for f, _ in B.PlanHost._fields_] == ["cu_tiles", "worker_chunk", "chunks",
+                                                   "seq_chunk", "seq_len_eff"]
+    assert ctypes.sizeof(B.PlanHost) == 5 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_stream_read_validates_before_any_launch(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    sink = ctypes.c_void_p(1 << 21)
+    for args, want in [((None, 1 << 15, 0, sink, None), B.E_INVALID),
+                       ((fake, 1 << 15, 0, None, None), B.E_INVALID),
+                       ((ctypes.c_void_p((1 << 20) + 8), 1 << 15, 0, sink, None), B.E_INVALID),
+                       ((fake, 0, 0, sink, None), B.E_INVALID),
+                       ((fake, (1 << 15) + 16, 0, sink, None), B.E_INVALID),
+                       ((fake, 1 << 15, -1, sink, None), B.E_INVALID)]:
+        assert lib.lbsr_stream_read(*args) == want, lib.lbsr_last_error()

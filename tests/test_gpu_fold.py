@@ -162,3 +162,34 @@ def test_folded_fp8_output(lens, Hq, Hkv, kv_dtype, workers):
     _, ro, rl = oracle_step(w, inp)
     check_output_fp8(res["out"].cpu().numpy(), ro, w.kv_dtype, out_scale)
     assert np.all(np.abs(to_f64(res["lse"]) - rl) <= 1e-4 + 1e-5 * np.abs(rl))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 4), (32, 16), (48, 12)])
+def test_folded_plan_reused_by_two_attention_calls(Hq, Hkv):
+    """One lbsr_plan, then lbsr_attention twice with the flag (as every layer
+    of a step would reuse one plan): the arrival counters must start from zero
+    again, so the second call merges its split sequences too.  Covers the
+    lockstep kernels (4 and 16 KV heads, one counter per pass) and the
+    per-wave form (12 KV heads on 8 waves)."""
+    from test_gpu_step import oracle_step
+    dev = device()
+    w = wl.custom([3000, 1, 640, 65, 2500], num_q_heads=Hq, num_kv_heads=Hkv, seed=28)
+    inp = wl.make_inputs(w)
+    _, ro, rl = oracle_step(w, inp)
+    g = to_device(inp, dev)
+    cfg = config_for(w, g)
+    sched = lb.Schedule("dynamic", num_workers=40, fold_merge=True)
+    res = run_step(w, g, sched)            # writes the new tokens; q_out for the calls below
+    check_output(to_f64(res["out"]), ro, w.kv_dtype, "step output")
+    ws = lb.alloc_workspace(cfg, w.batch, sched, device=dev)
+    lb.plan(cfg, g["seq_lens"], sched, ws)
+    for call in range(2):
+        out = torch.full_like(res["out"], float("nan"))
+        lse = torch.full_like(res["lse"], float("nan"))
+        lb.attention(cfg, res["q_out"], g["k_cache"], g["v_cache"], g["block_table"], sched, ws,
+                     out, lse)
+        torch.cuda.synchronize()
+        check_output(to_f64(out), ro, w.kv_dtype, f"attention call {call}")
+        assert np.all(np.abs(to_f64(lse) - rl) <= 1e-4 + 1e-5 * np.abs(rl)), call
+        assert torch.equal(out, res["out"]) and torch.equal(lse, res["lse"]), call
+    assert lb.read_error(cfg, w.batch, sched, ws) == 0

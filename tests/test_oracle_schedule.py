@@ -120,6 +120,23 @@ def test_mixed_batch_figures():
     assert max(t1 - t0 for _, t0, t1, _ in static.chunks) == 256
 
 
+def test_loguniform_batch_figures():
+    """The log-uniform FP8 batch: 64 lengths rint(exp(U(ln 512, ln 262144))) from
+    default_rng(5) hold 2,771,856 tokens in 43,341 tiles; on 256 workers each
+    takes 169 or 170 tiles (43341 / 256 = 169.3), cut into 318 chunks, at most
+    25 of them in one sequence."""
+    from load_balanced_split_rope_amd import workloads as wl
+    lens = wl.named("loguniform").seq_lens
+    assert len(lens) == 64 and min(lens) >= 512 and max(lens) <= 262144
+    assert sum(lens) == 2771856
+    plan = plan_dynamic(lens, 256)
+    assert plan.cu_tiles[-1] == 43341
+    loads = np.bincount(plan.chunks[:, 3], weights=plan.chunks[:, 2] - plan.chunks[:, 1], minlength=256)
+    assert loads.min() == 169 and loads.max() == 170
+    assert plan.num_chunks == 318
+    assert np.diff(plan.seq_chunk).max() == 25
+
+
 def test_uniform_batch_dynamic_equals_static():
     """With equal lengths both schedules give the same chunks (the control case)."""
     lens = [4096] * 32

@@ -15,7 +15,7 @@ import oracle
 from oracle import step as ostep
 from load_balanced_split_rope_amd import workloads as wl
 from checks import (poison_cache, host_pools, host_step_inputs, oracle_cfg,
-                    check_output)
+                    check_output, check_output_fp8, FP8_ATOL)
 
 
 def run_oracle(w, inp, plan_kind=("dynamic", 3)):
@@ -158,3 +158,56 @@ def test_mutation_dropped_tile_moves_lse_beyond_fp32_noise():
     short = oracle.decode_attention(zero_q, pools, None, lens_short, h["block_table"], cfg)
     assert abs(full[(0, 0)][1] - np.log(4160)) < 1e-12
     assert abs(full[(0, 0)][1] - short[(0, 0)][1]) > 100 * np.finfo(np.float32).eps * np.log(4160)
+
+
+# -------------------------------------------- long sequences, FP8 checks
+# At 131072 rows of N(0,1) values |o| is about 1.5e-2, below the FP8 cache's
+# elementwise bound of 6e-2: that bound alone would pass an all-zero output.
+# The relative-L2 gate is what makes the FP8 checks discriminate there.
+
+@pytest.fixture(scope="module")
+def long_fp8():
+    w = wl.custom([131072], num_q_heads=8, num_kv_heads=1, kv_dtype="fp8", seed=13)
+    inp = wl.make_inputs(w)
+    h, pools, pro, cfg, full = run_oracle(w, inp)
+    ref = np.stack([full[(0, hh)][0] for hh in range(8)])
+    return {"w": w, "inp": inp, "h": h, "pools": pools, "pro": pro, "cfg": cfg, "ref": ref}
+
+
+def test_long_fp8_output_is_below_the_elementwise_bound(long_fp8):
+    ref = long_fp8["ref"]
+    assert np.abs(ref).max() < FP8_ATOL
+    # so a zero output meets the elementwise bound: only the L2 gate can fail it
+    assert np.abs(np.zeros_like(ref) - ref).max() <= FP8_ATOL
+
+
+def test_mutation_long_fp8_zero_scaled_or_wrong_v_output_fails(long_fp8):
+    ref = long_fp8["ref"]
+    # positive control: the result as a BF16 store of it passes
+    good = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(ref))
+    check_output(good, ref, "fp8")
+    for bad in (np.zeros_like(ref), 0.5 * ref):
+        with pytest.raises(AssertionError):
+            check_output(bad, ref, "fp8")
+    # V read from the wrong pages: every V page moved one slot along the pool
+    kp, vp = long_fp8["pools"]
+    inp, h = long_fp8["inp"], long_fp8["h"]
+    rolled = np.roll(vp.reshape(inp["num_pages"], -1), 1, axis=0).reshape(-1)
+    wrong = oracle.decode_attention(long_fp8["pro"]["q_out"], (kp, rolled), long_fp8["pro"],
+                                    h["seq_lens"], h["block_table"], long_fp8["cfg"])
+    bad = np.stack([wrong[(0, hh)][0] for hh in range(8)])
+    assert np.abs(bad - ref).max() <= FP8_ATOL
+    with pytest.raises(AssertionError):
+        check_output(bad, ref, "fp8")
+
+
+def test_mutation_long_fp8_output_codes_fail(long_fp8):
+    """E4M3 output (scale 2^-7): the exact encoding passes; zero codes, codes of
+    half the result and codes of the wrong-V result fail the L2 gate."""
+    ref = long_fp8["ref"]
+    out_scale = 2.0 ** -7
+    check_output_fp8(oracle.encode_output(ref, "fp8", out_scale), ref, "fp8", out_scale)
+    for bad in (np.zeros_like(ref), 0.5 * ref, -ref[::-1]):
+        codes = oracle.encode_output(bad, "fp8", out_scale)
+        with pytest.raises(AssertionError):
+            check_output_fp8(codes, ref, "fp8", out_scale)
