@@ -461,6 +461,33 @@ lbsr_status lbsr_decode_step_timed(const lbsr_shape *shape, const lbsr_params *p
                                    size_t ws_bytes, void *out, float *lse_out,
                                    void *stream, float *kernel_ms, int64_t *trace);
 
+/*
+ * The decode step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * lbsr_decode_step with the same arguments minus the workspace.  The
+ * workspace lives in a scratch array of LBSR_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on, from its first use there until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); it fails with LBSR_E_WORKSPACE, launching nothing, when
+ * the step's workspace (lbsr_workspace_size) would exceed the scratch -- e.g.
+ * the 1 x 128K + 31 x 4K batch needs about 9.5 MB, a 4-token step of it about
+ * 38 MB.  All calls on one GPU share its scratch, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads) race
+ * and must be ordered by the caller.  The schedule launch rewrites every
+ * array the later launches read, so nothing carries over between calls.  The
+ * device error bits are not readable from outside; callers that need them use
+ * lbsr_decode_step with their own workspace.
+ */
+#define LBSR_NOALLOC_SCRATCH_BYTES (32u << 20) /* 32 MiB per GPU */
+lbsr_status lbsr_decode_step_noalloc(const lbsr_shape *shape, const lbsr_params *params,
+                                     int32_t batch, const void *q, const void *k,
+                                     const void *v, const int32_t *positions,
+                                     const int32_t *seq_lens, const void *q_norm_w,
+                                     const void *k_norm_w, const int32_t *block_table,
+                                     void *k_cache, void *v_cache, void *q_out,
+                                     const lbsr_sched_cfg *cfg, void *out, float *lse_out,
+                                     void *stream);
+
 /* Host arrays lbsr_read_plan fills; any may be NULL to skip it.  Sizes come
  * from lbsr_workspace_layout for the same shape, batch and cfg. */
 typedef struct {

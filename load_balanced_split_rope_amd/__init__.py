@@ -12,7 +12,8 @@ from .decode import (DecodeConfig, Schedule, device_workers, workspace_layout,
                      decode_step_timed, read_plan, read_error, xcd_rates,
                      xcd_weights_from_rates, prefill_attention, prefill_step,
                      prefill_attention_varlen, prefill_step_varlen,
-                     prefill_workspace_size, alloc_prefill_workspace, stream_read)
+                     prefill_workspace_size, alloc_prefill_workspace, stream_read,
+                     decode_step_noalloc)
 
 __all__ = [
     "LbsrError", "LibraryNotBuilt", "EXPORTS", "LIB_PATH", "DecodeConfig", "Schedule",
@@ -20,4 +21,5 @@ __all__ = [
     "attention", "decode_step", "decode_step_timed", "read_plan", "read_error", "xcd_rates",
     "xcd_weights_from_rates", "prefill_attention", "prefill_step", "prefill_attention_varlen",
     "prefill_step_varlen", "prefill_workspace_size", "alloc_prefill_workspace", "stream_read",
+    "decode_step_noalloc",
 ]

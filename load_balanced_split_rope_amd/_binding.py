@@ -21,6 +21,7 @@ HEAD_DIM = 128
 PAGE_SIZE = 64
 TILE_ELEMS = HEAD_DIM * PAGE_SIZE
 NUM_XCDS = 8
+NOALLOC_SCRATCH_BYTES = 32 << 20   # LBSR_NOALLOC_SCRATCH_BYTES
 MAX_XCD_WEIGHT = 65536
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
@@ -38,7 +39,7 @@ EXPORTS = (
     "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed", "lbsr_prefill_attention",
     "lbsr_prefill_step", "lbsr_prefill_attention_varlen", "lbsr_prefill_step_varlen",
     "lbsr_prefill_workspace_size", "lbsr_read_plan", "lbsr_read_device_error",
-    "lbsr_stream_read",
+    "lbsr_stream_read", "lbsr_decode_step_noalloc",
 )
 
 
@@ -141,6 +142,8 @@ def _declare(lib):
                                 _P]),
         "lbsr_read_device_error": (st, [_P, ctypes.POINTER(_I32), _P]),
         "lbsr_stream_read": (st, [_P, ctypes.c_size_t, _I32, _P, _P]),
+        "lbsr_decode_step_noalloc": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
+                                     + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -522,6 +522,38 @@ lbsr_status validate_uniform_workspace(const lbsr_shape* shape, int32_t batch, v
 
 }  // namespace
 
+// ---- scratch for the step that allocates nothing (lbsr_decode_step_noalloc) ----
+// One file-scope device array per GPU holds that call's workspace.  In host
+// code `scratch` is only a stand-in for the symbol: its device address comes
+// from hipGetSymbolAddress, once per device with that device current, and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[LBSR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mutex;
+
+lbsr_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LBSR_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LBSR_E_INVALID, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LBSR_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LBSR_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t lbsr_abi_version(void) { return LBSR_ABI_VERSION; }
@@ -772,6 +804,31 @@ lbsr_status lbsr_decode_step(const lbsr_shape* shape, const lbsr_params* params,
   return decode_step_impl(shape, params, batch, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
                           block_table, k_cache, v_cache, q_out, cfg, workspace, ws_bytes, out,
                           lse_out, stream, nullptr, nullptr);
+}
+
+lbsr_status lbsr_decode_step_noalloc(const lbsr_shape* shape, const lbsr_params* params,
+                                     int32_t batch, const void* q, const void* k, const void* v,
+                                     const int32_t* positions, const int32_t* seq_lens,
+                                     const void* q_norm_w, const void* k_norm_w,
+                                     const int32_t* block_table, void* k_cache, void* v_cache,
+                                     void* q_out, const lbsr_sched_cfg* cfg, void* out,
+                                     float* lse_out, void* stream) {
+  g_last_error[0] = 0;
+  lbsr_ws_layout l;
+  LBSR_CHECK(compute_layout(shape, batch, cfg, &l));
+  if (l.total > (size_t)LBSR_NOALLOC_SCRATCH_BYTES)
+    return fail(LBSR_E_WORKSPACE,
+                "this step needs %zu bytes of workspace; the library's scratch holds %zu "
+                "(use lbsr_decode_step with a caller workspace)",
+                l.total, (size_t)LBSR_NOALLOC_SCRATCH_BYTES);
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  void* ws = nullptr;
+  LBSR_CHECK(scratch_of_current_device(&ws));
+  return decode_step_impl(shape, params, batch, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
+                          block_table, k_cache, v_cache, q_out, cfg, ws,
+                          (size_t)LBSR_NOALLOC_SCRATCH_BYTES, out, lse_out, stream, nullptr,
+                          nullptr);
 }
 
 lbsr_status lbsr_decode_step_timed(const lbsr_shape* shape, const lbsr_params* params,

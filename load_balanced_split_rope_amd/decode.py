@@ -216,13 +216,15 @@ def _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_tabl
         _need(lse_out, "lse_out", torch.float32, shape=cfg.tokens_shape(batch, Hq))
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
-    _need(workspace, "workspace", torch.uint8)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
     s, p, c = cfg.shape(), cfg.params(), sched.cfg()
-    return (ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
+    head = (ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
             B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
             B._ptr(block_table), B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out),
-            ctypes.byref(c), B._ptr(workspace), workspace.numel(), B._ptr(out),
-            B._ptr(lse_out)), (s, p, c)
+            ctypes.byref(c))
+    ws = () if workspace is None else (B._ptr(workspace), workspace.numel())
+    return head + ws + (B._ptr(out), B._ptr(lse_out)), (s, p, c)
 
 
 def decode_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table,
@@ -232,6 +234,18 @@ def decode_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_nor
     args, keep = _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table,
                             k_cache, v_cache, q_out, sched, workspace, out, lse_out)
     B._check(B.lib().lbsr_decode_step(*args, B._stream(stream)))
+    del keep
+
+
+def decode_step_noalloc(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_norm_w,
+                        block_table, k_cache, v_cache, q_out, sched: Schedule, out, lse_out=None,
+                        stream=None):
+    """lbsr_decode_step_noalloc: the decode step with the library's own per-GPU
+    scratch as its workspace (for callers that cannot allocate).  Raises
+    LbsrError (LBSR_E_WORKSPACE) when the step needs more than the scratch."""
+    args, keep = _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_table,
+                            k_cache, v_cache, q_out, sched, None, out, lse_out)
+    B._check(B.lib().lbsr_decode_step_noalloc(*args, B._stream(stream)))
     del keep
 
 

@@ -401,3 +401,21 @@ def test_stream_read_validates_before_any_launch(lib):
                        ((fake, (1 << 15) + 16, 0, sink, None), B.E_INVALID),
                        ((fake, 1 << 15, -1, sink, None), B.E_INVALID)]:
         assert lib.lbsr_stream_read(*args) == want, lib.lbsr_last_error()
+
+
+def test_noalloc_step_refuses_beyond_its_scratch_before_any_launch(lib):
+    """lbsr_decode_step_noalloc: a step whose workspace exceeds the library's
+    scratch (4096 sequences: about 142 MB) is refused with LBSR_E_WORKSPACE
+    on the host, before any pointer is touched or kernel launched."""
+    s = cfg_mix().shape()
+    p = cfg_mix().params()
+    c = Schedule("dynamic", num_workers=256).cfg()
+    lay = workspace_layout(cfg_mix(), 4096, Schedule("dynamic", num_workers=256))
+    assert lay.total > B.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x10000)
+    got = lib.lbsr_decode_step_noalloc(ctypes.byref(s), ctypes.byref(p), 4096, *([fake] * 11),
+                                       ctypes.byref(c), fake, fake, None)
+    assert got == B.E_WORKSPACE and b"scratch" in lib.lbsr_last_error()
+    # the mix itself fits
+    assert workspace_layout(cfg_mix(), 32, Schedule("dynamic", num_workers=256)).total \
+        <= B.NOALLOC_SCRATCH_BYTES
