@@ -388,30 +388,40 @@ def cpu_baseline(w, dev, min_seconds=10.0):
                            "seconds": round(dt1, 2)}}
 
 
-def stream_ceiling(dev, nbytes=1 << 30, reps=10):
-    """The streaming-read probe over 1 GiB (the split kernel's load pattern,
-    one 8-wave workgroup per CU): median GB/s over ``reps`` launches timed
-    with HIP events on the launch stream."""
+def stream_ceiling(dev, nbytes=1 << 30, launches=10):
+    """The streaming-read ceiling over 1 GiB: the probe (lbsr_stream_read) in
+    the split kernel's load pattern and as a plain sweep, over a few grid
+    sizes; each timed as `launches` back-to-back launches between two HIP
+    events on the launch stream (the median of three such runs).  The best
+    rate is the ceiling; every variant is reported."""
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
     st = torch.cuda.current_stream()
-    for _ in range(2):
-        lb.stream_read(buf, sink)
-    ms = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        lb.stream_read(buf, sink)
-        e1.record(st)
-        e1.synchronize()
-        ms.append(e0.elapsed_time(e1))
+    P = lb.device_workers(0)
+    variants = [(0, P), (0, 2 * P), (1, 4 * P), (1, 8 * P)]
+    rows = []
+    for mode, wg in variants:
+        for _ in range(2):
+            lb.stream_read(buf, sink, wg, mode)
+        runs = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(launches):
+                lb.stream_read(buf, sink, wg, mode)
+            e1.record(st)
+            e1.synchronize()
+            runs.append(e0.elapsed_time(e1) / launches)
+        ms = float(np.median(runs))
+        rows.append({"mode": "split-kernel pattern (32 KiB bursts, waves in lockstep)" if mode == 0
+                     else "plain sweep (8 loads in flight per thread)",
+                     "workgroups": wg, "us_per_GiB": round(ms * 1e3, 2),
+                     "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
     del buf, sink
     torch.cuda.empty_cache()
-    med = float(np.median(ms))
-    return {"bytes": nbytes, "us": round(med * 1e3, 2), "GBs": round(nbytes / (med * 1e-3) / 1e9, 1),
-            "launches": reps,
-            "pattern": "non-temporal 16-byte loads, one 32 KiB burst per wave, 8 waves per "
-                       "workgroup, one workgroup per CU"}
+    best = max(rows, key=lambda r: r["GBs"])
+    return {"bytes": nbytes, "GBs": best["GBs"], "best": best, "variants": rows,
+            "timing": f"{launches} back-to-back launches between HIP events, median of 3"}
 
 
 def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_dtype="bf16"):

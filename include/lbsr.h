@@ -521,15 +521,18 @@ lbsr_status lbsr_read_device_error(const void *workspace, int32_t *code, void *s
 
 /*
  * Benchmark helper, not an operation of the method: reads `bytes` (a positive
- * multiple of 32 KiB) of device memory at `buf` (16-byte aligned) the way the
- * split-attention kernel reads K/V tiles -- non-temporal 16-byte loads, one
- * 32 KiB burst per wave, 8 waves per workgroup, `workgroups` workgroups (0 ->
- * the device's CU count) -- and writes one checksum word per workgroup to
- * `sink` (device, uint32[workgroups]).  Its rate is the streaming ceiling the
- * split kernel's bandwidth is reported against.  Asynchronous on `stream`.
+ * multiple of 32 KiB) of device memory at `buf` (16-byte aligned) with
+ * non-temporal 16-byte loads, in `workgroups` workgroups of 8 waves (0 -> the
+ * device's CU count), and writes one checksum word per workgroup to `sink`
+ * (device, uint32[workgroups]).  mode 0 reads the way the split-attention
+ * kernel reads K/V tiles: one 32 KiB burst per wave, the 8 waves meeting at a
+ * barrier after each burst is issued.  mode 1 is a plain sweep: every thread
+ * keeps 8 loads in flight, one grid-width apart, with no barriers.  The best
+ * rate over modes and grid sizes is the streaming ceiling the split kernel's
+ * bandwidth is reported against.  Asynchronous on `stream`.
  */
-lbsr_status lbsr_stream_read(const void *buf, size_t bytes, int32_t workgroups, uint32_t *sink,
-                             void *stream);
+lbsr_status lbsr_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t mode,
+                             uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

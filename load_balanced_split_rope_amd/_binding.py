@@ -141,7 +141,7 @@ def _declare(lib):
                                 ctypes.c_size_t, ctypes.POINTER(PlanHost), ctypes.POINTER(_I32),
                                 _P]),
         "lbsr_read_device_error": (st, [_P, ctypes.POINTER(_I32), _P]),
-        "lbsr_stream_read": (st, [_P, ctypes.c_size_t, _I32, _P, _P]),
+        "lbsr_stream_read": (st, [_P, ctypes.c_size_t, _I32, _I32, _P, _P]),
         "lbsr_decode_step_noalloc": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                                      + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, _P, _P]),
     }

@@ -880,8 +880,8 @@ lbsr_status lbsr_read_plan(const lbsr_shape* shape, int32_t batch, const lbsr_sc
   return LBSR_OK;
 }
 
-lbsr_status lbsr_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
-                             void* stream) {
+lbsr_status lbsr_stream_read(const void* buf, size_t bytes, int32_t workgroups, int32_t mode,
+                             uint32_t* sink, void* stream) {
   g_last_error[0] = 0;
   LBSR_CHECK(check_ptr(buf, 16, "buf"));
   LBSR_CHECK(check_ptr(sink, 4, "sink"));
@@ -891,10 +891,11 @@ lbsr_status lbsr_stream_read(const void* buf, size_t bytes, int32_t workgroups, 
                 (long long)blk);
   if (workgroups < 0 || workgroups > (1 << 20))
     return fail(LBSR_E_INVALID, "workgroups %d outside [0, 2^20]", workgroups);
+  if (mode != 0 && mode != 1) return fail(LBSR_E_INVALID, "mode %d is not 0 or 1", mode);
   DeviceInfo d;
   LBSR_CHECK(current_device(&d));
   const int wg = workgroups ? workgroups : d.cu_count;
-  return hip_status(lbsr::launch_stream_read(buf, bytes, wg, sink, (hipStream_t)stream),
+  return hip_status(lbsr::launch_stream_read(buf, bytes, wg, mode, sink, (hipStream_t)stream),
                     "stream_read_kernel launch");
 }
 

@@ -63,9 +63,10 @@ hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 double k_scale, double v_scale, hipStream_t stream);
 
 // Streaming-read probe (measurement only): `bytes` must be a multiple of
-// stream_read_block_bytes(); sink holds one word per workgroup.
+// stream_read_block_bytes(); sink holds one word per workgroup.  mode 0: the
+// split kernel's load pattern; 1: a plain grid-wide sweep.
 int64_t stream_read_block_bytes();
-hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
-                              hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, int mode,
+                              uint32_t* sink, hipStream_t stream);
 
 }  // namespace lbsr

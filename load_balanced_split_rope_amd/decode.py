@@ -441,15 +441,15 @@ def read_error(cfg: DecodeConfig, batch: int, sched: Schedule, workspace, stream
     return int(code.value)
 
 
-def stream_read(buf, sink, workgroups=0, stream=None):
+def stream_read(buf, sink, workgroups=0, mode=0, stream=None):
     """The streaming-read probe (lbsr_stream_read): reads all of ``buf`` (a
-    device tensor whose size is a multiple of 32 KiB) with the split kernel's
-    load pattern; ``sink`` is a device uint32-sized buffer of at least
-    ``workgroups`` (or CU count) words.  Asynchronous."""
+    device tensor whose size is a multiple of 32 KiB); ``sink`` is a device
+    buffer of at least ``workgroups`` (or CU count) 32-bit words.  mode 0: the
+    split kernel's load pattern; 1: a plain grid-wide sweep.  Asynchronous."""
     if buf.device.type != "cuda" or sink.device.type != "cuda":
         raise ValueError("stream_read needs device tensors")
-    B._check(B.lib().lbsr_stream_read(B._ptr(buf), _nbytes(buf), int(workgroups), B._ptr(sink),
-                                      B._stream(stream)))
+    B._check(B.lib().lbsr_stream_read(B._ptr(buf), _nbytes(buf), int(workgroups), int(mode),
+                                      B._ptr(sink), B._stream(stream)))
 
 
 def xcd_rates(traces, plans):

@@ -394,12 +394,13 @@ def test_plan_host_struct_matches_header():
 def test_stream_read_validates_before_any_launch(lib):
     fake = ctypes.c_void_p(1 << 20)
     sink = ctypes.c_void_p(1 << 21)
-    for args, want in [((None, 1 << 15, 0, sink, None), B.E_INVALID),
-                       ((fake, 1 << 15, 0, None, None), B.E_INVALID),
-                       ((ctypes.c_void_p((1 << 20) + 8), 1 << 15, 0, sink, None), B.E_INVALID),
-                       ((fake, 0, 0, sink, None), B.E_INVALID),
-                       ((fake, (1 << 15) + 16, 0, sink, None), B.E_INVALID),
-                       ((fake, 1 << 15, -1, sink, None), B.E_INVALID)]:
+    for args, want in [((None, 1 << 15, 0, 0, sink, None), B.E_INVALID),
+                       ((fake, 1 << 15, 0, 0, None, None), B.E_INVALID),
+                       ((ctypes.c_void_p((1 << 20) + 8), 1 << 15, 0, 0, sink, None), B.E_INVALID),
+                       ((fake, 0, 0, 0, sink, None), B.E_INVALID),
+                       ((fake, (1 << 15) + 16, 0, 0, sink, None), B.E_INVALID),
+                       ((fake, 1 << 15, -1, 0, sink, None), B.E_INVALID),
+                       ((fake, 1 << 15, 0, 2, sink, None), B.E_INVALID)]:
         assert lib.lbsr_stream_read(*args) == want, lib.lbsr_last_error()
 
 
