@@ -90,9 +90,44 @@ __device__ inline double bf16_to_f64(uint16_t b) {
   return (double)__uint_as_float((uint32_t)b << 16);
 }
 
+// One fp64 value moved across lanes by a DPP pattern (both halves alike).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, kCtrl, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), kCtrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wave, every lane receiving it: the xor butterfly at distances
+// 32, 16, 8, 4, 2, 1 (each lane adds its partner's value; the two partners
+// add the same pair, so they stay equal).  No step goes through LDS:
+// distances 32 and 16 use gfx950's permlane swaps (their two outputs are the
+// lower and the upper lane's value), 8 and 4 a rotation inside the 16-lane
+// row (by 8 it is the xor; by 4 it matches the xor once the values repeat
+// every 8 lanes), 2 and 1 a quad permutation.
 __device__ inline double wave_sum_f64(double x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+#pragma clang fp contract(off)
+  {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32),
+                                                     false, false);
+    x = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+        __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+  }
+  {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32),
+                                                     false, false);
+    x = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]) +
+        __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+  }
+  x = x + dpp_f64<0x128>(x);   // row_ror:8
+  x = x + dpp_f64<0x124>(x);   // row_ror:4
+  x = x + dpp_f64<0x4E>(x);    // quad_perm [2,3,0,1]
+  x = x + dpp_f64<0xB1>(x);    // quad_perm [1,0,3,2]
   return x;
 }
 
