@@ -33,9 +33,10 @@
  *   - Array pointers are DEVICE pointers unless a comment says "host".
  *     `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - The caller owns and allocates every buffer (inputs, outputs, caches,
- *     workspace).  The library allocates no device memory, keeps no pointer
- *     after a call returns, and launches asynchronously on `stream`; buffers
- *     must stay alive until the stream has passed the launch.
+ *     workspace).  The library allocates no device memory (the one static
+ *     device array it holds is the scratch of lbsr_decode_step_noalloc),
+ *     keeps no pointer after a call returns, and launches asynchronously on
+ *     `stream`; buffers must stay alive until the stream has passed the launch.
  *   - Host-side validation happens before any launch; on failure nothing is
  *     launched, a status is returned and lbsr_last_error() holds a message.
  *   - No entry point synchronises, except lbsr_decode_step_timed (bench) and
