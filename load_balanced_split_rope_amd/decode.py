@@ -342,7 +342,7 @@ def alloc_prefill_workspace(cfg: DecodeConfig, batch: int, total_tokens: int, de
 
 
 def _nbytes(t):
-    return 0 if t is None else t.numel()
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _check_varlen(cfg, q_start, batch, total, workspace):
@@ -448,6 +448,11 @@ def stream_read(buf, sink, workgroups=0, mode=0, stream=None):
     split kernel's load pattern; 1: a plain grid-wide sweep.  Asynchronous."""
     if buf.device.type != "cuda" or sink.device.type != "cuda":
         raise ValueError("stream_read needs device tensors")
+    if sink.dtype not in (torch.int32, torch.uint32) or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous int32 or uint32 tensor")
+    n = int(workgroups) or device_workers(buf.device.index or 0)
+    if sink.numel() < n:
+        raise ValueError(f"sink holds {sink.numel()} words; the probe writes one per workgroup ({n})")
     B._check(B.lib().lbsr_stream_read(B._ptr(buf), _nbytes(buf), int(workgroups), int(mode),
                                       B._ptr(sink), B._stream(stream)))
 
