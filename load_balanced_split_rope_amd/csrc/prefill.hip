@@ -345,15 +345,22 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
 }
 
 // The work list of a prefill (ragged, or uniform with q_start null): every
-// (sequence, block of new tokens) with at
-// least one token, sorted by its tile count (the rows its last token attends,
-// in 64-row tiles), longest first -- a counting sort over tile-count buckets
-// (tiles >> shift), in one 1024-thread workgroup: per-sequence item counts
-// and their prefix sums in LDS (batch + 1 ints), then thread t takes items
-// t, t + 1024, ... (its sequence by binary search over the prefix sums).  Layout of `work`: [0] item
-// count, then from byte kPrefillListOffset int2 (sequence, block) pairs, at
-// most max_items of them.  Order within a bucket is arrival order; it decides
-// only which workgroup runs an item, not any result.
+// (sequence, block of new tokens) with at least one token, grouped by
+// sequence and longest first.  A sequence's key is its longest item's tile
+// count (the rows its last token attends, in 64-row tiles); a counting sort
+// over key buckets (tiles >> shift) orders the sequences longest first, and
+// each sequence's items follow each other from its last block (the longest)
+// down to its first.  The blocks of one sequence read the same prefix tiles,
+// and the attention grid puts an item's KV heads on consecutive workgroups
+// (head h of every item on the same XCD when Hkv = 8), so neighbouring items
+// of one sequence meet in their XCD's L2.  One 1024-thread workgroup:
+// per-sequence item counts, their prefix sums and each sequence's first slot
+// in LDS (2 batch + 1 ints); thread t places items t, t + 1024, ... (its
+// sequence by binary search over the prefix sums).  Layout of `work`: [0]
+// item count, then from byte kPrefillListOffset int2 (sequence, block)
+// pairs, at most max_items of them.  The order of sequences within a bucket
+// is arrival order; it decides only which workgroup runs an item, not any
+// result.
 __device__ inline bool ragged_range(const int32_t* q_start, const int32_t* seq_lens, int b,
                                     int total_tokens, int bound, int max_len, int& T, int& L) {
   // no q_start: every sequence has `bound` new tokens (the uniform call)
@@ -370,27 +377,32 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     Geometry geo, const int32_t* __restrict__ q_start, const int32_t* __restrict__ seq_lens,
     int total_tokens, int32_t* __restrict__ work, int max_items, int shift,
     int32_t* __restrict__ error_word) {
-  extern __shared__ int s_cu[];                     // batch + 1: items before each sequence
+  extern __shared__ int s_dyn[];
+  int* s_cu = s_dyn;                                // batch + 1: items before each sequence
+  int* s_first = s_dyn + geo.batch + 1;             // batch: each sequence's first list slot
   __shared__ int s_bucket[kPrefillBuckets];
   __shared__ int s_wave[kPlanThreads / kWave + 1];
   const int tid = threadIdx.x, B = geo.batch;
   const int tpb = kPrefillColumns / geo.group;
   const int max_len = geo.max_blocks * kPage;
-  auto bucket_of = [&](int T, int L, int qb) {
-    const int tok_end = (qb + 1) * tpb < T ? (qb + 1) * tpb : T;
-    const int tiles = (L - T + tok_end + kPage - 1) / kPage;
+  // bucket of a sequence with T new tokens and L rows: its longest item's tile count
+  auto bucket_of = [&](int T, int L) {
+    const int tiles = (L + kPage - 1) / kPage;      // the last new token attends all L rows
     const int k = tiles >> shift;
     return kPrefillBuckets - 1 - (k < kPrefillBuckets ? k : kPrefillBuckets - 1);  // longest first
   };
   // items (blocks of new tokens) per sequence; none for a malformed range
   bool bad = false;
+  for (int i = tid; i < kPrefillBuckets; i += kPlanThreads) s_bucket[i] = 0;
+  __syncthreads();
   for (int b = tid; b < B; b += kPlanThreads) {
     int T, L;
     const bool ok = ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L);
     bad |= !ok;
-    s_cu[b] = ok ? (T + tpb - 1) / tpb : 0;
+    const int n = ok ? (T + tpb - 1) / tpb : 0;
+    s_cu[b] = n;
+    if (n > 0) atomicAdd(&s_bucket[bucket_of(T, L)], n);
   }
-  for (int i = tid; i < kPrefillBuckets; i += kPlanThreads) s_bucket[i] = 0;
   __syncthreads();
   int carry = 0;                                    // exclusive prefix sums, 1024 at a time
   for (int base = 0; base < B; base += kPlanThreads) {
@@ -402,26 +414,6 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     carry += sum;
   }
   if (tid == 0) s_cu[B] = carry;
-  __syncthreads();
-  const int N = carry;
-  // item i -> (sequence, block): the last b with s_cu[b] <= i (empty sequences skipped)
-  auto locate = [&](int i, int& b, int& qb, int& T, int& L) {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_cu[mid] <= i) lo = mid;
-      else hi = mid - 1;
-    }
-    b = lo;
-    qb = i - s_cu[b];
-    ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L);
-  };
-  for (int i = tid; i < N; i += kPlanThreads) {
-    int b, qb, T, L;
-    locate(i, b, qb, T, L);
-    atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
-  }
-  __syncthreads();
   // exclusive offsets over the buckets: thread t owns buckets [4t, 4t + 4)
   constexpr int kPer = kPrefillBuckets / kPlanThreads;
   int local = 0;
@@ -436,11 +428,28 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     off += c;
   }
   __syncthreads();
+  const int N = carry;
+  // each sequence takes a run of slots in its bucket
+  for (int b = tid; b < B; b += kPlanThreads) {
+    const int n = s_cu[b + 1] - s_cu[b];
+    if (n > 0) {
+      int T, L;
+      ragged_range(q_start, seq_lens, b, total_tokens, geo.tokens, max_len, T, L);
+      s_first[b] = atomicAdd(&s_bucket[bucket_of(T, L)], n);
+    }
+  }
+  __syncthreads();
+  // item i -> (sequence, block): the last b with s_cu[b] <= i (empty sequences skipped)
   int2* list = (int2*)((char*)work + kPrefillListOffset);
   for (int i = tid; i < N; i += kPlanThreads) {
-    int b, qb, T, L;
-    locate(i, b, qb, T, L);
-    const int pos = atomicAdd(&s_bucket[bucket_of(T, L, qb)], 1);
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_cu[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = lo, qb = i - s_cu[b], n = s_cu[b + 1] - s_cu[b];
+    const int pos = s_first[b] + (n - 1 - qb);      // the sequence's last block first
     if (pos < max_items) list[pos] = make_int2(b, qb);
   }
   // overlapping ranges (a malformed q_start) can give more items than the list holds
@@ -471,7 +480,7 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
     const int max_items = prefill_max_items(geo, total_tokens);
     int shift = 0;
     while ((geo.max_blocks >> shift) >= kPrefillBuckets) ++shift;
-    const size_t lds = sizeof(int) * ((size_t)geo.batch + 1);
+    const size_t lds = sizeof(int) * (2 * (size_t)geo.batch + 1);
     prefill_plan_kernel<<<1, kPlanThreads, lds, stream>>>(geo, q_start, seq_lens, total_tokens,
                                                            work, max_items, shift, error_word);
     grid = (size_t)max_items * geo.num_kv_heads;
