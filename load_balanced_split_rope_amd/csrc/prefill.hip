@@ -458,6 +458,12 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     atomicOr(error_word, (int32_t)kErrQueryStart);
 }
 
+// The plan's LDS at the batch limit: counts and prefix sums (batch + 1), first
+// slots (batch), the buckets and the scan's per-wave sums, within gfx950's 160 KiB.
+static_assert(sizeof(int) * ((2 * (size_t)kMaxBatch + 1) + kPrefillBuckets +
+                             (kPlanThreads / kWave + 1)) <= 160 * 1024,
+              "prefill plan LDS exceeds 160 KiB at kMaxBatch");
+
 int prefill_blocks_q(const Geometry& geo) {
   const int per = kPrefillColumns / geo.group;
   return (geo.tokens + per - 1) / per;
