@@ -354,9 +354,9 @@ lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
  *   lse_out nullable float[batch][Tq][Hq]  error_word nullable int32*
  *   workspace nullable: lbsr_prefill_workspace_size(shape, batch, batch * Tq)
  *     bytes, 256-byte aligned, caller-owned, overwritten by each call.  With
- *     it, a first launch sorts the (sequence, block) work items by the rows
- *     they attend, longest first, and the attention runs in that order (as
- *     the ragged call does); without it the grid runs blocks of the last new
+ *     it, a first launch lists the (sequence, block) work items longest first
+ *     (grouped by sequence, as the ragged call does) and the attention runs
+ *     in that order; without it the grid runs blocks of the last new
  *     tokens first, which is the same order only when every sequence has
  *     the same length.  Workgroups reach compute units in a fixed rotation,
  *     so with unequal lengths the sorted order is much faster (2.1x with one
@@ -398,9 +398,12 @@ lbsr_status lbsr_prefill_step(const lbsr_shape *shape, const lbsr_params *params
  * workspace: device memory of lbsr_prefill_workspace_size bytes (required here),
  * 256-byte aligned, caller-owned, overwritten by every call (so calls that
  * share one must be ordered).  A first launch writes there the list of
- * (sequence, block of 256/G new tokens) work items sorted by the rows they
- * attend, longest first; the attention launch runs one workgroup per (item,
- * KV head) in that order.  (Workgroups reach compute units in a fixed
+ * (sequence, block of 256/G new tokens) work items grouped by sequence: the
+ * sequences by the rows their longest item attends, longest first, and each
+ * sequence's items from its last block (the longest) down, so that blocks
+ * which read the same prefix tiles run side by side and share them in L2.
+ * The attention launch runs one workgroup per (item, KV head) in that
+ * order.  (Workgroups reach compute units in a fixed
  * rotation by index: a grid ordered by sequence, or holding empty blocks,
  * binds CUs to the same few sequences and idles the rest.)  A sequence whose q_start range is
  * malformed (negative, decreasing, past total_tokens, or n_b above the bound)

@@ -116,6 +116,44 @@ def test_equal_counts_match_uniform_call():
     assert torch.equal(rv["lse"].view(lse.shape), lse)
 
 
+def test_work_list_is_grouped_by_sequence_longest_first():
+    """The plan's work list, read from the workspace (white box: the item
+    count in its first word, (sequence, block) int32 pairs from byte 256):
+    every item once; each sequence's items contiguous, from its last block
+    (the longest) down; sequences ordered by their longest item's tile count,
+    longest first.  The order decides only which workgroup runs an item, not
+    any result; this pins the grouping that lets the blocks of one sequence
+    share its prefix tiles in L2."""
+    dev = device()
+    lens = [300, 5, 700, 64, 1, 4096, 2000, 129, 4160, 33]
+    counts = [300, 0, 33, 1, 1, 1000, 64, 129, 65, 33]
+    w = wl.custom(lens, seed=890, new_tokens=counts)
+    g = to_device(wl.make_inputs(w), dev)
+    cfg = config_for(w, g)
+    ws = lb.alloc_prefill_workspace(cfg, len(lens), g["q"].shape[0], device=dev)
+    q_out = torch.empty_like(g["q"])
+    out = torch.zeros(g["q"].shape, dtype=cfg.out_torch_dtype, device=dev)
+    lb.prefill_step_varlen(cfg, g["q_start"], g["q"], g["k"], g["v"], g["positions"],
+                           g["seq_lens"], g["q_norm_w"], g["k_norm_w"], g["block_table"],
+                           g["k_cache"], g["v_cache"], q_out, ws, out)
+    torch.cuda.synchronize()
+    words = ws.cpu().numpy().view(np.int32)
+    tpb = 256 // (w.num_q_heads // w.num_kv_heads)
+    items = [-(-n // tpb) for n in counts]
+    n = int(words[0])
+    assert n == sum(items)
+    lst = words[64:64 + 2 * n].reshape(n, 2)
+    assert sorted(map(tuple, lst.tolist())) == sorted((b, q) for b in range(len(lens))
+                                                     for q in range(items[b]))
+    first = {}
+    for pos, (b, q) in enumerate(lst.tolist()):
+        first.setdefault(b, pos)
+        assert pos == first[b] + (items[b] - 1 - q), (pos, b, q)   # contiguous, last block first
+    order = sorted(first, key=first.get)
+    keys = [-(-lens[b] // 64) for b in order]
+    assert keys == sorted(keys, reverse=True), (order, keys)
+
+
 def test_mixed_batch_decode_and_prefill():
     """Sequences 0-2 decode one token (split-KV decode step, dynamic schedule);
     sequences 3-4 prefill a chunk (ragged prefill); one cache, one stream."""
