@@ -420,3 +420,56 @@ def test_noalloc_step_refuses_beyond_its_scratch_before_any_launch(lib):
     # the mix itself fits
     assert workspace_layout(cfg_mix(), 32, Schedule("dynamic", num_workers=256)).total \
         <= B.NOALLOC_SCRATCH_BYTES
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "lbsr.h"
+
+int main(void) {
+  lbsr_shape s;
+  lbsr_sched_cfg c;
+  lbsr_ws_layout l;
+  size_t bytes = 0;
+  lbsr_status st;
+  memset(&s, 0, sizeof s);
+  memset(&c, 0, sizeof c);
+  s.num_q_heads = 64; s.num_kv_heads = 8; s.head_dim = 128; s.page_size = 64;
+  s.kv_dtype = LBSR_KV_BF16; s.max_blocks_per_seq = 2048; s.tokens_per_seq = 1;
+  s.num_pages = 4096; s.page_stride = 8 * 8192; s.head_stride = 8192;
+  c.sched = LBSR_SCHED_DYNAMIC; c.num_workers = 256;
+  st = lbsr_workspace_layout(&s, 32, &c, &l);
+  printf("%d %d %zu %d %d\n", lbsr_abi_version(), (int)st, l.total, l.num_workers, l.max_chunks);
+  s.head_dim = 64;
+  st = lbsr_workspace_size(&s, 32, &c, &bytes);
+  printf("%s|%s\n", lbsr_status_string(st), lbsr_last_error());
+  return 0;
+}
+"""
+
+
+def test_header_is_c_and_the_library_links_from_c(lib, tmp_path):
+    """include/lbsr.h is a C header (pedantic C99, warnings as errors), and a C
+    program linked against liblbsr.so gets the same host-side answers as the
+    binding: the workspace layout of a decode step, and a refused shape."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(B.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", libdir, "-l:" + os.path.basename(B.LIB_PATH),
+                    "-Wl,-rpath," + libdir], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    abi, st, total, workers, max_chunks = out[0].split()
+    cfg = DecodeConfig(64, 8, "bf16", 2048, 4096)
+    ref = workspace_layout(cfg, 32, Schedule("dynamic", num_workers=256))
+    assert (int(abi), int(st)) == (lib.lbsr_abi_version(), 0)
+    assert (int(total), int(workers), int(max_chunks)) == (ref.total, ref.num_workers, ref.max_chunks)
+    assert out[1].startswith("LBSR_E_UNSUPPORTED") and "head_dim 64" in out[1], out[1]
