@@ -141,38 +141,35 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> OCP E4M3 (E4M3FN) code: clamp to +-448, then one round-to-nearest-
-// even step on the bit pattern (so the result does not depend on the
-// hardware conversion's rounding or saturation mode).
-__device__ inline uint32_t f32_to_e4m3_sat(float x) {
-  if (__builtin_isnan(x)) return 0x7F;
-  x = fminf(fmaxf(x, -448.f), 448.f);
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 31) << 7;
-  const int ex = (int)((u >> 23) & 0xFF);
-  if (ex == 0) return sign;                     // below 2^-126: rounds to zero
-  int e = ex - 127;
-  const uint32_t sig = (u & 0x7FFFFFu) | 0x800000u;   // value = sig * 2^(e - 23)
-  if (e >= -6) {
-    uint32_t q = sig >> 20;                     // 4 significant bits
-    const uint32_t rem = sig & 0xFFFFFu, half = 0x80000u;
-    if (rem > half || (rem == half && (q & 1))) q++;
-    if (q == 16) { q = 8; e++; }                // cannot pass 448 after the clamp
-    return sign | (uint32_t)((e + 7) << 3) | (q & 7);
-  }
-  // subnormal: multiples of 2^-9, value / 2^-9 = sig * 2^(e - 14)
-  const int sh = 14 - e;                        // >= 21
-  if (sh >= 32) return sign;
-  uint32_t q = sig >> sh;
-  const uint32_t rem = sig & ((1u << sh) - 1), half = 1u << (sh - 1);
-  if (rem > half || (rem == half && (q & 1))) q++;
-  return sign | q;                              // q == 8 encodes the smallest normal
+// fp32 -> OCP E4M3 (E4M3FN) codes: clamp to +-448, then one round to nearest
+// (ties to even).  The rounding is gfx950's packed conversion
+// (v_cvt_scalef32_pk_fp8_f32, scale 1): after the clamp no value can reach its
+// saturation handling, and on every fp32 value of magnitude <= 448 (both signs,
+// 2^31 + 2 of them, checked exhaustively on the device) it gives the same code
+// as rounding the bit pattern by hand -- 4 significant bits for normals,
+// multiples of 2^-9 below 2^-6, zeros keeping their sign.  A NaN gives 0x7F
+// (the clamp alone would turn it into -448).
+typedef short e4m3_v2i16 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float e4m3_clamp(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
+
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+  e4m3_v2i16 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, e4m3_clamp(x), 0.f, 1.f, false);
+  return __builtin_isnan(x) ? 0x7Fu : ((uint32_t)r[0] & 0xFFu);
 }
 
 // Four values -> four E4M3 codes in one little-endian word.
 __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
-  return f32_to_e4m3_sat(a) | (f32_to_e4m3_sat(b) << 8) | (f32_to_e4m3_sat(c) << 16) |
-         (f32_to_e4m3_sat(d) << 24);
+  e4m3_v2i16 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, e4m3_clamp(a), e4m3_clamp(b), 1.f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, e4m3_clamp(c), e4m3_clamp(d), 1.f, true);
+  uint32_t w = __builtin_bit_cast(uint32_t, r);
+  if (__builtin_isnan(a)) w = (w & 0xFFFFFF00u) | 0x7Fu;
+  if (__builtin_isnan(b)) w = (w & 0xFFFF00FFu) | 0x7F00u;
+  if (__builtin_isnan(c)) w = (w & 0xFF00FFFFu) | 0x7F0000u;
+  if (__builtin_isnan(d)) w = (w & 0x00FFFFFFu) | 0x7F000000u;
+  return w;
 }
 
 }  // namespace lbsr
