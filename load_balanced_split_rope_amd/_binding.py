@@ -178,10 +178,13 @@ def _check(status):
 
 
 def _ptr(t):
-    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+    # every entry point declares its pointer arguments as c_void_p, so a plain
+    # int (or None for NULL) is passed as is
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream):
+    """The HIP stream handle: `stream`'s, or torch's current stream on the current device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+    return stream.cuda_stream

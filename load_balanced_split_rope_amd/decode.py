@@ -13,8 +13,26 @@ import torch
 from . import _binding as B
 
 
+class _Memo:
+    """The ctypes structs a config marshals to, built once and rebuilt after any
+    field is assigned (the dataclasses below stay mutable)."""
+
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        object.__setattr__(self, "_memo", {})
+
+    def _memoised(self, key, build):
+        memo = self.__dict__.get("_memo")
+        if memo is None:
+            memo = {}
+            object.__setattr__(self, "_memo", memo)
+        if key not in memo:
+            memo[key] = build()
+        return memo[key]
+
+
 @dataclass
-class DecodeConfig:
+class DecodeConfig(_Memo):
     """Geometry of the KV pools and the per-step constants (lbsr_shape + lbsr_params)."""
     num_q_heads: int
     num_kv_heads: int
@@ -36,11 +54,17 @@ class DecodeConfig:
     q_scale: float = 1.0          # Q.K^T on FP8 matrix cores
 
     def shape(self):
-        return B.Shape(self.num_q_heads, self.num_kv_heads, B.HEAD_DIM, B.PAGE_SIZE,
-                       B.KV_BF16 if self.kv_dtype == "bf16" else B.KV_FP8_E4M3,
-                       self.max_blocks_per_seq, self.tokens_per_seq, 0, self.num_pages,
-                       self.page_stride or self.num_kv_heads * B.TILE_ELEMS,
-                       self.head_stride or B.TILE_ELEMS)
+        """lbsr_shape of this config (a fresh struct the caller may modify)."""
+        return B.Shape.from_buffer_copy(self._shape())
+
+    def _shape(self):
+        # shared by the binding's calls; never modified
+        return self._memoised("shape", lambda: B.Shape(
+            self.num_q_heads, self.num_kv_heads, B.HEAD_DIM, B.PAGE_SIZE,
+            B.KV_BF16 if self.kv_dtype == "bf16" else B.KV_FP8_E4M3,
+            self.max_blocks_per_seq, self.tokens_per_seq, 0, self.num_pages,
+            self.page_stride or self.num_kv_heads * B.TILE_ELEMS,
+            self.head_stride or B.TILE_ELEMS))
 
     def tokens_shape(self, batch, *rest):
         """Shape of a per-new-token array: (batch, *rest), or (batch, Tq, *rest) when Tq > 1."""
@@ -48,14 +72,18 @@ class DecodeConfig:
         return (batch,) + rest if Tq == 1 else (batch, Tq) + rest
 
     def params(self):
+        """lbsr_params of this config (a fresh struct the caller may modify)."""
+        return B.Params.from_buffer_copy(self._params())
+
+    def _params(self):
         for name in ("out_dtype", "qk_dtype"):
             if getattr(self, name) not in ("bf16", "fp8"):
                 raise ValueError(f"{name} {getattr(self, name)!r}: 'bf16' or 'fp8'")
-        return B.Params(self.rope_theta, self.rms_eps, int(self.norm_before_rope),
-                        self.k_scale, self.v_scale, self.sm_scale,
-                        B.OUT_BF16 if self.out_dtype == "bf16" else B.OUT_FP8_E4M3,
-                        self.out_scale,
-                        B.QK_BF16 if self.qk_dtype == "bf16" else B.QK_FP8_E4M3, self.q_scale)
+        return self._memoised("params", lambda: B.Params(
+            self.rope_theta, self.rms_eps, int(self.norm_before_rope), self.k_scale,
+            self.v_scale, self.sm_scale,
+            B.OUT_BF16 if self.out_dtype == "bf16" else B.OUT_FP8_E4M3, self.out_scale,
+            B.QK_BF16 if self.qk_dtype == "bf16" else B.QK_FP8_E4M3, self.q_scale))
 
     @property
     def out_torch_dtype(self):
@@ -68,13 +96,15 @@ class DecodeConfig:
 
     def pool_elems(self):
         """Elements a pool must hold: one past the last element of the last tile."""
-        s = self.shape()
-        return ((s.num_pages - 1) * s.page_stride + (s.num_kv_heads - 1) * s.head_stride
-                + B.TILE_ELEMS)
+        def count():
+            s = self._shape()
+            return ((s.num_pages - 1) * s.page_stride + (s.num_kv_heads - 1) * s.head_stride
+                    + B.TILE_ELEMS)
+        return self._memoised("pool_elems", count)
 
 
 @dataclass
-class Schedule:
+class Schedule(_Memo):
     """lbsr_sched_cfg: "dynamic" (P workers, 0 = CU count) or "static" (S splits, 0 = P/B).
 
     xcd_weights: None (equal shares) or 8 integer weights in [1, 65536], the
@@ -89,15 +119,19 @@ class Schedule:
     fold_merge: bool = False
 
     def cfg(self):
+        """lbsr_sched_cfg of this schedule (a fresh struct the caller may modify)."""
+        return B.SchedCfg.from_buffer_copy(self._cfg())
+
+    def _cfg(self):
         if self.kind not in ("dynamic", "static"):
             raise ValueError(f"unknown schedule {self.kind!r}")
         wts = [0] * B.NUM_XCDS if self.xcd_weights is None else [int(x) for x in self.xcd_weights]
         if len(wts) != B.NUM_XCDS:
             raise ValueError(f"xcd_weights needs {B.NUM_XCDS} entries, got {len(wts)}")
-        return B.SchedCfg(B.SCHED_DYNAMIC if self.kind == "dynamic" else B.SCHED_STATIC,
-                          self.num_workers, self.static_splits,
-                          B.SCHED_FOLD_MERGE if self.fold_merge else 0,
-                          (ctypes.c_int32 * B.NUM_XCDS)(*wts))
+        return self._memoised("cfg", lambda: B.SchedCfg(
+            B.SCHED_DYNAMIC if self.kind == "dynamic" else B.SCHED_STATIC, self.num_workers,
+            self.static_splits, B.SCHED_FOLD_MERGE if self.fold_merge else 0,
+            (ctypes.c_int32 * B.NUM_XCDS)(*wts)))
 
 
 def device_workers(device=0):
@@ -108,7 +142,7 @@ def device_workers(device=0):
 
 def workspace_layout(cfg: DecodeConfig, batch: int, sched: Schedule):
     out = B.WsLayout()
-    s, c = cfg.shape(), sched.cfg()
+    s, c = cfg._shape(), sched._cfg()
     B._check(B.lib().lbsr_workspace_layout(ctypes.byref(s), int(batch), ctypes.byref(c),
                                            ctypes.byref(out)))
     return out
@@ -122,6 +156,14 @@ def alloc_workspace(cfg: DecodeConfig, batch: int, sched: Schedule, device="cuda
 # ---------------------------------------------------------------- checks
 
 def _need(t, name, dtype, shape=None, numel=None):
+    # the common case in one comparison chain; the diagnosis below only on failure
+    if (type(t) is torch.Tensor and t.dtype is dtype and t.is_cuda and t.is_contiguous()
+            and (shape is None or t.shape == shape) and (numel is None or t.numel() >= numel)):
+        return
+    _diagnose(t, name, dtype, shape, numel)
+
+
+def _diagnose(t, name, dtype, shape=None, numel=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -163,7 +205,7 @@ def rope_norm_kv_write(cfg: DecodeConfig, q, k, v, positions, q_norm_w, k_norm_w
     _check_pools(cfg, k_cache, v_cache)
     if error_word is not None:
         _need(error_word, "error_word", torch.int32, numel=1)
-    s, p = cfg.shape(), cfg.params()
+    s, p = cfg._shape(), cfg._params()
     B._check(B.lib().lbsr_rope_norm_kv_write(
         ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
         B._ptr(positions), B._ptr(q_norm_w), B._ptr(k_norm_w), B._ptr(block_table),
@@ -175,7 +217,7 @@ def plan(cfg: DecodeConfig, seq_lens, sched: Schedule, workspace, stream=None):
     batch = seq_lens.shape[0]
     _need(seq_lens, "seq_lens", torch.int32, shape=(batch,))
     _need(workspace, "workspace", torch.uint8)
-    s, c = cfg.shape(), sched.cfg()
+    s, c = cfg._shape(), sched._cfg()
     B._check(B.lib().lbsr_plan(ctypes.byref(s), batch, B._ptr(seq_lens), ctypes.byref(c),
                                B._ptr(workspace), workspace.numel(), B._stream(stream)))
 
@@ -192,7 +234,7 @@ def attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, sched: Sc
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
     _need(workspace, "workspace", torch.uint8)
-    s, p, c = cfg.shape(), cfg.params(), sched.cfg()
+    s, p, c = cfg._shape(), cfg._params(), sched._cfg()
     B._check(B.lib().lbsr_attention(
         ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q_out), B._ptr(k_cache),
         B._ptr(v_cache), B._ptr(block_table), ctypes.byref(c), B._ptr(workspace),
@@ -218,7 +260,7 @@ def _step_args(cfg, q, k, v, positions, seq_lens, q_norm_w, k_norm_w, block_tabl
     _check_pools(cfg, k_cache, v_cache)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    s, p, c = cfg.shape(), cfg.params(), sched.cfg()
+    s, p, c = cfg._shape(), cfg._params(), sched._cfg()
     head = (ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
             B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
             B._ptr(block_table), B._ptr(k_cache), B._ptr(v_cache), B._ptr(q_out),
@@ -286,7 +328,7 @@ def prefill_attention(cfg: DecodeConfig, q_out, k_cache, v_cache, block_table, s
     _check_pools(cfg, k_cache, v_cache)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    s, p = cfg.shape(), cfg.params()
+    s, p = cfg._shape(), cfg._params()
     B._check(B.lib().lbsr_prefill_attention(
         ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q_out), B._ptr(k_cache), B._ptr(v_cache),
         B._ptr(block_table), B._ptr(seq_lens), B._ptr(workspace), _nbytes(workspace),
@@ -317,7 +359,7 @@ def prefill_step(cfg: DecodeConfig, q, k, v, positions, seq_lens, q_norm_w, k_no
     _check_pools(cfg, k_cache, v_cache)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    s, p = cfg.shape(), cfg.params()
+    s, p = cfg._shape(), cfg._params()
     B._check(B.lib().lbsr_prefill_step(
         ctypes.byref(s), ctypes.byref(p), batch, B._ptr(q), B._ptr(k), B._ptr(v),
         B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
@@ -330,7 +372,7 @@ def prefill_workspace_size(cfg: DecodeConfig, batch: int, total_tokens: int) -> 
     """Bytes of a prefill's workspace (its longest-first work list): total_tokens
     is the packed count of a ragged batch, or batch * tokens_per_seq."""
     n = ctypes.c_size_t()
-    s = cfg.shape()
+    s = cfg._shape()
     B._check(B.lib().lbsr_prefill_workspace_size(ctypes.byref(s), batch, total_tokens,
                                                  ctypes.byref(n)))
     return n.value
@@ -371,7 +413,7 @@ def prefill_attention_varlen(cfg: DecodeConfig, q_start, q_out, k_cache, v_cache
         _need(error_word, "error_word", torch.int32, numel=1)
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
-    s, p = cfg.shape(), cfg.params()
+    s, p = cfg._shape(), cfg._params()
     B._check(B.lib().lbsr_prefill_attention_varlen(
         ctypes.byref(s), ctypes.byref(p), batch, total, B._ptr(q_start), B._ptr(q_out),
         B._ptr(k_cache), B._ptr(v_cache), B._ptr(block_table), B._ptr(seq_lens),
@@ -402,7 +444,7 @@ def prefill_step_varlen(cfg: DecodeConfig, q_start, q, k, v, positions, seq_lens
         _need(error_word, "error_word", torch.int32, numel=1)
     _check_table(cfg, block_table, batch)
     _check_pools(cfg, k_cache, v_cache)
-    s, p = cfg.shape(), cfg.params()
+    s, p = cfg._shape(), cfg._params()
     B._check(B.lib().lbsr_prefill_step_varlen(
         ctypes.byref(s), ctypes.byref(p), batch, total, B._ptr(q_start), B._ptr(q), B._ptr(k),
         B._ptr(v), B._ptr(positions), B._ptr(seq_lens), B._ptr(q_norm_w), B._ptr(k_norm_w),
@@ -423,8 +465,8 @@ def read_plan(cfg: DecodeConfig, batch: int, sched: Schedule, workspace, stream=
             "seq_len_eff": np.zeros(batch, np.int32)}
     host = B.PlanHost(*(a.ctypes.data for a in arrs.values()))
     n = ctypes.c_int32(0)
-    s = cfg.shape()
-    B._check(B.lib().lbsr_read_plan(ctypes.byref(s), batch, ctypes.byref(sched.cfg()),
+    s = cfg._shape()
+    B._check(B.lib().lbsr_read_plan(ctypes.byref(s), batch, ctypes.byref(sched._cfg()),
                                     B._ptr(workspace), workspace.numel(), ctypes.byref(host),
                                     ctypes.byref(n), B._stream(stream)))
     arrs["chunks"] = arrs["chunks"][:n.value].copy()

@@ -473,3 +473,21 @@ def test_header_is_c_and_the_library_links_from_c(lib, tmp_path):
     assert (int(abi), int(st)) == (lib.lbsr_abi_version(), 0)
     assert (int(total), int(workers), int(max_chunks)) == (ref.total, ref.num_workers, ref.max_chunks)
     assert out[1].startswith("LBSR_E_UNSUPPORTED") and "head_dim 64" in out[1], out[1]
+
+
+def test_config_structs_follow_field_changes():
+    """The binding builds each config's ctypes structs once; assigning a field
+    rebuilds them, and a struct handed to a caller is the caller's copy."""
+    c = DecodeConfig(64, 8, "bf16", 2048, 4300)
+    s = c.shape()
+    s.head_dim = 64
+    assert c.shape().head_dim == 128
+    c.num_pages = 10
+    assert c.shape().num_pages == 10
+    assert c.pool_elems() == 9 * 8 * 8192 + 7 * 8192 + 8192
+    c.out_dtype = "fp8"
+    assert c.params().out_dtype == B.OUT_FP8_E4M3
+    sched = Schedule("dynamic", num_workers=5)
+    before = sched.cfg()
+    sched.num_workers = 7
+    assert sched.cfg().num_workers == 7 and before.num_workers == 5
