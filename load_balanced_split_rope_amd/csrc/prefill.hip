@@ -107,10 +107,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     int num_blocks_q, const int32_t* __restrict__ q_start, int total_tokens,
     const int32_t* __restrict__ work, float inv_q_scale) {
   constexpr int NF = kFp8 ? 8 : 16;                  // 1 KiB fragments per K (or V) tile
-  constexpr int kStage = 2 * NF * kWave;             // u32x4 per stage: K then V
+  constexpr int kStage = 2 * NF * kWave;             // u32x4 of one tile in HBM: K then V
   constexpr int kPerThread = kStage / (kPrefillWaves * kWave);   // 4 (BF16) or 2 (FP8)
   constexpr int kElemBytes = kFp8 ? 1 : 2;
-  __shared__ u32x4 s_kv[2][kStage];                  // 64 KiB (BF16) / 32 KiB (FP8)
+  // FP8 cache with BF16 scores: each tile is converted to BF16 once, as it is
+  // staged into LDS, instead of by each of the workgroup's waves as they read
+  // it; the tile loop then runs the BF16 form.  An FP8 fragment f holds, per
+  // lane, the values of BF16 fragments 2f (its low 8 bytes) and 2f + 1 (its
+  // high 8 bytes), for K and for V.  With FP8 scores K stays FP8 in LDS.
+  constexpr bool kCvtStage = kFp8 && !kQk8;
+  constexpr bool kFp8Lds = kFp8 && !kCvtStage;       // the LDS stage holds E4M3 codes
+  constexpr int NFL = kFp8Lds ? 8 : 16;              // 1 KiB fragments per K (or V) tile in LDS
+  __shared__ u32x4 s_kv[2][2 * NFL * kWave];         // 64 KiB (BF16 in LDS) / 32 KiB (FP8)
 
   const int G = geo.group, Hq = geo.num_q_heads;
   int qb, b, g;
@@ -199,7 +207,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
   };
   auto store_tile = [&](int stage, const u32x4 (&src)[kPerThread]) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) s_kv[stage][tid + i * kPrefillWaves * kWave] = src[i];
+    for (int i = 0; i < kPerThread; ++i) {
+      const int q = tid + i * kPrefillWaves * kWave;          // slot in the HBM tile
+      if constexpr (kCvtStage) {
+        const int f = q / kWave, l = q - f * kWave;           // fragment (K, then V) and lane
+        const bf16x8 lo = e4m3x8_to_bf16x8(src[i][0], src[i][1]);
+        const bf16x8 hi = e4m3x8_to_bf16x8(src[i][2], src[i][3]);
+        s_kv[stage][(2 * f) * kWave + l] = __builtin_bit_cast(u32x4, lo);
+        s_kv[stage][(2 * f + 1) * kWave + l] = __builtin_bit_cast(u32x4, hi);
+      } else {
+        s_kv[stage][q] = src[i];
+      }
+    }
   };
 
   SoftmaxState st[kPrefillBlocks];
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     const int stage = t & 1;
     if constexpr (!kLast) load_tile(t + 1, pre);
     const u32x4* kf = s_kv[stage];
-    const u32x4* vf = s_kv[stage] + NF * kWave;
+    const u32x4* vf = s_kv[stage] + NFL * kWave;
 
     // ---- scores: every K fragment read from LDS serves all column blocks ----
     f32x4 S[kPrefillBlocks][4];
@@ -247,7 +266,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8 a;
-        if constexpr (kFp8) {
+        if constexpr (kFp8Lds) {
           const u32x4 w = kf[(2 * tb + (s >> 1)) * kWave + lane];
           a = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
         } else {
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
     if constexpr (kLast) {
       const int rem = L - row0;
       if (rem < kPage) {
-        v_keep_masks<kFp8>(rem, kc, keep);
+        v_keep_masks<kFp8Lds>(rem, kc, keep);
       } else {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -284,7 +303,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         bf16x8 a;
-        if constexpr (kFp8) {
+        if constexpr (kFp8Lds) {
           u32x4 w = vf[db * kWave + lane];
           if constexpr (kLast) {
 #pragma unroll
