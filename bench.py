@@ -424,12 +424,15 @@ def stream_ceiling(dev, nbytes=1 << 30, launches=10):
             "timing": f"{launches} back-to-back launches between HIP events, median of 3"}
 
 
-def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_dtype="bf16"):
+def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_dtype="bf16",
+            loops=1):
     """Dynamic step time, per-kernel times, and (full) graph time and static sweep.
 
     weighted: calibrate per-XCD weights from traced steps, compare weighted and
     equal shares with interleaved untimed-for-the-headline loops, and time the
-    headline with the faster of the two (both figures are reported)."""
+    headline with the faster of the two (both figures are reported).
+    loops: the step time is the median of this many timed loops of `steps`
+    steps (1 for the headline: exactly `steps` steps between two syncs)."""
     equal = lb.Schedule("dynamic", num_workers=P)
     case = Case(w, dev, out_dtype=out_dtype, out_scale=2.0 ** -7, qk_dtype=qk_dtype,
                 q_scale=Q_SCALE)
@@ -452,7 +455,8 @@ def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_
         if mw < me:
             dyn = cand
     r["schedule"] = dyn
-    r["ms"] = case.timed_steps(dyn, steps, warmup)
+    r["ms"] = float(np.median([case.timed_steps(dyn, steps, warmup if i == 0 else 0)
+                               for i in range(loops)]))
     r["step_dist"] = case.step_distribution(dyn, steps)
     _, kmean = case.kernel_times(dyn, max(20, min(steps, 100)))
     r["kernel_ms"] = kmean
@@ -472,9 +476,12 @@ def measure(w, dev, P, steps, warmup, full, weighted=True, out_dtype="bf16", qk_
     return r
 
 
-def case_static_ms(case, P, steps):
-    """Step time of the static split-KV baseline at its default S."""
-    return case.timed_steps(lb.Schedule("static", num_workers=P), steps, 5)
+def case_static_ms(case, P, steps, loops=1):
+    """Step time of the static split-KV baseline at its default S (median of
+    `loops` timed loops)."""
+    sched = lb.Schedule("static", num_workers=P)
+    return float(np.median([case.timed_steps(sched, steps, 5 if i == 0 else 0)
+                            for i in range(loops)]))
 
 
 def main():
@@ -625,14 +632,15 @@ def main():
             }
             # controls: a uniform batch, where the static split at its default S
             # equals the dynamic plan (expected ratio ~1), and the log-uniform
-            # mixed batch with an FP8 cache
+            # mixed batch with an FP8 cache; each time is the median of three
+            # timed loops, so one stalled loop does not set it
             controls = {}
             for name in ("tiny", "uniform", "loguniform"):
                 wc = wl.named(name)
                 steps_c = args.steps if name == "uniform" else max(10, args.steps // 4)
-                rc = measure(wc, dev, P, steps_c, args.warmup, False, False)
+                rc = measure(wc, dev, P, steps_c, args.warmup, False, False, loops=3)
                 cc = Case(wc, dev)
-                st = case_static_ms(cc, P, steps_c)
+                st = case_static_ms(cc, P, steps_c, loops=3)
                 # the launch-bound case: the step replayed as one captured graph
                 graph_ms = cc.graph_ms(rc["schedule"], steps_c) if name == "tiny" else None
                 del cc
@@ -640,6 +648,7 @@ def main():
                 cbc = compulsory_bytes(wc)["total"]
                 controls[name] = {
                     "workload": WORKLOAD_TEXT[name], "us_per_step": round(rc["ms"] * 1e3, 2),
+                    "timing": f"median of 3 timed loops of {steps_c} steps",
                     "step_us_distribution": rc["step_dist"],
                     "value_GBs": round(cbc / (rc["ms"] * 1e-3) / 1e9, 1),
                     "hbm_frac_step": round(cbc / (rc["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
