@@ -18,9 +18,10 @@
 //   * the block's causal range [0, L - Tq + last token] is walked tile by
 //     tile; each K/V tile is read from HBM once per workgroup, straight into
 //     LDS in its fragment order (the page layout already is the operand
-//     order), double-buffered: every thread loads its share of tile t+1
-//     into registers while the waves compute on tile t from LDS, then writes
-//     it to the other buffer before the workgroup barrier.
+//     order), double-buffered: tile t+1 is requested while the waves compute
+//     on tile t from LDS, and lands in the other buffer before the workgroup
+//     barrier.  A BF16 tile goes there by global-to-LDS loads; an FP8 tile
+//     through registers (converted to BF16 on the way for BF16 scores).
 //   * one online-softmax pass per column over the whole range, so the result
 //     goes straight to the output: no partials, no merge.
 //   * workgroups are numbered longest-first (the blocks of the last tokens
@@ -39,6 +40,11 @@
 
 namespace lbsr {
 
+// s_waitcnt operand: vmcnt(0), with expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
+// cache-policy operand of a global-to-LDS load: nt, as for the streamed tiles
+constexpr int kLoadNonTemporal = 2;
+
 // maximum with lane l ^ kXor (16 or 32), by the gfx950 lane-swap instructions
 template <int kXor>
 __device__ __forceinline__ float lane_maximum(float x) {
@@ -52,9 +58,28 @@ __device__ __forceinline__ float lane_maximum(float x) {
 // scale applied inside the exponent: the column max is taken over the raw
 // scores and scaled once (c > 0, so fl(max s * c) = max fl(s * c): the same
 // running max), and p = 2^fma(s, c, -m), one instruction per score where
-// softmax_tile spends a multiply and a subtract.  p differs from softmax_tile's
-// only by the rounding of s * c that the fma skips (the row at the max gets
-// 2^r with |r| <= half an ulp of m instead of exactly 1).
+// softmax_tile spends a multiply and a subtract.
+//
+// The running max m need not be the exact maximum: any m at or below it gives
+// the same softmax (the factor 2^-m cancels between O and the sum) as long as
+// no p overflows.  So once every column of the wave has a finite m, a tile
+// first takes p = 2^fma(s, c, -m) against the m it has, and keeps it when no
+// lane's sum of the tile's p reaches 2^16: then every p is below 2^16 (the
+// tile's scores rose at most about 16 above m in the log2 domain), which
+// leaves O and the sum far from fp32 overflow and keeps P's BF16 rounding
+// relative, as before.  That skips the tile's max, its cross-lane reduction
+// and the rescale test.  Otherwise (a score far above m, the first tile, a
+// NaN or an infinity) the tile takes the full update: the max over its
+// scores, and a rescale when that max is more than 8 above m.
+__device__ __forceinline__ float sum16(const float (&x)[16]) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
 __device__ __forceinline__ void softmax_tile_fma(const f32x4 (&S)[4], SoftmaxState& st, bool mask,
                                                  int lim, int kc, float c, bf16x8 (&pB)[2]) {
   float x[16];
@@ -69,33 +94,41 @@ __device__ __forceinline__ void softmax_tile_fma(const f32x4 (&S)[4], SoftmaxSta
       for (int e = 0; e < 4; ++e)
         if (16 * tb + 4 * kc + e >= lim) x[4 * tb + e] = -__builtin_inff();
   }
-  // IEEE maximum (NaN-propagating): a chain of v_maximum3_f32, without the
-  // operand quieting that fmaxf needs; equal to fmaxf on the finite and -inf
-  // scores, and a NaN score reaches the output through P either way
-  float mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
-  mx = lane_maximum<32>(lane_maximum<16>(mx)) * c;
-  if (__any(mx > st.m + 8.f)) {                          // wave-uniform
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = fast_exp2(st.m - (m_new == -__builtin_inff() ? 0.f : m_new));
-    st.lsum *= alpha;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.O[i] *= alpha;
-    st.m = m_new;
-  }
-  const float nbase = st.m == -__builtin_inff() ? 0.f : -st.m;
+  float p[16];
   float psum = 0.f;
+  bool kept = false;
+  if (__all(st.m != -__builtin_inff())) {                // wave-uniform
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = fast_exp2(__builtin_fmaf(x[i], c, nbase));
-    psum += x[i];
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(x[i], c, -st.m));
+    psum = sum16(p);
+    kept = __all(psum < 65536.f);                        // false on NaN and infinity
+  }
+  if (!kept) {
+    // IEEE maximum (NaN-propagating): a chain of v_maximum3_f32, without the
+    // operand quieting that fmaxf needs; equal to fmaxf on the finite and -inf
+    // scores, and a NaN score reaches the output through P either way
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
+    mx = lane_maximum<32>(lane_maximum<16>(mx)) * c;
+    if (__any(mx > st.m + 8.f)) {                        // wave-uniform
+      const float m_new = fmaxf(st.m, mx);
+      const float alpha = fast_exp2(st.m - (m_new == -__builtin_inff() ? 0.f : m_new));
+      st.lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.O[i] *= alpha;
+      st.m = m_new;
+    }
+    const float nbase = st.m == -__builtin_inff() ? 0.f : -st.m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(x[i], c, nbase));
+    psum = sum16(p);
   }
   st.lsum += psum;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)x[8 * s + e];
+    for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)p[8 * s + e];
 }
 
 template <bool kFp8, bool kQk8>
@@ -118,7 +151,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
   constexpr bool kCvtStage = kFp8 && !kQk8;
   constexpr bool kFp8Lds = kFp8 && !kCvtStage;       // the LDS stage holds E4M3 codes
   constexpr int NFL = kFp8Lds ? 8 : 16;              // 1 KiB fragments per K (or V) tile in LDS
-  __shared__ u32x4 s_kv[2][2 * NFL * kWave];         // 64 KiB (BF16 in LDS) / 32 KiB (FP8)
+  // A BF16 cache is staged by the global-to-LDS loads: each lane's 16 bytes
+  // go straight to its slot (the fragment order puts lane l of a wave's 1 KiB
+  // at l * 16, which is where those loads write), with no trip through
+  // registers and no LDS store instructions.  The two stages are then
+  // separate arrays, and the loop takes tiles in pairs so that every step
+  // names its stage statically: the compiler can tell a step's LDS reads from
+  // the loads filling the other stage, and waits for those only at the step's
+  // end.  (With FP8 codes in LDS, for FP8 scores, the same staging measured
+  // about 3% slower than staging through registers.)  Staged through
+  // registers, the two stages are one array indexed by t & 1.
+  constexpr bool kDma = !kFp8;
+  constexpr int kStageLds = 2 * NFL * kWave;         // u32x4: 32 KiB (BF16 in LDS) / 16 KiB (FP8)
 
   const int G = geo.group, Hq = geo.num_q_heads;
   int qb, b, g;
@@ -205,7 +249,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
       dst[i] = __builtin_nontemporal_load(src);
     }
   };
-  auto store_tile = [&](int stage, const u32x4 (&src)[kPerThread]) {
+  auto store_tile = [&](u32x4* dst, const u32x4 (&src)[kPerThread]) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int q = tid + i * kPrefillWaves * kWave;          // slot in the HBM tile
@@ -213,11 +257,30 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
         const int f = q / kWave, l = q - f * kWave;           // fragment (K, then V) and lane
         const bf16x8 lo = e4m3x8_to_bf16x8(src[i][0], src[i][1]);
         const bf16x8 hi = e4m3x8_to_bf16x8(src[i][2], src[i][3]);
-        s_kv[stage][(2 * f) * kWave + l] = __builtin_bit_cast(u32x4, lo);
-        s_kv[stage][(2 * f + 1) * kWave + l] = __builtin_bit_cast(u32x4, hi);
+        dst[(2 * f) * kWave + l] = __builtin_bit_cast(u32x4, lo);
+        dst[(2 * f + 1) * kWave + l] = __builtin_bit_cast(u32x4, hi);
       } else {
-        s_kv[stage][q] = src[i];
+        dst[q] = src[i];
       }
+    }
+  };
+  // tile t straight into LDS: wave w's load i fills slots [i * 512 + 64 w, +64)
+  auto dma_tile = [&](int t, u32x4* dst) {
+    const int p = bt_row[t];
+    const bool ok = p >= 0 && p < geo.num_pages;
+    bad_page |= !ok;
+    const size_t base = ((size_t)(ok ? p : 0) * geo.page_stride + (size_t)g * geo.head_stride) *
+                        kElemBytes;
+    const u32x4* kt = (const u32x4*)(k_pool + base);
+    const u32x4* vt = (const u32x4*)(v_pool + base);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int q = tid + i * kPrefillWaves * kWave;
+      const u32x4* src = q < NF * kWave ? kt + q : vt + (q - NF * kWave);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src,
+          (__attribute__((address_space(3))) void*)(dst + i * kPrefillWaves * kWave + wave * kWave),
+          16, 0, kLoadNonTemporal);
     }
   };
 
@@ -231,25 +294,33 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
   }
 
   u32x4 pre[kPerThread];
-  load_tile(0, pre);
-  // FP8 scores: q's codes for each column block, computed while tile 0 streams in
   i32x8 qF[kPrefillBlocks];
+  // tile 0 into stage 0; FP8 scores: q's codes for each column block,
+  // computed while it streams in
+  auto first_tile = [&](u32x4* dst) {
+    if constexpr (kDma) dma_tile(0, dst);
+    else load_tile(0, pre);
 #pragma unroll
-  for (int cb = 0; cb < kPrefillBlocks; ++cb) {
-    qF[cb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (kQk8) qF[cb] = q_fp8_operand(qB[cb], inv_q_scale);
-  }
-  store_tile(0, pre);
-  __syncthreads();
+    for (int cb = 0; cb < kPrefillBlocks; ++cb) {
+      qF[cb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if constexpr (kQk8) qF[cb] = q_fp8_operand(qB[cb], inv_q_scale);
+    }
+    if constexpr (kDma) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads into LDS
+    else store_tile(dst, pre);
+    __syncthreads();
+  };
   // One tile: scores, online softmax, P.V.  Only the block's last tile can
   // reach past the sequence end, so the V-row masking is compiled into that
   // step alone (applied to every tile it costs two VALU ops per V dword).
-  auto tile_step = [&](int t, auto last_c) {
+  // cur: tile t's stage; nxt: the other, which receives tile t + 1
+  auto tile_step = [&](int t, auto last_c, u32x4* cur, u32x4* nxt) {
     constexpr bool kLast = decltype(last_c)::value;
-    const int stage = t & 1;
-    if constexpr (!kLast) load_tile(t + 1, pre);
-    const u32x4* kf = s_kv[stage];
-    const u32x4* vf = s_kv[stage] + NFL * kWave;
+    if constexpr (!kLast) {
+      if constexpr (kDma) dma_tile(t + 1, nxt);
+      else load_tile(t + 1, pre);
+    }
+    const u32x4* kf = cur;
+    const u32x4* vf = cur + NFL * kWave;
 
     // ---- scores: every K fragment read from LDS serves all column blocks ----
     f32x4 S[kPrefillBlocks][4];
@@ -324,12 +395,34 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(
       }
     }
     if constexpr (!kLast) {
-      store_tile(stage ^ 1, pre);
+      if constexpr (kDma) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      else store_tile(nxt, pre);
       __syncthreads();
     }
   };
-  for (int t = 0; t + 1 < ntiles; ++t) tile_step(t, std::false_type{});
-  tile_step(ntiles - 1, std::true_type{});
+  if constexpr (kDma) {
+    __shared__ u32x4 s_kv0[kStageLds];
+    __shared__ u32x4 s_kv1[kStageLds];
+    first_tile(s_kv0);
+    // tiles in pairs (stage 0, then stage 1), the last one peeled
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      tile_step(t, std::false_type{}, s_kv0, s_kv1);
+      tile_step(t + 1, std::false_type{}, s_kv1, s_kv0);
+    }
+    if (t + 1 < ntiles) {
+      tile_step(t, std::false_type{}, s_kv0, s_kv1);
+      tile_step(t + 1, std::true_type{}, s_kv1, s_kv0);
+    } else {
+      tile_step(t, std::true_type{}, s_kv0, s_kv1);
+    }
+  } else {
+    __shared__ u32x4 s_kv[2][kStageLds];
+    first_tile(s_kv[0]);
+    for (int t = 0; t + 1 < ntiles; ++t)
+      tile_step(t, std::false_type{}, s_kv[t & 1], s_kv[(t & 1) ^ 1]);
+    tile_step(ntiles - 1, std::true_type{}, s_kv[(ntiles - 1) & 1], s_kv[ntiles & 1]);
+  }
   if (bad_page && error_word) atomicOr(error_word, (int32_t)kErrPage);
 
   // ---- output ----
