@@ -106,7 +106,12 @@ def poison_indices(inp, w, kind, spare_pages=True):
         owned.update(bt[b, :-(-L // PAGE_SIZE)].tolist())
     idx = [np.zeros(0, dtype=np.int64)]
     if spare_pages:
-        idx += [np.arange(p * ps, p * ps + Hkv * hs) for p in range(inp["num_pages"]) if p not in owned]
+        # the tile of this kind for every (unowned page, KV head): with K and V
+        # interleaved in one allocation the page's other tiles belong to the
+        # other kind (and one view's range past them to the next page)
+        tile = PAGE_SIZE * 128
+        idx += [np.arange(p * ps + g * hs, p * ps + g * hs + tile)
+                for p in range(inp["num_pages"]) if p not in owned for g in range(Hkv)]
     d = np.arange(128)
     for b, L in enumerate(lens):
         t = (L - 1) // PAGE_SIZE

@@ -211,3 +211,21 @@ def test_mutation_long_fp8_output_codes_fail(long_fp8):
         codes = oracle.encode_output(bad, "fp8", out_scale)
         with pytest.raises(AssertionError):
             check_output_fp8(codes, ref, "fp8", out_scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_interleaved_layout_changes_nothing(dtype):
+    """The same cache with each (page, KV head)'s V tile right after its K tile
+    in one allocation (head stride two tiles, page stride 2 Hkv tiles, V read
+    through a view one tile in): the oracle reads the same values through the
+    other strides, so every output row and lse equals the default layout's
+    bit for bit."""
+    w = wl.custom([200, 5, 129], num_q_heads=16, num_kv_heads=2, kv_dtype=dtype, seed=4)
+    a = wl.make_inputs(w)
+    b = wl.make_inputs(w, kv_interleave=True)
+    assert (b["page_stride"], b["head_stride"]) == (2 * a["page_stride"], 2 * a["head_stride"])
+    _, _, _, _, fa = run_oracle(w, a)
+    _, _, _, _, fb = run_oracle(w, b)
+    assert fa.keys() == fb.keys()
+    for key in fa:
+        assert np.array_equal(fa[key][0], fb[key][0]) and fa[key][1] == fb[key][1], key
