@@ -18,6 +18,16 @@ import numpy as np
 import torch
 
 from oracle import tile_offset, PAGE_SIZE, BF16_NAN_BITS, E4M3_NAN_CODE
+from oracle.qk import query_values
+from oracle.step import apply_prologue_writes, gather_kv
+
+# R23 with FP8 scores: the FP8 matrix cores accumulate a score's 128 products
+# with less than fp32 precision.  Measured on the device over 16,384 one-row
+# scores (four q scales; with one row, lse is the score itself), the error was
+# at most 2^-16.05 of M = sm * sum_d |q_d k_d|.  An lse is a softmax-weighted
+# mean of its row's scores, so its error is at most the largest score error;
+# FP8-score lse checks add twice the measured bound times the row's largest M.
+FP8_SCORE_REL = 2.0 ** -15
 
 BF16_ATOL, BF16_RTOL, BF16_REL_L2 = 2e-2, 1e-2, 1e-2
 FP8_ATOL, FP8_REL_L2 = 6e-2, 2e-2
@@ -160,3 +170,39 @@ def host_step_inputs(inp):
         "seq_lens": inp["seq_lens"].cpu().numpy().astype(np.int64),
         "block_table": inp["block_table"].cpu().numpy().astype(np.int64),
     }
+
+
+def fp8_lse_slack(w, k_pool, block_table, seq_lens, page_stride, head_stride, q_out_bits,
+                  q_scale, seq_of_row, seqs=None):
+    """FP8-score lse slack, [rows, Hq]: FP8_SCORE_REL * sm * max over the L_b keys of
+    sum_d |q_d k_d|, for query row r of sequence b = seq_of_row[r] (q_out_bits
+    [rows, Hq, D] BF16 bits, quantised under R23 as the scores use them).
+    k_pool holds the new tokens' keys; seqs: only these sequences (0 elsewhere)."""
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, 128
+    G = Hq // Hkv
+    seq_of_row = np.asarray(seq_of_row)
+    qv = np.abs(query_values(q_out_bits, {"qk_dtype": "fp8", "q_scale": q_scale}))
+    qv = qv.reshape(len(seq_of_row), Hq, D)
+    k_scale = float(np.float32(w.k_scale))
+    out = np.zeros((len(seq_of_row), Hq))
+    for b in (np.unique(seq_of_row) if seqs is None else seqs):
+        rs = np.nonzero(seq_of_row == b)[0]
+        if rs.size == 0:
+            continue
+        for g in range(Hkv):
+            K = np.abs(gather_kv(k_pool, "k", w.kv_dtype, block_table[b], int(seq_lens[b]), g,
+                                 page_stride=page_stride, head_stride=head_stride, scale=k_scale))
+            M = qv[rs, g * G:(g + 1) * G].reshape(-1, D) @ K.T          # [rows * G, L]
+            out[rs, g * G:(g + 1) * G] = M.max(axis=1).reshape(rs.size, G)
+    return FP8_SCORE_REL / np.sqrt(128.0) * out
+
+
+def fp8_lse_slack_for(inp, w, pro, q_scale, seq_of_row):
+    """fp8_lse_slack for host inputs ``inp`` and the oracle's prologue ``pro``
+    (its k and v written into copies of the pools)."""
+    kp, vp = (np.array(p, copy=True) for p in host_pools(inp, w))
+    apply_prologue_writes(kp, vp, pro, kv_dtype=w.kv_dtype, page_stride=inp["page_stride"],
+                          head_stride=inp["head_stride"])
+    h = host_step_inputs(inp)
+    return fp8_lse_slack(w, kp, h["block_table"], h["seq_lens"], inp["page_stride"],
+                         inp["head_stride"], pro["q_out"], q_scale, seq_of_row)

@@ -11,7 +11,7 @@ import torch
 
 import load_balanced_split_rope_amd as lb
 from load_balanced_split_rope_amd import workloads as wl
-from checks import check_output, poison_cache, to_f64
+from checks import check_output, poison_cache, to_f64, fp8_lse_slack, fp8_lse_slack_for
 from gpu_util import device, to_device, run_step, config_for
 from test_gpu_step import oracle_step
 from test_gpu_prefill import run_prefill, oracle_prefill
@@ -57,11 +57,13 @@ def test_decode_fp8_scores(case, sched):
     print(f"fp8 scores decode case {case} {sched}", flush=True)
     res = run_step(w, g, s, cfg=qk_cfg(w, g, COARSE))
     assert res["error"] == 0
-    _, ro, rl = oracle_step(w, inp, {"qk_dtype": "fp8", "q_scale": COARSE})
+    pro, ro, rl = oracle_step(w, inp, {"qk_dtype": "fp8", "q_scale": COARSE})
     got = to_f64(res["out"]).reshape(ro.shape)
     check_output(got, ro, "fp8", "fp8-score output")
     lse = to_f64(res["lse"]).reshape(rl.shape)
-    assert np.all(np.abs(lse - rl) <= 1e-4 + 1e-5 * np.abs(rl)), float(np.abs(lse - rl).max())
+    slack = fp8_lse_slack_for(inp, w, pro, COARSE, np.repeat(np.arange(w.batch), w.tokens))
+    assert np.all(np.abs(lse - rl) <= 1e-4 + 1e-5 * np.abs(rl) + slack.reshape(rl.shape)), \
+        float(np.abs(lse - rl).max())
     _, rb, _ = oracle_step(w, inp)
     closer_to_quantised(got, ro, rb)
 
@@ -73,9 +75,10 @@ def test_decode_fine_scale():
     inp = wl.make_inputs(w)
     g = to_device(inp, dev)
     res = run_step(w, g, lb.Schedule("dynamic", num_workers=64), cfg=qk_cfg(w, g, FINE))
-    _, ro, rl = oracle_step(w, inp, {"qk_dtype": "fp8", "q_scale": FINE})
+    pro, ro, rl = oracle_step(w, inp, {"qk_dtype": "fp8", "q_scale": FINE})
     check_output(to_f64(res["out"]), ro, "fp8", "fine-scale output")
-    assert np.all(np.abs(to_f64(res["lse"]) - rl) <= 1e-4 + 1e-5 * np.abs(rl))
+    slack = fp8_lse_slack_for(inp, w, pro, FINE, np.arange(w.batch))
+    assert np.all(np.abs(to_f64(res["lse"]) - rl) <= 1e-4 + 1e-5 * np.abs(rl) + slack)
 
 
 @pytest.mark.parametrize("case", [
@@ -93,11 +96,12 @@ def test_prefill_fp8_scores(case):
     g = to_device(inp, dev)
     res = run_prefill(w, g, qk_cfg(w, g, COARSE))
     assert res["error"] == 0
-    _, ro, rl = oracle_prefill(w, inp, {"qk_dtype": "fp8", "q_scale": COARSE})
+    pro, ro, rl = oracle_prefill(w, inp, {"qk_dtype": "fp8", "q_scale": COARSE})
     got = to_f64(res["out"]).reshape(ro.shape)
     check_output(got, ro, "fp8", "fp8-score prefill output")
     lse = to_f64(res["lse"]).reshape(rl.shape)
-    assert np.all(np.abs(lse - rl) <= 1e-4 + 1e-5 * np.abs(rl))
+    slack = fp8_lse_slack_for(inp, w, pro, COARSE, np.repeat(np.arange(w.batch), w.tokens))
+    assert np.all(np.abs(lse - rl) <= 1e-4 + 1e-5 * np.abs(rl) + slack.reshape(rl.shape))
     _, rb, _ = oracle_prefill(w, inp)
     closer_to_quantised(got, ro, rb)
 
@@ -110,8 +114,9 @@ def test_ragged_prefill_fp8_scores():
     g = to_device(inp, dev)
     res = run_varlen(w, g, cfg=qk_cfg(w, g, COARSE))
     assert res["error"] == 0
-    _, ref = oracle_varlen(w, inp, extra={"qk_dtype": "fp8", "q_scale": COARSE})
-    check_against(w, res, ref)
+    pro, ref = oracle_varlen(w, inp, extra={"qk_dtype": "fp8", "q_scale": COARSE})
+    seq_of_row = np.repeat(np.arange(w.batch), w.new_tokens)
+    check_against(w, res, ref, fp8_lse_slack_for(inp, w, pro, COARSE, seq_of_row))
 
 
 @pytest.mark.slow
@@ -136,6 +141,9 @@ def test_full_mix_fp8_scores_sampled():
     ref = oracle.decode_attention(pro["q_out"], (kp, vp), remap_slots(pro, pmap), h["seq_lens"],
                                   bt, cfg, seqs=seqs, heads=list(range(64)))
     out, lse = to_f64(res["out"]), to_f64(res["lse"])
+    # the cache as read back holds the step's new keys (bit-exact to the oracle's)
+    slack = fp8_lse_slack(w, kp, bt, h["seq_lens"], g["page_stride"], g["head_stride"],
+                          pro["q_out"], q_scale, np.arange(w.batch), seqs=seqs)
     for (b, hh), (o, l) in ref.items():
         check_output(out[b, hh], o, "fp8", f"seq {b} head {hh}")
-        assert abs(lse[b, hh] - l) <= 1e-4 + 1e-5 * abs(l)
+        assert abs(lse[b, hh] - l) <= 1e-4 + 1e-5 * abs(l) + slack[b, hh]

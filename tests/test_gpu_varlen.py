@@ -54,7 +54,9 @@ def oracle_varlen(w, inp, seqs=None, extra=None):
     return pro, ref
 
 
-def check_against(w, res, ref):
+def check_against(w, res, ref, lse_slack=None):
+    """res's output and lse rows against the oracle's; lse_slack [rows, Hq]: the
+    FP8-score term added to lse's bound (R23), per packed row."""
     starts = mt.query_starts(w.new_tokens)
     out, lse = to_f64(res["out"]), to_f64(res["lse"])
     rows = sorted({(b, j) for (b, j, _) in ref})
@@ -63,7 +65,8 @@ def check_against(w, res, ref):
         o_ref = np.stack([ref[(b, j, hh)][0] for hh in range(w.num_q_heads)])
         l_ref = np.array([ref[(b, j, hh)][1] for hh in range(w.num_q_heads)])
         check_output(out[r], o_ref, w.kv_dtype, f"seq {b} token {j}")
-        assert np.all(np.abs(lse[r] - l_ref) <= 1e-4 + 1e-5 * np.abs(l_ref)), (b, j)
+        slack = 0.0 if lse_slack is None else lse_slack[r]
+        assert np.all(np.abs(lse[r] - l_ref) <= 1e-4 + 1e-5 * np.abs(l_ref) + slack), (b, j)
 
 
 CASES = [

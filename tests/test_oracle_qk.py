@@ -87,3 +87,32 @@ def test_representable_queries_reduce_to_the_bf16_path():
         assert not np.array_equal(q2, qv[b])                     # re-rounded: values move
         o2, _ = oracle.attend_full(q2, K[b], V[b], 128 ** -0.5)
         assert np.abs(o2 - o0).max() > 1e-3
+
+
+def test_fp8_lse_slack_is_the_measured_bound_times_the_largest_product_sum():
+    """The FP8-score lse slack (R23's tolerance term for the FP8 matrix cores'
+    accumulation) equals 2^-15 * sm * max over the keys of sum_d |q_d k_d|:
+    brute force over a two-sequence step, both sequences, every head."""
+    import oracle
+    from load_balanced_split_rope_amd import workloads as wl
+    from checks import fp8_lse_slack_for, host_step_inputs, host_pools, FP8_SCORE_REL
+    from oracle.step import apply_prologue_writes, gather_kv
+    w = wl.custom([1, 70], num_q_heads=16, num_kv_heads=2, kv_dtype="fp8", seed=5)
+    inp = wl.make_inputs(w)
+    h = host_step_inputs(inp)
+    pro = oracle.prologue(h["q"], h["k"], h["v"], h["positions"], h["wq"], h["wk"],
+                          h["block_table"], theta=w.rope_theta, eps=w.rms_eps, kv_dtype="fp8",
+                          k_scale=w.k_scale, v_scale=w.v_scale)
+    got = fp8_lse_slack_for(inp, w, pro, 0.3, np.arange(2))
+    kp, vp = (np.array(p, copy=True) for p in host_pools(inp, w))
+    apply_prologue_writes(kp, vp, pro, kv_dtype="fp8", page_stride=inp["page_stride"],
+                          head_stride=inp["head_stride"])
+    qv = qk.query_values(pro["q_out"], {"qk_dtype": "fp8", "q_scale": 0.3})
+    for b in range(2):
+        L = int(h["seq_lens"][b])
+        for hh in range(16):
+            K = gather_kv(kp, "k", "fp8", h["block_table"][b], L, hh // 8,
+                          page_stride=inp["page_stride"], head_stride=inp["head_stride"],
+                          scale=float(np.float32(w.k_scale)))
+            want = max(np.sum(np.abs(qv[b, hh] * K[i])) for i in range(L))
+            assert np.isclose(got[b, hh], FP8_SCORE_REL / np.sqrt(128.0) * want, rtol=1e-12)
