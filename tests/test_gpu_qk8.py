@@ -147,3 +147,25 @@ def test_full_mix_fp8_scores_sampled():
     for (b, hh), (o, l) in ref.items():
         check_output(out[b, hh], o, "fp8", f"seq {b} head {hh}")
         assert abs(lse[b, hh] - l) <= 1e-4 + 1e-5 * abs(l) + slack[b, hh]
+
+
+@pytest.mark.parametrize("q_scale", [2.0 ** -6, 2.0 ** -5, 2.0 ** -3, COARSE])
+def test_fp8_score_error_within_the_accumulation_bound(q_scale):
+    """One-row sequences, so each lse is a single score: its error against the
+    oracle's exact dot product of the same codes stays within FP8_SCORE_REL
+    times sm * sum_d |q_d k_d| with no absolute floor (the bound the FP8-score
+    lse checks add), and the BF16-score step on the same inputs is exact to
+    fp32 rounding."""
+    dev = device()
+    w = wl.custom([1] * 64, num_q_heads=64, num_kv_heads=8, kv_dtype="fp8", seed=4242)
+    inp = wl.make_inputs(w)
+    g = to_device(inp, dev)
+    res = run_step(w, g, lb.Schedule("dynamic", num_workers=256), cfg=qk_cfg(w, g, q_scale))
+    assert res["error"] == 0
+    pro, _, rl = oracle_step(w, inp, {"qk_dtype": "fp8", "q_scale": q_scale})
+    slack = fp8_lse_slack_for(inp, w, pro, q_scale, np.arange(w.batch))
+    err = np.abs(to_f64(res["lse"]) - rl)
+    assert np.all(err <= slack), float(np.max(err / slack))
+    rb = run_step(w, to_device(inp, dev), lb.Schedule("dynamic", num_workers=256))
+    _, _, lb16 = oracle_step(w, inp)
+    assert np.max(np.abs(to_f64(rb["lse"]) - lb16)) < 2e-6
