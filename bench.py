@@ -250,6 +250,46 @@ def prefill_flops(w):
     return 4 * 128 * w.num_q_heads * tot
 
 
+def pack_leg(dev, reps=10):
+    """lbsr_pack_cache and lbsr_unpack_cache on the mix's K pool (BF16, 8 KV
+    heads) from a token-major row-major copy: HIP events on the launch stream,
+    median of `reps`; each call reads and writes every byte of the pool once,
+    so its roofline is 2 x pool bytes against HBM peak; a plain device copy of
+    the same pool (torch's copy kernel) is timed beside it for reference."""
+    w = wl.named("mix")
+    heads = w.num_kv_heads
+    g = wl.make_inputs(w, device=dev)
+    pages = g["num_pages"]
+    cfg = lb.DecodeConfig(w.num_q_heads, heads, "bf16", g["max_blocks"], pages)
+    rows = torch.empty((pages, 64, heads, 128), dtype=torch.bfloat16, device=dev)
+    lb.unpack_cache(cfg, "k", g["k_cache"], rows)
+    pool = torch.empty_like(g["k_cache"])
+    out = {}
+    for name, fn in (("pack", lambda: lb.pack_cache(cfg, "k", rows, pool)),
+                     ("unpack", lambda: lb.unpack_cache(cfg, "k", pool, rows)),
+                     ("plain_copy", lambda: pool.copy_(g["k_cache"]))):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        t = float(np.median(ts))
+        nbytes = 2 * pool.numel() * pool.element_size()
+        out[name] = {"us": round(t * 1e6, 1), "GBs": round(nbytes / t / 1e9, 1),
+                     "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    lb.pack_cache(cfg, "k", rows, pool)
+    ok = torch.equal(pool.view(torch.int16), g["k_cache"].view(torch.int16))
+    del g, rows, pool
+    torch.cuda.empty_cache()
+    return {"workload": f"the mix's K pool, {pages} pages x {heads} KV heads, BF16 "
+                        f"({2 * pages * heads * 16384 / 1e6:.0f} MB moved per call)",
+            "round_trip_exact": ok, **out}
+
+
 def prefill_leg(dev, reps=10, warmup=3, names=None):
     """lbsr_prefill_step (prologue + attention) and lbsr_prefill_attention alone,
     each timed with HIP events on the launch stream; the attention kernel is
@@ -502,6 +542,8 @@ def main():
     ap.add_argument("--prefill-names", default="",
                     help="with --prefill-only: comma-separated prefill workloads to run "
                          "(BF16 scores only), e.g. 'prefill' for a counter pass")
+    ap.add_argument("--pack-only", action="store_true",
+                    help="run only the cache pack/unpack leg and print it")
     ap.add_argument("--no-xcd-weights", action="store_true",
                     help="equal worker shares only (skip the per-XCD rate calibration)")
     ap.add_argument("--quick", action="store_true",
@@ -524,6 +566,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": 5}))
+        return
+    if args.pack_only:
+        print(json.dumps({"pack_cache": pack_leg(dev)}), flush=True)
         return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_leg(dev, names=prefill_names or None)}), flush=True)
@@ -698,6 +743,7 @@ def main():
                 "step_time_vs_bf16_scores": round(rq["ms"] / ms8, 4),
             }
             result["prefill"] = prefill_leg(dev)
+            result["pack_cache"] = pack_leg(dev)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(w, dev)
     print(json.dumps(result), flush=True)

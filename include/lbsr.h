@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LBSR_ABI_VERSION 6
+#define LBSR_ABI_VERSION 7
 #define LBSR_NUM_XCDS 8     /* accelerator complex dies of an MI355X */
 #define LBSR_MAX_XCD_WEIGHT 65536
 #define LBSR_HEAD_DIM 128
@@ -85,6 +85,9 @@ typedef enum { LBSR_OUT_BF16 = 0, LBSR_OUT_FP8_E4M3 = 1 } lbsr_out_dtype;
  * S = sum over channels of code_q * code_k on FP8 matrix cores (16x16x128),
  * times q_scale * k_scale * sm_scale.  P.V is the same in both. */
 typedef enum { LBSR_QK_BF16 = 0, LBSR_QK_FP8_E4M3 = 1 } lbsr_qk_dtype;
+/* which pool lbsr_pack_cache / lbsr_unpack_cache convert: K and V tiles
+ * order their elements differently */
+typedef enum { LBSR_CACHE_K = 0, LBSR_CACHE_V = 1 } lbsr_cache_kind;
 
 /* Sticky device error bits (int32 at lbsr_ws_layout.error_word). */
 #define LBSR_DEV_ERR_SEQ_LEN 1   /* seq_len outside [1, max_blocks_per_seq*64]: clamped */
@@ -537,6 +540,43 @@ lbsr_status lbsr_read_device_error(const void *workspace, int32_t *code, void *s
  */
 lbsr_status lbsr_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t mode,
                              uint32_t *sink, void *stream);
+
+/*
+ * Cache layout conversion, for callers whose paged cache is a plain row-major
+ * array.  [A] "Why does dynamic scheduling matter in attention?" fixes the
+ * 64-token page as the unit the cache is read in; the element order inside a
+ * page (the "cache page layout" above) is this library's own, so such a
+ * caller repacks its pool once with lbsr_pack_cache and can read it back with
+ * lbsr_unpack_cache.
+ *
+ * The row-major form: element (page p, token row r in [0,64), KV head g,
+ * channel d) at  p * row_page_stride + r * row_token_stride
+ *                + g * row_head_stride + d  elements from `rows`.
+ * Channels are contiguous; any order of the other three axes works (e.g.
+ * token-major [pages][64][Hkv][128]: strides 64*Hkv*128, Hkv*128, 128;
+ * head-major [pages][Hkv][64][128]: Hkv*64*128, 128, 64*128).  The strides
+ * must be positive, their byte sizes multiples of 16, and no two (page, row,
+ * head) rows may overlap (sorted by stride, each stride at least the extent
+ * of the axes below it); else LBSR_E_INVALID.
+ *
+ * `cache` is a pool of the library's layout with shape->num_pages pages,
+ * shape->page_stride and shape->head_stride; every (page, KV head) tile of it
+ * is converted.  The element type is shape->kv_dtype: BF16, or E4M3 codes
+ * moved as bytes (no scale is applied: the codes must already be those of
+ * the cache's per-tensor scale).  `kind` (lbsr_cache_kind) selects K or V.
+ * Device pointers, 16-byte aligned; `rows` and `cache` must not overlap.
+ * The shape is validated as for the other calls (with a batch of 1).
+ * Asynchronous on `stream`; the library allocates nothing.
+ */
+lbsr_status lbsr_pack_cache(const lbsr_shape *shape, int32_t kind, const void *rows,
+                            int64_t row_page_stride, int64_t row_token_stride,
+                            int64_t row_head_stride, void *cache, void *stream);
+
+/* The inverse of lbsr_pack_cache: every tile of `cache` written back to the
+ * row-major `rows` (same arguments and checks). */
+lbsr_status lbsr_unpack_cache(const lbsr_shape *shape, int32_t kind, const void *cache,
+                              void *rows, int64_t row_page_stride, int64_t row_token_stride,
+                              int64_t row_head_stride, void *stream);
 
 #ifdef __cplusplus
 }

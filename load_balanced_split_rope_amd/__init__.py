@@ -13,7 +13,7 @@ from .decode import (DecodeConfig, Schedule, device_workers, workspace_layout,
                      xcd_weights_from_rates, prefill_attention, prefill_step,
                      prefill_attention_varlen, prefill_step_varlen,
                      prefill_workspace_size, alloc_prefill_workspace, stream_read,
-                     decode_step_noalloc)
+                     decode_step_noalloc, pack_cache, unpack_cache)
 
 __all__ = [
     "LbsrError", "LibraryNotBuilt", "EXPORTS", "LIB_PATH", "DecodeConfig", "Schedule",
@@ -21,5 +21,5 @@ __all__ = [
     "attention", "decode_step", "decode_step_timed", "read_plan", "read_error", "xcd_rates",
     "xcd_weights_from_rates", "prefill_attention", "prefill_step", "prefill_attention_varlen",
     "prefill_step_varlen", "prefill_workspace_size", "alloc_prefill_workspace", "stream_read",
-    "decode_step_noalloc",
+    "decode_step_noalloc", "pack_cache", "unpack_cache",
 ]

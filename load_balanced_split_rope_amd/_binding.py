@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # LBSR_LIB may name another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("LBSR_LIB") or os.path.join(HERE, "liblbsr.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 HEAD_DIM = 128
 PAGE_SIZE = 64
 TILE_ELEMS = HEAD_DIM * PAGE_SIZE
@@ -39,7 +39,7 @@ EXPORTS = (
     "lbsr_attention", "lbsr_decode_step", "lbsr_decode_step_timed", "lbsr_prefill_attention",
     "lbsr_prefill_step", "lbsr_prefill_attention_varlen", "lbsr_prefill_step_varlen",
     "lbsr_prefill_workspace_size", "lbsr_read_plan", "lbsr_read_device_error",
-    "lbsr_stream_read", "lbsr_decode_step_noalloc",
+    "lbsr_stream_read", "lbsr_decode_step_noalloc", "lbsr_pack_cache", "lbsr_unpack_cache",
 )
 
 
@@ -144,6 +144,10 @@ def _declare(lib):
         "lbsr_stream_read": (st, [_P, ctypes.c_size_t, _I32, _I32, _P, _P]),
         "lbsr_decode_step_noalloc": (st, [ctypes.POINTER(Shape), ctypes.POINTER(Params), _I32]
                                      + [_P] * 11 + [ctypes.POINTER(SchedCfg), _P, _P, _P]),
+        "lbsr_pack_cache": (st, [ctypes.POINTER(Shape), _I32, _P, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int64, _P, _P]),
+        "lbsr_unpack_cache": (st, [ctypes.POINTER(Shape), _I32, _P, _P, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int64, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

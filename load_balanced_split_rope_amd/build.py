@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblbsr.so")
 SOURCES = ["api.hip", "prologue.hip", "plan.hip", "step.hip", "attention.hip", "prefill.hip",
-           "stream_read.hip"]
+           "stream_read.hip", "pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -899,6 +899,81 @@ lbsr_status lbsr_stream_read(const void* buf, size_t bytes, int32_t workgroups, 
                     "stream_read_kernel launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// The row-major form of lbsr_pack_cache / lbsr_unpack_cache: positive
+// strides whose byte sizes are multiples of 16, and no two (page, row, head)
+// rows overlapping -- with the axes sorted by stride, each stride at least
+// the extent of the axes below it (a 128-channel row first).
+lbsr_status check_rows(const lbsr_shape* s, int32_t kind, const void* rows, const void* cache,
+                       int64_t ps, int64_t ts, int64_t hs) {
+  LBSR_CHECK(check_shape(s, 1));
+  if (kind != LBSR_CACHE_K && kind != LBSR_CACHE_V)
+    return fail(LBSR_E_INVALID, "kind %d is not LBSR_CACHE_K or LBSR_CACHE_V", kind);
+  LBSR_CHECK(check_ptr(rows, 16, "rows"));
+  LBSR_CHECK(check_ptr(cache, 16, "cache"));
+  const int64_t elem = s->kv_dtype == LBSR_KV_BF16 ? 2 : 1;
+  const int64_t strides[3] = {ps, ts, hs};
+  const int64_t extents[3] = {s->num_pages, LBSR_PAGE_SIZE, s->num_kv_heads};
+  const char* names[3] = {"row_page_stride", "row_token_stride", "row_head_stride"};
+  for (int i = 0; i < 3; ++i) {
+    if (strides[i] <= 0 || strides[i] > ((int64_t)1 << 40) || (strides[i] * elem) % 16)
+      return fail(LBSR_E_INVALID, "%s %lld must be positive, below 2^40, and %lld-element aligned",
+                  names[i], (long long)strides[i], (long long)(16 / elem));
+  }
+  int order[3] = {0, 1, 2};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (strides[order[j]] < strides[order[i]]) { const int t = order[i]; order[i] = order[j]; order[j] = t; }
+  int64_t reach = LBSR_HEAD_DIM;   // elements one row spans
+  for (int i = 0; i < 3; ++i) {
+    const int a = order[i];
+    if (extents[a] > 1 && strides[a] < reach)
+      return fail(LBSR_E_INVALID, "%s %lld overlaps the %lld elements below it", names[a],
+                  (long long)strides[a], (long long)reach);
+    if (extents[a] > 1) reach = strides[a] * extents[a];
+  }
+  // the farthest element must be addressable
+  const int64_t last = (s->num_pages - 1) * ps + (LBSR_PAGE_SIZE - 1) * ts +
+                       (int64_t)(s->num_kv_heads - 1) * hs + LBSR_HEAD_DIM;
+  if (last > ((int64_t)1 << 46)) return fail(LBSR_E_INVALID, "row-major extent too large");
+  return LBSR_OK;
+}
+
+lbsr_status pack_common(bool pack, const lbsr_shape* shape, int32_t kind, const void* src,
+                        void* dst, const void* rows, const void* cache, int64_t ps, int64_t ts,
+                        int64_t hs, void* stream) {
+  g_last_error[0] = 0;
+  LBSR_CHECK(check_rows(shape, kind, rows, cache, ps, ts, hs));
+  DeviceInfo d;
+  LBSR_CHECK(current_device(&d));
+  return hip_status(lbsr::launch_pack(shape->kv_dtype == LBSR_KV_FP8_E4M3, kind == LBSR_CACHE_V,
+                                      pack, src, dst, shape->num_pages, shape->num_kv_heads,
+                                      shape->page_stride, shape->head_stride, ps, ts, hs,
+                                      (hipStream_t)stream),
+                    pack ? "pack_kernel launch" : "unpack kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+lbsr_status lbsr_pack_cache(const lbsr_shape* shape, int32_t kind, const void* rows,
+                            int64_t row_page_stride, int64_t row_token_stride,
+                            int64_t row_head_stride, void* cache, void* stream) {
+  return pack_common(true, shape, kind, rows, cache, rows, cache, row_page_stride,
+                     row_token_stride, row_head_stride, stream);
+}
+
+lbsr_status lbsr_unpack_cache(const lbsr_shape* shape, int32_t kind, const void* cache,
+                              void* rows, int64_t row_page_stride, int64_t row_token_stride,
+                              int64_t row_head_stride, void* stream) {
+  return pack_common(false, shape, kind, cache, rows, rows, cache, row_page_stride,
+                     row_token_stride, row_head_stride, stream);
+}
+
 lbsr_status lbsr_read_device_error(const void* workspace, int32_t* code, void* stream) {
   g_last_error[0] = 0;
   if (!code) return fail(LBSR_E_INVALID, "code is NULL");

@@ -69,4 +69,11 @@ int64_t stream_read_block_bytes();
 hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, int mode,
                               uint32_t* sink, hipStream_t stream);
 
+// Cache layout conversion: pack (rows -> tiles) or unpack (tiles -> rows) of
+// every (page, KV head) tile; strides in elements, checked on the host.
+hipError_t launch_pack(bool fp8, bool v, bool pack, const void* src, void* dst, int64_t num_pages,
+                       int num_kv_heads, int64_t tile_page_stride, int64_t tile_head_stride,
+                       int64_t row_page_stride, int64_t row_token_stride, int64_t row_head_stride,
+                       hipStream_t stream);
+
 }  // namespace lbsr

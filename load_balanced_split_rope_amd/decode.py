@@ -499,6 +499,48 @@ def stream_read(buf, sink, workgroups=0, mode=0, stream=None):
                                       B._ptr(sink), B._stream(stream)))
 
 
+_ROW_AXES = {"NHD": (0, 1, 2), "HND": (0, 2, 1)}   # (page, token, head) axis of each form
+_KINDS = {"k": 0, "v": 1}
+
+
+def _row_strides(cfg, rows, layout):
+    """Element strides (page, token, head) of a row-major cache view: a tensor
+    [num_pages, 64, Hkv, 128] ("NHD") or [num_pages, Hkv, 64, 128] ("HND") of
+    the cache dtype, with contiguous channels (other strides are free)."""
+    if layout not in _ROW_AXES:
+        raise ValueError(f"layout must be 'NHD' or 'HND', not {layout!r}")
+    pa, ta, ha = _ROW_AXES[layout]
+    want = [cfg.num_pages, 0, 0, B.HEAD_DIM]
+    want[ta], want[ha] = B.PAGE_SIZE, cfg.num_kv_heads
+    if not isinstance(rows, torch.Tensor) or not rows.is_cuda or rows.dtype != cfg.cache_dtype:
+        raise ValueError(f"rows must be a device tensor of {cfg.cache_dtype}")
+    if tuple(rows.shape) != tuple(want) or rows.stride(3) != 1:
+        raise ValueError(f"rows must be {layout} {tuple(want)} with contiguous channels, "
+                         f"got {tuple(rows.shape)} strides {rows.stride()}")
+    st = rows.stride()
+    return st[pa], st[ta], st[ha]
+
+
+def pack_cache(cfg: DecodeConfig, kind, rows, cache, layout="NHD", stream=None):
+    """lbsr_pack_cache: a row-major paged K or V cache (``kind`` "k" or "v";
+    ``rows`` a [num_pages, 64, Hkv, 128] "NHD" or [num_pages, Hkv, 64, 128]
+    "HND" view, any strides with contiguous channels) into ``cache``, a pool of
+    the library's tile layout with cfg's geometry.  Asynchronous."""
+    ps, ts, hs = _row_strides(cfg, rows, layout)
+    _need(cache, "cache", cfg.cache_dtype, numel=cfg.pool_elems())
+    B._check(B.lib().lbsr_pack_cache(ctypes.byref(cfg._shape()), _KINDS[kind], B._ptr(rows),
+                                     ps, ts, hs, B._ptr(cache), B._stream(stream)))
+
+
+def unpack_cache(cfg: DecodeConfig, kind, cache, rows, layout="NHD", stream=None):
+    """lbsr_unpack_cache: the inverse of pack_cache (``rows`` receives the
+    row-major form).  Asynchronous."""
+    ps, ts, hs = _row_strides(cfg, rows, layout)
+    _need(cache, "cache", cfg.cache_dtype, numel=cfg.pool_elems())
+    B._check(B.lib().lbsr_unpack_cache(ctypes.byref(cfg._shape()), _KINDS[kind], B._ptr(cache),
+                                       B._ptr(rows), ps, ts, hs, B._stream(stream)))
+
+
 def xcd_rates(traces, plans):
     """Measured tile rate (tiles per microsecond of busy time) of each XCD.
 

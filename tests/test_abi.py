@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.lbsr_abi_version() == 6
+    assert lib.lbsr_abi_version() == 7
     for st in range(5):
         assert lib.lbsr_status_string(st).startswith(b"LBSR_")
     assert lib.lbsr_status_string(99) == b"unknown lbsr_status"
@@ -491,3 +491,38 @@ def test_config_structs_follow_field_changes():
     before = sched.cfg()
     sched.num_workers = 7
     assert sched.cfg().num_workers == 7 and before.num_workers == 5
+
+
+def test_pack_cache_validates_before_any_launch(lib):
+    """lbsr_pack_cache / lbsr_unpack_cache check the kind, the pointers and the
+    row-major strides (positive, 16-byte multiples, rows not overlapping) on
+    the host: each refusal comes back without touching a device, and a valid
+    call gets past validation (it fails only where a device is needed)."""
+    cfg = DecodeConfig(64, 8, "bf16", 4, 100)
+    s = cfg.shape()
+    fake, odd, nul = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10008), ctypes.c_void_p(0)
+    H = 8
+    nhd = (64 * H * 128, H * 128, 128)        # token-major rows
+    hnd = (H * 64 * 128, 128, 64 * 128)       # head-major rows
+    for fn in (lib.lbsr_pack_cache, lib.lbsr_unpack_cache):
+        def call(kind=0, a=fake, b=fake, st=nhd, shape=s):
+            return fn(ctypes.byref(shape), kind, a, *st, b, nul) if fn is lib.lbsr_pack_cache \
+                else fn(ctypes.byref(shape), kind, a, b, *st, nul)
+        assert call(kind=2) == B.E_INVALID and b"kind" in lib.lbsr_last_error()
+        assert call(a=nul) == B.E_INVALID
+        assert call(b=odd) == B.E_INVALID and b"aligned" in lib.lbsr_last_error()
+        assert call(st=(nhd[0], nhd[1], 4)) == B.E_INVALID          # 8-byte head stride
+        assert call(st=(nhd[0], 0, 128)) == B.E_INVALID             # zero token stride
+        assert call(st=(nhd[0], 128, 128)) == B.E_INVALID           # token and head rows collide
+        assert b"overlaps" in lib.lbsr_last_error()
+        assert call(st=(64 * 128, H * 128, 128)) == B.E_INVALID     # pages overlap
+        bad = DecodeConfig(64, 8, "bf16", 4, 100).shape()
+        bad.head_dim = 64
+        assert call(shape=bad) == B.E_UNSUPPORTED
+        for st in (nhd, hnd, (2 * nhd[0], 2 * nhd[1], 2 * 128)):    # padded rows are fine
+            got = call(st=st)
+            assert got not in (B.E_INVALID, B.E_UNSUPPORTED), lib.lbsr_last_error()
+    # FP8 rows: one-byte elements, 16-element alignment
+    s8 = DecodeConfig(64, 8, "fp8", 4, 100).shape()
+    assert lib.lbsr_pack_cache(ctypes.byref(s8), 1, fake, 64 * H * 128, H * 128, 120, fake,
+                               nul) == B.E_INVALID
