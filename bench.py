@@ -430,7 +430,8 @@ def cpu_baseline(w, dev, min_seconds=10.0):
 
 def stream_ceiling(dev, nbytes=1 << 30, launches=10):
     """The streaming-read ceiling over 1 GiB: the probe (lbsr_stream_read) in
-    the split kernel's load pattern and as a plain sweep, over a few grid
+    the split kernel's load pattern, as a plain sweep, and in the split
+    kernel's pattern with the bytes going straight into LDS, over a few grid
     sizes; each timed as `launches` back-to-back launches between two HIP
     events on the launch stream (the median of three such runs).  The best
     rate is the ceiling; every variant is reported."""
@@ -438,7 +439,10 @@ def stream_ceiling(dev, nbytes=1 << 30, launches=10):
     sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
     st = torch.cuda.current_stream()
     P = lb.device_workers(0)
-    variants = [(0, P), (0, 2 * P), (1, 4 * P), (1, 8 * P)]
+    variants = [(0, P), (0, 2 * P), (1, 4 * P), (1, 8 * P), (2, P), (2, 2 * P)]
+    labels = {0: "split-kernel pattern (32 KiB bursts, waves in lockstep)",
+              1: "plain sweep (8 loads in flight per thread)",
+              2: "global-to-LDS loads (16 KiB bursts into LDS, waves in lockstep)"}
     rows = []
     for mode, wg in variants:
         for _ in range(2):
@@ -453,9 +457,7 @@ def stream_ceiling(dev, nbytes=1 << 30, launches=10):
             e1.synchronize()
             runs.append(e0.elapsed_time(e1) / launches)
         ms = float(np.median(runs))
-        rows.append({"mode": "split-kernel pattern (32 KiB bursts, waves in lockstep)" if mode == 0
-                     else "plain sweep (8 loads in flight per thread)",
-                     "workgroups": wg, "us_per_GiB": round(ms * 1e3, 2),
+        rows.append({"mode": labels[mode], "workgroups": wg, "us_per_GiB": round(ms * 1e3, 2),
                      "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
     del buf, sink
     torch.cuda.empty_cache()

@@ -534,9 +534,11 @@ lbsr_status lbsr_read_device_error(const void *workspace, int32_t *code, void *s
  * (device, uint32[workgroups]).  mode 0 reads the way the split-attention
  * kernel reads K/V tiles: one 32 KiB burst per wave, the 8 waves meeting at a
  * barrier after each burst is issued.  mode 1 is a plain sweep: every thread
- * keeps 8 loads in flight, one grid-width apart, with no barriers.  The best
- * rate over modes and grid sizes is the streaming ceiling the split kernel's
- * bandwidth is reported against.  Asynchronous on `stream`.
+ * keeps 8 loads in flight, one grid-width apart, with no barriers.  mode 2 is
+ * mode 0 with 16 KiB bursts loaded straight into LDS (global-to-LDS loads,
+ * 128 KiB of LDS per workgroup) and read back from there.  The best rate over
+ * modes and grid sizes is the streaming ceiling the split kernel's bandwidth
+ * is reported against.  Asynchronous on `stream`.
  */
 lbsr_status lbsr_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t mode,
                              uint32_t *sink, void *stream);

@@ -891,7 +891,7 @@ lbsr_status lbsr_stream_read(const void* buf, size_t bytes, int32_t workgroups, 
                 (long long)blk);
   if (workgroups < 0 || workgroups > (1 << 20))
     return fail(LBSR_E_INVALID, "workgroups %d outside [0, 2^20]", workgroups);
-  if (mode != 0 && mode != 1) return fail(LBSR_E_INVALID, "mode %d is not 0 or 1", mode);
+  if (mode < 0 || mode > 2) return fail(LBSR_E_INVALID, "mode %d is not 0, 1 or 2", mode);
   DeviceInfo d;
   LBSR_CHECK(current_device(&d));
   const int wg = workgroups ? workgroups : d.cu_count;

@@ -487,7 +487,8 @@ def stream_read(buf, sink, workgroups=0, mode=0, stream=None):
     """The streaming-read probe (lbsr_stream_read): reads all of ``buf`` (a
     device tensor whose size is a multiple of 32 KiB); ``sink`` is a device
     buffer of at least ``workgroups`` (or CU count) 32-bit words.  mode 0: the
-    split kernel's load pattern; 1: a plain grid-wide sweep.  Asynchronous."""
+    split kernel's load pattern; 1: a plain grid-wide sweep; 2: mode 0's
+    bursts loaded straight into LDS.  Asynchronous."""
     if buf.device.type != "cuda" or sink.device.type != "cuda":
         raise ValueError("stream_read needs device tensors")
     if sink.dtype not in (torch.int32, torch.uint32) or not sink.is_contiguous():

@@ -20,7 +20,7 @@ def xor_all(t):
     return int(np.bitwise_xor.reduce(t.cpu().numpy().view(np.uint32).ravel()))
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("blocks,workgroups", [(1, 1), (1000, 0), (1000, 7), (1000, 256),
                                                (4099, 1000), (64, 2048)])
 def test_stream_read_reads_every_byte_once(mode, blocks, workgroups):
