@@ -400,7 +400,7 @@ def test_stream_read_validates_before_any_launch(lib):
                        ((fake, 0, 0, 0, sink, None), B.E_INVALID),
                        ((fake, (1 << 15) + 16, 0, 0, sink, None), B.E_INVALID),
                        ((fake, 1 << 15, -1, 0, sink, None), B.E_INVALID),
-                       ((fake, 1 << 15, 0, 2, sink, None), B.E_INVALID)]:
+                       ((fake, 1 << 15, 0, 3, sink, None), B.E_INVALID)]:
         assert lib.lbsr_stream_read(*args) == want, lib.lbsr_last_error()
 
 
