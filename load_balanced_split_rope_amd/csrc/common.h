@@ -15,7 +15,8 @@ constexpr int kMaxColumns = 64;    // (new token, q head) pairs per KV head: 4 c
 constexpr int kMaxTokensPerSeq = 1 << 18;  // new tokens per sequence (prefill)
 
 // Prefill workgroups: 8 waves, each with kPrefillBlocks blocks of 16 (token,
-// head) columns; every K/V fragment a wave reads from LDS feeds all its blocks.
+// head) columns (kPrefillBlocksQk8 with FP8 scores, whose operands leave room
+// for a third); every K/V fragment a wave reads from LDS feeds all its blocks.
 #ifndef LBSR_PREFILL_WAVES
 #define LBSR_PREFILL_WAVES 8
 #endif
@@ -24,7 +25,13 @@ constexpr int kPrefillWaves = LBSR_PREFILL_WAVES;
 #define LBSR_PREFILL_BLOCKS 2
 #endif
 constexpr int kPrefillBlocks = LBSR_PREFILL_BLOCKS;
-constexpr int kPrefillColumns = kPrefillWaves * 16 * kPrefillBlocks;   // per workgroup
+constexpr int kPrefillBlocksQk8 = 3;
+// (token, head) columns per workgroup; the narrower width bounds the work list
+constexpr int kPrefillColumns = kPrefillWaves * 16 * kPrefillBlocks;
+__host__ __device__ constexpr int prefill_columns(bool qk8) {
+  return kPrefillWaves * 16 * (qk8 ? kPrefillBlocksQk8 : kPrefillBlocks);
+}
+static_assert(kPrefillBlocksQk8 >= kPrefillBlocks, "work lists are sized for the narrower width");
 constexpr int kPrefillBuckets = 4096;  // tile-count buckets of the ragged prefill's work list
 constexpr int kPrefillListOffset = 256;  // work list after a 256-byte header in its workspace
 constexpr int kMergeLdsBytes = 65536;  // the merge stages chunks x columns weights in LDS

@@ -51,8 +51,9 @@ hipError_t launch_prefill(const Geometry& geo, bool fp8, bool out_fp8, const voi
                           const int32_t* q_start, int total_tokens, int32_t* work, bool qk_fp8,
                           float inv_q_scale, hipStream_t stream);
 
-// Work-list entries a ragged prefill may need: one per block of new tokens.
-int prefill_max_items(const Geometry& geo, int total_tokens);
+// Work-list entries a ragged prefill may need: one per block of new tokens,
+// blocks of `columns` (token, head) columns (kPrefillColumns bounds them all).
+int prefill_max_items(const Geometry& geo, int total_tokens, int columns = kPrefillColumns);
 
 hipError_t launch_plan_prologue(const int32_t* seq_lens, const SchedParams& sp,
                                 const PlanPtrs& plan, const Geometry& geo,
