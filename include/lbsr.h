@@ -350,8 +350,8 @@ lbsr_status lbsr_decode_step(const lbsr_shape *shape, const lbsr_params *params,
  * and v already in the cache) attends rows [0, L_b - Tq + t]:
  *   out[b][t][h]     = sum_j softmax_j(sm_scale * <q_out[b][t][h], K_j>) V_j
  *   lse_out[b][t][h] = ln sum_j exp(sm_scale * <q_out[b][t][h], K_j>)
- * One pass per (sequence, KV head, block of 256/G new tokens) over its causal
- * range, each K/V tile read once per block.
+ * One pass per (sequence, KV head, block of 256/G new tokens; 384/G with FP8
+ * scores) over its causal range, each K/V tile read once per block.
  *   q_out [batch][Tq][Hq][128] BF16        seq_lens [batch] int32 (device)
  *   out   [batch][Tq][Hq][128] BF16, or E4M3 codes (params->out_dtype)
  *   lse_out nullable float[batch][Tq][Hq]  error_word nullable int32*
@@ -401,7 +401,8 @@ lbsr_status lbsr_prefill_step(const lbsr_shape *shape, const lbsr_params *params
  * workspace: device memory of lbsr_prefill_workspace_size bytes (required here),
  * 256-byte aligned, caller-owned, overwritten by every call (so calls that
  * share one must be ordered).  A first launch writes there the list of
- * (sequence, block of 256/G new tokens) work items grouped by sequence: the
+ * (sequence, block of 256/G new tokens, 384/G with FP8 scores) work items
+ * grouped by sequence: the
  * sequences by the rows their longest item attends, longest first, and each
  * sequence's items from its last block (the longest) down, so that blocks
  * which read the same prefix tiles run side by side and share them in L2.
@@ -426,7 +427,8 @@ lbsr_status lbsr_prefill_attention_varlen(const lbsr_shape *shape, const lbsr_pa
 
 /* Bytes of a prefill's workspace (its sorted work list): 256 + 8 *
  * (ceil(total_tokens * G / 256) + batch), total_tokens = the packed count of
- * a ragged batch, or batch * tokens_per_seq for the uniform calls.  Host only. */
+ * a ragged batch, or batch * tokens_per_seq for the uniform calls (sized for
+ * the narrower blocks, so it also holds the FP8-score list).  Host only. */
 lbsr_status lbsr_prefill_workspace_size(const lbsr_shape *shape, int32_t batch,
                                         int32_t total_tokens, size_t *bytes);
 
