@@ -402,9 +402,9 @@ lbsr_status lbsr_prefill_step(const lbsr_shape *shape, const lbsr_params *params
  * 256-byte aligned, caller-owned, overwritten by every call (so calls that
  * share one must be ordered).  A first launch writes there the list of
  * (sequence, block of 256/G new tokens, 384/G with FP8 scores) work items
- * grouped by sequence: the
- * sequences by the rows their longest item attends, longest first, and each
- * sequence's items from its last block (the longest) down, so that blocks
+ * grouped by sequence: the sequences by the rows their longest item attends,
+ * longest first, and each sequence's items from its last block (the longest)
+ * down, so that blocks
  * which read the same prefix tiles run side by side and share them in L2.
  * The attention launch runs one workgroup per (item, KV head) in that
  * order.  (Workgroups reach compute units in a fixed
