@@ -85,3 +85,51 @@ def test_random_ragged_prefill(i):
     pro, ref = oracle_varlen(w, inp)
     assert np.array_equal(bits_u16(res["q_out"]), pro["q_out"])
     check_against(w, res, ref)
+
+
+def draw_prefill(i):
+    rng = np.random.default_rng(11000 + i)
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    batch = int(rng.integers(1, 5))
+    tokens = int(rng.choice([1, 2, 17, 31, 32, 33, 47, 48, 49, 64, 65, 130, 300]))
+    lens = [tokens + int(rng.choice([0, 0, 1, 63, 64, 65, 700, 3000])) for _ in range(batch)]
+    kv = "fp8" if rng.random() < 0.5 else "bf16"
+    qk = "fp8" if kv == "fp8" and rng.random() < 0.5 else "bf16"
+    w = wl.custom(lens, num_q_heads=hq, num_kv_heads=hkv, kv_dtype=kv, seed=11000 + i,
+                  tokens=tokens, norm_before_rope=bool(rng.random() < 0.25))
+    return w, qk, bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_uniform_prefill(i):
+    """Uniform prefill (every sequence the same count of new tokens, block
+    widths of 256/G and, with FP8 scores, 384/G columns crossed at random) vs
+    the oracle: q_out bits, outputs and lse (FP8 scores: with the matrix
+    cores' accumulation term), with and without the work list."""
+    from test_gpu_prefill import run_prefill, oracle_prefill
+    from checks import check_output, to_f64, fp8_lse_slack_for
+    from gpu_util import config_for
+    dev = device()
+    w, qk, listed = draw_prefill(i)
+    inp = wl.make_inputs(w)
+    poison_cache(inp, w)
+    g = to_device(inp, dev)
+    cfg = config_for(w, g)
+    extra = None
+    if qk == "fp8":
+        cfg.qk_dtype, cfg.q_scale = "fp8", 2.0 ** -5
+        extra = {"qk_dtype": "fp8", "q_scale": 2.0 ** -5}
+    print(f"random prefill case {i}: lens {w.seq_lens} tokens {w.tokens} "
+          f"{w.num_q_heads}q/{w.num_kv_heads}kv {w.kv_dtype} scores {qk} list {listed}", flush=True)
+    res = run_prefill(w, g, cfg, sorted_list=listed)
+    assert res["error"] == 0
+    pro, ro, rl = oracle_prefill(w, inp, extra)
+    assert np.array_equal(bits_u16(res["q_out"]).reshape(-1), pro["q_out"].reshape(-1))
+    check_output(to_f64(res["out"]).reshape(ro.shape), ro, w.kv_dtype, "random prefill output")
+    slack = 0.0
+    if qk == "fp8":
+        slack = fp8_lse_slack_for(inp, w, pro, 2.0 ** -5,
+                                  np.repeat(np.arange(w.batch), w.tokens)).reshape(rl.shape)
+    lse = to_f64(res["lse"]).reshape(rl.shape)
+    assert np.all(np.abs(lse - rl) <= 1e-4 + 1e-5 * np.abs(rl) + slack), \
+        float(np.max(np.abs(lse - rl)))
