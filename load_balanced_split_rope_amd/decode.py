@@ -59,6 +59,8 @@ class DecodeConfig(_Memo):
 
     def _shape(self):
         # shared by the binding's calls; never modified
+        if self.kv_dtype not in ("bf16", "fp8"):
+            raise ValueError(f"kv_dtype {self.kv_dtype!r}: 'bf16' or 'fp8'")
         return self._memoised("shape", lambda: B.Shape(
             self.num_q_heads, self.num_kv_heads, B.HEAD_DIM, B.PAGE_SIZE,
             B.KV_BF16 if self.kv_dtype == "bf16" else B.KV_FP8_E4M3,

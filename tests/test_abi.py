@@ -526,3 +526,14 @@ def test_pack_cache_validates_before_any_launch(lib):
     s8 = DecodeConfig(64, 8, "fp8", 4, 100).shape()
     assert lib.lbsr_pack_cache(ctypes.byref(s8), 1, fake, 64 * H * 128, H * 128, 120, fake,
                                nul) == B.E_INVALID
+
+
+@pytest.mark.parametrize("field,value", [("kv_dtype", "bf8"), ("kv_dtype", "BF16"),
+                                         ("out_dtype", "fp16"), ("qk_dtype", "e4m3")])
+def test_binding_refuses_unknown_dtype_names(field, value):
+    """The binding names dtypes by string; an unknown name is refused rather than
+    read as the other type."""
+    cfg = cfg_mix()
+    setattr(cfg, field, value)
+    with pytest.raises(ValueError, match=field):
+        cfg.shape() if field == "kv_dtype" else cfg.params()
