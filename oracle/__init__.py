@@ -28,9 +28,10 @@ docstrings here.
 
 Parity status per function (what pins it is in ``tests/test_oracle_*.py``):
 every public function is pinned by a library routine, a closed form, an
-invariant or brute force, except the RoPE/QK-Norm *order* (R2), which the
-pages do not fix: "parity unpinned" for the order itself; only the part both
-orders share (per-channel weight = 1) is pinned.
+invariant or brute force, except the choice of RoPE/QK-Norm *order* (R2),
+which the pages do not fix: "parity unpinned" for that choice.  The
+composition of either order is pinned (an invariant each order alone
+satisfies for any weights, and the exact agreement of the two at weight 1).
 """
 
 from .formats import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_to_f64,

@@ -10,8 +10,11 @@ name neither the RoPE variant nor the norm's formula; the readings are:
 * R2 -- RoPE first, then the norm (the order the pages list the operations
   in).  ``norm_before_rope`` selects the other order.  RoPE is an isometry and
   the RMS is rotation invariant, so the two orders differ only through the
-  per-channel weight; with weight 1 they agree exactly.  The order itself is
-  parity unpinned.
+  per-channel weight; with weight 1 they agree exactly.  Which order the
+  pages mean is parity unpinned (they do not say); the composition of each
+  order is pinned by an invariant it alone satisfies for any weights (norm
+  last: y / w has the RMS of a normalised vector; RoPE last: so does y
+  rotated back, divided by w).
 * R3 -- RMSNorm y = x / sqrt(mean(x**2) + eps) * w, eps inside the root, one
   weight vector of length D for all q heads and one for all k heads.
 * R4 -- v is neither rotated nor normalised.

@@ -92,3 +92,36 @@ def test_norm_and_rope_orders_agree_with_unit_weight():
     a = qk_transform(x, w, 777, 1e4, 1e-6, norm_before_rope=False)
     b = qk_transform(x, w, 777, 1e4, 1e-6, norm_before_rope=True)
     assert np.max(np.abs(a - b)) > 1e-3
+
+
+def _unrotate(y, pos, theta):
+    """Inverse of rotate-half RoPE, written as the complex rotation by -angle:
+    channel pairs (i, i + D/2) are the real and imaginary parts of z_i."""
+    half = D // 2
+    a = pos * theta ** (-2.0 * np.arange(half) / D)
+    z = (y[..., :half] + 1j * y[..., half:]) * np.exp(-1j * a)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+@pytest.mark.parametrize("pos", [0, 1, 777, 131071])
+def test_composition_order_invariants(pos):
+    """Each order leaves its own trace whatever the weights: with the norm last
+    (the default, R2), y / w has RMS sqrt(ms / (ms + eps)) for ms = mean(x^2)
+    (RoPE keeps ms); with RoPE last, rotating y back gives a vector whose ratio
+    to w has that RMS.  A swapped order, a dropped step or a weight applied in
+    the wrong place breaks the one that is asserted."""
+    rng = np.random.default_rng(40 + pos % 97)
+    x = rng.standard_normal((6, D)) * rng.uniform(0.01, 30.0, (6, 1))
+    w = 1 + 0.3 * rng.standard_normal(D)
+    eps = 1e-6
+    ms = np.mean(x * x, axis=-1)
+    want = np.sqrt(ms / (ms + eps))
+    y = qk_transform(x, w, pos, 1e4, eps, norm_before_rope=False)
+    got = np.sqrt(np.mean((y / w) ** 2, axis=-1))
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+    y2 = qk_transform(x, w, pos, 1e4, eps, norm_before_rope=True)
+    got2 = np.sqrt(np.mean((_unrotate(y2, pos, 1e4) / w) ** 2, axis=-1))
+    assert np.allclose(got2, want, rtol=1e-12, atol=0)
+    # and each invariant fails for the other order once the weight is not flat
+    if pos:
+        assert not np.allclose(np.sqrt(np.mean((y2 / w) ** 2, axis=-1)), want, rtol=1e-6, atol=0)
