@@ -737,6 +737,10 @@ def main():
                 if name == "tiny":
                     fold[name]["two_launches_graph_us"] = round(cf.graph_ms(s2, 40) * 1e3, 2)
                     fold[name]["folded_graph_us"] = round(cf.graph_ms(s1, 40) * 1e3, 2)
+                    fold[name]["two_launches_graph_10_steps_us"] = round(
+                        cf.graph_ms(s2, 40, per_graph=10) * 1e3, 2)
+                    fold[name]["folded_graph_10_steps_us"] = round(
+                        cf.graph_ms(s1, 40, per_graph=10) * 1e3, 2)
                 del cf
                 torch.cuda.empty_cache()
             result["fold_merge"] = fold
