@@ -87,3 +87,32 @@ def test_ragged_prefill_step_in_a_graph():
 
     replay_and_compare(call, [q_out, out, lse])
     assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("fold", [False, True])
+def test_consecutive_steps_in_one_graph(fold):
+    """Two decode steps of different batches captured in one graph, sharing one
+    workspace (as a decode loop captures several steps or layers at once): the
+    second step's schedule overwrites the first's in stream order, and each
+    step's outputs must equal its eager run on every replay."""
+    dev = device()
+    wa = wl.custom([3000, 70, 5000, 1, 64], num_q_heads=64, num_kv_heads=8, seed=962)
+    wb = wl.custom([129, 8000, 2, 640, 65, 4096], num_q_heads=64, num_kv_heads=8, seed=963)
+    ga, gb = to_device(wl.make_inputs(wa), dev), to_device(wl.make_inputs(wb), dev)
+    sched = lb.Schedule("dynamic", num_workers=256, fold_merge=fold)
+    cfa, cfb = config_for(wa, ga), config_for(wb, gb)
+    ws = lb.alloc_workspace(cfb if wb.batch >= wa.batch else cfa, max(wa.batch, wb.batch), sched,
+                            device=dev)
+    assert ws.numel() >= lb.workspace_layout(cfa, wa.batch, sched).total
+    bufs = []
+    for w, g in ((wa, ga), (wb, gb)):
+        bufs.append((torch.empty_like(g["q"]), torch.empty_like(g["q"]),
+                     torch.empty(w.batch, 64, dtype=torch.float32, device=dev)))
+
+    def call():
+        for (w, g, cf), (q_out, out, lse) in zip(((wa, ga, cfa), (wb, gb, cfb)), bufs):
+            lb.decode_step(cf, g["q"], g["k"], g["v"], g["positions"], g["seq_lens"],
+                           g["q_norm_w"], g["k_norm_w"], g["block_table"], g["k_cache"],
+                           g["v_cache"], q_out, sched, ws, out, lse)
+
+    replay_and_compare(call, [t for b in bufs for t in b])
