@@ -149,8 +149,8 @@ typedef struct {
                                  (multi-token decode, see below); 1 = one-token step */
   int32_t reserved;           /* must be 0 */
   int64_t num_pages;          /* pages in each pool, >= 1 */
-  int64_t page_stride;        /* elements; multiple of 8192 */
-  int64_t head_stride;        /* elements; multiple of 8192 */
+  int64_t page_stride;        /* elements; multiple of 8192; num_pages * page_stride <= 2^46 */
+  int64_t head_stride;        /* elements; multiple of 8192; num_kv_heads * head_stride <= 2^46 */
 } lbsr_shape;
 
 typedef struct {
@@ -559,9 +559,10 @@ lbsr_status lbsr_stream_read(const void *buf, size_t bytes, int32_t workgroups, 
  * Channels are contiguous; any order of the other three axes works (e.g.
  * token-major [pages][64][Hkv][128]: strides 64*Hkv*128, Hkv*128, 128;
  * head-major [pages][Hkv][64][128]: Hkv*64*128, 128, 64*128).  The strides
- * must be positive, their byte sizes multiples of 16, and no two (page, row,
- * head) rows may overlap (sorted by stride, each stride at least the extent
- * of the axes below it); else LBSR_E_INVALID.
+ * must be positive, their byte sizes multiples of 16, each axis may span at
+ * most 2^46 elements (stride x entries), and no two (page, row, head) rows
+ * may overlap (sorted by stride, each stride at least the extent of the axes
+ * below it); else LBSR_E_INVALID.
  *
  * `cache` is a pool of the library's layout with shape->num_pages pages,
  * shape->page_stride and shape->head_stride; every (page, KV head) tile of it

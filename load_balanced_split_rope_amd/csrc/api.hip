@@ -115,6 +115,14 @@ lbsr_status check_shape(const lbsr_shape* s, int32_t batch) {
       s->head_stride < LBSR_TILE_ELEMS || s->head_stride % LBSR_TILE_ELEMS)
     return fail(LBSR_E_INVALID, "page_stride %lld / head_stride %lld must be positive multiples of 8192",
                 (long long)s->page_stride, (long long)s->head_stride);
+  // offsets page * page_stride + head * head_stride stay far inside int64:
+  // each term (and so a pool's extent) is bounded by 2^46 elements, more than
+  // any device holds
+  constexpr int64_t kMaxPoolElems = (int64_t)1 << 46;
+  if (s->page_stride > kMaxPoolElems / s->num_pages ||
+      s->head_stride > kMaxPoolElems / s->num_kv_heads)
+    return fail(LBSR_E_INVALID, "page_stride %lld / head_stride %lld: a pool would exceed 2^46 elements",
+                (long long)s->page_stride, (long long)s->head_stride);
   const bool page_major = s->page_stride >= (int64_t)s->num_kv_heads * s->head_stride;
   const bool head_major = s->head_stride >= s->num_pages * s->page_stride;
   if (!page_major && !head_major)
@@ -918,10 +926,15 @@ lbsr_status check_rows(const lbsr_shape* s, int32_t kind, const void* rows, cons
   const int64_t strides[3] = {ps, ts, hs};
   const int64_t extents[3] = {s->num_pages, LBSR_PAGE_SIZE, s->num_kv_heads};
   const char* names[3] = {"row_page_stride", "row_token_stride", "row_head_stride"};
+  // each axis spans at most 2^46 elements, so the reach and the farthest
+  // offset below stay far inside int64
+  constexpr int64_t kMaxRowElems = (int64_t)1 << 46;
   for (int i = 0; i < 3; ++i) {
-    if (strides[i] <= 0 || strides[i] > ((int64_t)1 << 40) || (strides[i] * elem) % 16)
-      return fail(LBSR_E_INVALID, "%s %lld must be positive, below 2^40, and %lld-element aligned",
-                  names[i], (long long)strides[i], (long long)(16 / elem));
+    if (strides[i] <= 0 || strides[i] > kMaxRowElems / extents[i] || (strides[i] * elem) % 16)
+      return fail(LBSR_E_INVALID,
+                  "%s %lld must be positive, span at most 2^46 elements over its %lld entries, "
+                  "and be %lld-element aligned",
+                  names[i], (long long)strides[i], (long long)extents[i], (long long)(16 / elem));
   }
   int order[3] = {0, 1, 2};
   for (int i = 0; i < 3; ++i)

@@ -513,6 +513,7 @@ def test_pack_cache_validates_before_any_launch(lib):
         assert call(b=odd) == B.E_INVALID and b"aligned" in lib.lbsr_last_error()
         assert call(st=(nhd[0], nhd[1], 4)) == B.E_INVALID          # 8-byte head stride
         assert call(st=(nhd[0], 0, 128)) == B.E_INVALID             # zero token stride
+        assert call(st=(1 << 40, nhd[1], 128)) == B.E_INVALID       # pages would span > 2^46
         assert call(st=(nhd[0], 128, 128)) == B.E_INVALID           # token and head rows collide
         assert b"overlaps" in lib.lbsr_last_error()
         assert call(st=(64 * 128, H * 128, 128)) == B.E_INVALID     # pages overlap
@@ -537,3 +538,29 @@ def test_binding_refuses_unknown_dtype_names(field, value):
     setattr(cfg, field, value)
     with pytest.raises(ValueError, match=field):
         cfg.shape() if field == "kv_dtype" else cfg.params()
+
+
+@pytest.mark.parametrize("page_stride,head_stride", [
+    (1 << 62, 8192),                      # would overflow int64 in num_pages * page_stride
+    (8192 * 8, (1 << 46) // 4),           # 8 KV heads x head_stride > 2^46
+    ((1 << 46) // 4000 // 8192 * 8192 + 8192 * 8, 8192)])   # just above the bound at 4000 pages
+def test_huge_strides_are_refused(lib, page_stride, head_stride):
+    """Strides whose pool would pass 2^46 elements are refused on the host,
+    before any product of them could overflow."""
+    cfg = DecodeConfig(64, 8, "bf16", max_blocks_per_seq=64, num_pages=4000,
+                       page_stride=page_stride, head_stride=head_stride)
+    s = cfg.shape()
+    out = B.WsLayout()
+    c = Schedule("dynamic", num_workers=256).cfg()
+    got = lib.lbsr_workspace_layout(ctypes.byref(s), 16, ctypes.byref(c), ctypes.byref(out))
+    assert got == B.E_INVALID and b"2^46" in lib.lbsr_last_error()
+
+
+def test_large_strides_within_the_bound_are_accepted(lib):
+    cfg = DecodeConfig(64, 8, "bf16", max_blocks_per_seq=64, num_pages=4000,
+                       page_stride=(1 << 46) // 4000 // 8192 * 8192, head_stride=8192)
+    s = cfg.shape()
+    out = B.WsLayout()
+    c = Schedule("dynamic", num_workers=256).cfg()
+    assert lib.lbsr_workspace_layout(ctypes.byref(s), 16, ctypes.byref(c),
+                                     ctypes.byref(out)) == B.OK, lib.lbsr_last_error()
