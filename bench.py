@@ -199,6 +199,8 @@ WORKLOAD_TEXT = {
     "chunked_prefill": "chunked_prefill: 32 x (4096-token prefix + 512 new tokens), BF16 cache",
     "ragged_prefill": "ragged_prefill: 8 prompts, 512 to 8192 new tokens each (25,788 packed) "
                       "after prefixes of 0 to 20,000 tokens, BF16 cache",
+    "mixed_prefill": "mixed_prefill: 4 sequences prefilling 1024 new tokens each after "
+                     "8192 cached, BF16 cache",
 }
 WALL_CLOCK_MHZ = 100.0   # the constant clock the trace stamps (100 MHz on MI300-class GPUs)
 
@@ -306,47 +308,21 @@ def prefill_leg(dev, reps=10, warmup=3, names=None):
         runs = [(n, "bf16") for n in names]
     for name, qk in runs:
         w = wl.named(name)
-        g = wl.make_inputs(w, device=dev)
-        cfg = lb.DecodeConfig(w.num_q_heads, w.num_kv_heads, w.kv_dtype, g["max_blocks"],
-                              g["num_pages"], page_stride=g["page_stride"],
-                              head_stride=g["head_stride"], rope_theta=w.rope_theta,
-                              rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale,
-                              tokens_per_seq=w.max_new_tokens, qk_dtype=qk, q_scale=Q_SCALE)
-        q_out = torch.empty_like(g["q"])
-        out = torch.empty_like(g["q"])
-        lse = torch.empty(g["q"].shape[:-1], dtype=torch.float32, device=dev)
-        err = torch.zeros(1, dtype=torch.int32, device=dev)
-        common = (g["seq_lens"], g["q_norm_w"], g["k_norm_w"], g["block_table"], g["k_cache"],
-                  g["v_cache"], q_out, out, lse, err)
-        if w.varlen:
-            ws = lb.alloc_prefill_workspace(cfg, w.batch, g["q"].shape[0], device=dev)
-            step_fn, attn_fn = lb.prefill_step_varlen, lb.prefill_attention_varlen
-            step_args = ((cfg, g["q_start"], g["q"], g["k"], g["v"], g["positions"]) + common[:7]
-                         + (ws,) + common[7:])
-            attn_args = (cfg, g["q_start"], q_out, g["k_cache"], g["v_cache"], g["block_table"],
-                         g["seq_lens"], ws, out, lse, err)
-        else:
-            # with a workspace: the longest-first work list, as the ragged call
-            ws = lb.alloc_prefill_workspace(cfg, w.batch, w.batch * w.tokens, device=dev)
-            step_fn = lambda *a: lb.prefill_step(*a, workspace=ws)
-            attn_fn = lambda *a: lb.prefill_attention(*a, workspace=ws)
-            step_args = (cfg, g["q"], g["k"], g["v"], g["positions"]) + common
-            attn_args = (cfg, q_out, g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"],
-                         out, lse, err)
+        step, attn, err, _ = prefill_calls(w, dev, qk)
 
-        def event_ms(fn, args):
+        def event_ms(fn):
             for _ in range(warmup):
-                fn(*args)
+                fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(reps):
-                fn(*args)
+                fn()
             e1.record()
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
-        step_ms = event_ms(step_fn, step_args)
-        attn_ms = event_ms(attn_fn, attn_args)
+        step_ms = event_ms(step)
+        attn_ms = event_ms(attn)
         if int(err.item()) != 0:
             raise RuntimeError(f"prefill leg {name}: device error word {int(err.item()):#x}")
         f = prefill_flops(w)
@@ -361,9 +337,94 @@ def prefill_leg(dev, reps=10, warmup=3, names=None):
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": f"prefill_kernel<{w.kv_dtype}{', fp8 scores' if qk == 'fp8' else ''}>"},
         }
-        del g, q_out, out, lse, step_args, attn_args
+        del step, attn
         torch.cuda.empty_cache()
     return legs
+
+
+def prefill_calls(w, dev, qk="bf16"):
+    """Inputs for prefill workload `w` on the GPU and two closures on them: the
+    whole prefill step (prologue + attention) and attention alone; plus the
+    error word and the input dict."""
+    g = wl.make_inputs(w, device=dev)
+    cfg = lb.DecodeConfig(w.num_q_heads, w.num_kv_heads, w.kv_dtype, g["max_blocks"],
+                          g["num_pages"], page_stride=g["page_stride"],
+                          head_stride=g["head_stride"], rope_theta=w.rope_theta,
+                          rms_eps=w.rms_eps, k_scale=w.k_scale, v_scale=w.v_scale,
+                          tokens_per_seq=w.max_new_tokens, qk_dtype=qk, q_scale=Q_SCALE)
+    q_out = torch.empty_like(g["q"])
+    out = torch.empty_like(g["q"])
+    lse = torch.empty(g["q"].shape[:-1], dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    common = (g["seq_lens"], g["q_norm_w"], g["k_norm_w"], g["block_table"], g["k_cache"],
+              g["v_cache"], q_out, out, lse, err)
+    if w.varlen:
+        ws = lb.alloc_prefill_workspace(cfg, w.batch, g["q"].shape[0], device=dev)
+        step_args = ((cfg, g["q_start"], g["q"], g["k"], g["v"], g["positions"]) + common[:7]
+                     + (ws,) + common[7:])
+        attn_args = (cfg, g["q_start"], q_out, g["k_cache"], g["v_cache"], g["block_table"],
+                     g["seq_lens"], ws, out, lse, err)
+        return (lambda: lb.prefill_step_varlen(*step_args),
+                lambda: lb.prefill_attention_varlen(*attn_args), err, g)
+    # with a workspace: the longest-first work list, as the ragged call
+    ws = lb.alloc_prefill_workspace(cfg, w.batch, w.batch * w.tokens, device=dev)
+    step_args = (cfg, g["q"], g["k"], g["v"], g["positions"]) + common
+    attn_args = (cfg, q_out, g["k_cache"], g["v_cache"], g["block_table"], g["seq_lens"],
+                 out, lse, err)
+    return (lambda: lb.prefill_step(*step_args, workspace=ws),
+            lambda: lb.prefill_attention(*attn_args, workspace=ws), err, g)
+
+
+def mixed_leg(dev, P, sched, reps=20, warmup=3):
+    """A mixed batch (page B, "Why is this good?"): the mix's decode step and a
+    ragged chunked prefill of other sequences (4 x 1024 new tokens after 8192
+    cached) on one stream, each on its own pools; HIP events on the launch
+    stream, the two alone and back to back."""
+    case = Case(wl.named("mix"), dev)
+    wp = wl.named("mixed_prefill")
+    pstep, _, err, _ = prefill_calls(wp, dev)
+    state = {"i": 0}
+
+    def dec():
+        case.step(state["i"], sched)
+        state["i"] += 1
+
+    def both():
+        dec()
+        pstep()
+
+    def event_ms(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # interleaved rounds, median per part
+    t = {"decode": [], "prefill": [], "mixed": []}
+    for _ in range(3):
+        t["decode"].append(event_ms(dec))
+        t["prefill"].append(event_ms(pstep))
+        t["mixed"].append(event_ms(both))
+    if int(err.item()) != 0:
+        raise RuntimeError(f"mixed leg: device error word {int(err.item()):#x}")
+    m = {k: float(np.median(v)) for k, v in t.items()}
+    f = prefill_flops(wp)
+    out = {"workload": WORKLOAD_TEXT["mix"] + " decoding one token each, plus "
+                       + WORKLOAD_TEXT["mixed_prefill"] + ", one stream",
+           "us_per_step": round(m["mixed"] * 1e3, 1),
+           "decode_alone_us": round(m["decode"] * 1e3, 1),
+           "prefill_step_alone_us": round(m["prefill"] * 1e3, 1),
+           "sum_of_parts_us": round((m["decode"] + m["prefill"]) * 1e3, 1),
+           "prefill_flops": f,
+           "timing": f"median of 3 rounds of {reps} steps each, HIP events"}
+    del case
+    torch.cuda.empty_cache()
+    return out
 
 
 def oracle_threads():
@@ -760,6 +821,7 @@ def main():
                 "step_time_vs_bf16_scores": round(rq["ms"] / ms8, 4),
             }
             result["prefill"] = prefill_leg(dev)
+            result["mixed"] = mixed_leg(dev, P, r["schedule"])
             result["pack_cache"] = pack_leg(dev)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(w, dev)

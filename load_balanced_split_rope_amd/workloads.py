@@ -23,6 +23,8 @@ head dim 128; 64-token pages):
 * ``ragged_prefill``  8 prompts with their own chunk lengths (8192, 4096,
                   2048, 1024, 512, 3072, 6144, 700 new tokens) after prefixes
                   of 0, 4096, 0, 8192, 0, 1024, 0, 20000 tokens (packed)
+* ``mixed_prefill``  the prefill half of a mixed batch: 4 sequences each
+                  prefilling 1024 new tokens after 8192 cached (packed)
 
 Recipe (per workload, seed s): ``numpy.random.SeedSequence(s)`` spawns child
 streams, in order: 0 lengths (unused: fixed lists, or for ``loguniform``
@@ -124,6 +126,10 @@ def named(name):
         prefix = [0, 4096, 0, 8192, 0, 1024, 0, 20000]
         return Workload("ragged_prefill", [p + n for p, n in zip(prefix, new)], seed=11,
                         new_tokens=new)
+    if name == "mixed_prefill":
+        # the prefill half of a mixed batch: 4 sequences each prefilling a
+        # 1024-token chunk after 8192 cached tokens (ragged call)
+        return Workload("mixed_prefill", [9216] * 4, seed=12, new_tokens=[1024] * 4)
     raise KeyError(name)
 
 
