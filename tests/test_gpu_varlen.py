@@ -210,19 +210,21 @@ def test_malformed_q_start_is_flagged():
 
 
 @pytest.mark.slow
-def test_ragged_prefill_full_size_sampled():
-    """The benchmark's ragged prefill (8 prompts, 25,788 packed new tokens) in
-    its launch configuration: q_out of sampled sequences bit-exact, sampled
-    (token, head) outputs and lse against the oracle."""
+@pytest.mark.parametrize("name,seqs", [("ragged_prefill", [0, 3, 7]),   # no prefix; 8192; 20000
+                                       ("mixed_prefill", [0, 3])])      # 8192-token prefixes
+def test_ragged_prefill_full_size_sampled(name, seqs):
+    """The benchmark's ragged prefills (8 prompts and 25,788 packed new tokens;
+    the mixed batch's 4 x 1024 after 8192 cached) in their launch
+    configuration: q_out of sampled sequences bit-exact, sampled (token, head)
+    outputs and lse against the oracle."""
     dev = device()
-    w = wl.named("ragged_prefill")
+    w = wl.named(name)
     g = wl.make_inputs(w, device=dev)
     pools = host_pools(g, w)              # the caches before the step writes them
-    print("ragged prefill full size", flush=True)
+    print(f"{name} full size", flush=True)
     res = run_varlen(w, g)
     assert res["error"] == 0
     h = host_step_inputs(g)
-    seqs = [0, 3, 7]                       # no prefix; 8192-token prefix; 20000-token prefix
     starts = mt.query_starts(w.new_tokens)
     rows = np.concatenate([np.arange(starts[b], starts[b + 1]) for b in seqs])
     sub_counts = [w.new_tokens[b] for b in seqs]
