@@ -53,5 +53,5 @@ __all__ = [
     "tiles_per_sequence", "plan_dynamic", "plan_static",
     "default_static_splits", "Plan", "attend_full", "attend_chunk",
     "combine_lse", "prologue", "cache_slot", "gather_kv", "decode_attention",
-    "split_attention", "encode_output", "multitoken",
+    "split_attention", "encode_output", "multitoken", "qk",
 ]
